@@ -1,0 +1,50 @@
+"""The seeded input generators: rounding, determinism, per-head regeneration, config shapes."""
+import numpy as np
+import torch
+
+from attention_kl_amd import workloads as wl
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 3,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 65504.0, 1e-30], np.float32)])
+    mine = wl.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(mine, ref)
+    back = wl.bf16_bits_to_f32(mine)
+    np.testing.assert_array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_heads_regenerate_independently():
+    w = wl.custom(2, 3, 40, 48, 64, 64, True, seed=7)
+    full = wl.full_f32(w)
+    for b in range(2):
+        for h in range(3):
+            one = wl.head_f32(w, b, h)
+            for a, f in zip(one, full):
+                np.testing.assert_array_equal(a, f[b, h])
+    assert not np.array_equal(full[0][0, 0], full[0][0, 1])
+
+
+def test_recipes():
+    w = wl.CONFIGS[2]
+    qt, kt, qs, ks = wl.head_f32(wl.custom(1, 1, 64, 64, 128, 128, True, recipe="noise", sigma=0.1, seed=2), 0, 0)
+    assert 0.05 < np.std(qs - qt) < 0.15  # student = teacher + 0.1 N(0,1), bf16-rounded
+    bits = wl.f32_to_bf16_bits(qt)
+    np.testing.assert_array_equal(wl.bf16_bits_to_f32(bits), qt)  # already bf16 values
+    pk = wl.Workload("p", 1, 1, 16, 1000, 8, 8, True, "fp32", "independent", peak_frac=0.01, peak_scale=4.0, seed=3)
+    kt_p = wl.head_f32(pk, 0, 0)[1]
+    kt_0 = wl.head_f32(wl.Workload("p", 1, 1, 16, 1000, 8, 8, True, "fp32", "independent", seed=3), 0, 0)[1]
+    ratio = np.abs(kt_p).sum(1) / np.abs(kt_0).sum(1)
+    assert np.sum(np.isclose(ratio, 4.0)) == 10 and np.sum(np.isclose(ratio, 1.0)) == 990
+    assert w.B * w.H * w.Nq == 65536
+
+
+def test_config_flops():
+    c3 = wl.CONFIGS[3]
+    assert c3.pairs_per_head() == 32768 * 32769 // 2
+    assert abs(c3.fwd_flops() - 8.796e12) / 8.796e12 < 1e-3
+    assert wl.CONFIGS[4].pairs_per_head() == 8192 * 8192
+    g = wl.head_g(c3, 0, 5)
+    assert g.shape == (32768,) and g.min() >= 0.5 and g.max() <= 1.5
