@@ -1,0 +1,144 @@
+// Device-side building blocks shared by the attention-KL kernels (gfx950 only).
+//
+// MFMA tile convention used everywhere (v_mfma_f32_32x32x16_bf16 and
+// v_mfma_f32_32x32x2f32, 64-lane wavefront):
+//   A operand  : lane l supplies row  m = l % 32 of the 32 x k block
+//   B operand  : lane l supplies col  n = l % 32 of the k x 32 block
+//   lane half  : hf = l / 32 supplies the second half of the k block
+//   D (32x32)  : lane l holds column n = l % 32, rows  8*(i/4) + 4*hf + (i%4),  i = 0..15
+// Operand rows are read as 16-byte chunks: lane half hf takes chunks 2c+hf of a
+// row for step c.  A and B always use the same chunk-to-k mapping, so the
+// contraction pairs the same feature index on both sides whatever the dtype.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skl {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maxima start here rather than at -inf so that a lane whose keys are all
+// masked so far still rescales by exp2(0) = 1 instead of exp2(-inf + inf) = NaN.
+constexpr float kMaxInit = -1.0e30f;
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+  static constexpr int kPer16 = 8;  // elements per 16-byte chunk
+};
+template <>
+struct Elt<float> {
+  static constexpr int kPer16 = 4;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// acc += A * B over one 16-byte chunk per lane of each operand.
+template <typename T>
+__device__ __forceinline__ void mma_chunk(f32x16& acc, const u32x4& a, const u32x4& b);
+
+template <>
+__device__ __forceinline__ void mma_chunk<__bf16>(f32x16& acc, const u32x4& a, const u32x4& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_chunk<float>(f32x16& acc, const u32x4& a, const u32x4& b) {
+  // Copy each lane element to a scalar before reinterpreting it: a bit-cast applied directly to
+  // an ext-vector element reads the vector's first element.
+  const uint32_t av[4] = {a[0], a[1], a[2], a[3]};
+  const uint32_t bv[4] = {b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[e]), __uint_as_float(bv[e]), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 lds_read8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Row of the 32x32 accumulator held in register i by lane half hf.
+__device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
+
+// 32x32 tile product S = rows(A) . rows(B)^T over D features, A rows read from LDS
+// (row pitch `pitch` bytes, first row = lane's m row already applied in `a_row`) and
+// B rows held in registers as D*sizeof(T)/32 chunks.
+template <typename T, int D>
+__device__ __forceinline__ void tile_dot_lds_a(f32x16& acc, const char* a_row, int hf, const u32x4* b_regs) {
+  constexpr int NC = D * (int)sizeof(T) / 16;
+#pragma unroll
+  for (int c = 0; c < NC / 2; ++c) mma_chunk<T>(acc, lds_read16(a_row + (2 * c + hf) * 16), b_regs[c]);
+}
+
+// Same product with the A operand in registers and B rows from LDS.
+template <typename T, int D>
+__device__ __forceinline__ void tile_dot_lds_b(f32x16& acc, const u32x4* a_regs, const char* b_row, int hf) {
+  constexpr int NC = D * (int)sizeof(T) / 16;
+#pragma unroll
+  for (int c = 0; c < NC / 2; ++c) mma_chunk<T>(acc, a_regs[c], lds_read16(b_row + (2 * c + hf) * 16));
+}
+
+// Load one row's operand chunks (2c + hf) from global memory, or zeros past the end.
+template <typename T, int D>
+__device__ __forceinline__ void load_row_regs(u32x4* regs, const T* row, bool valid, int hf) {
+  constexpr int NC = D * (int)sizeof(T) / 16;
+  const char* p = reinterpret_cast<const char*>(row);
+#pragma unroll
+  for (int c = 0; c < NC / 2; ++c) {
+    regs[c] = valid ? *reinterpret_cast<const u32x4*>(p + (2 * c + hf) * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Cooperative copy of a tile of `rows` rows (D features each) from global memory to LDS
+// (row pitch `pitch` bytes); rows at or past `valid_rows` are zero-filled.  When T_PITCH > 0
+// the tile is also written transposed ([feature][row], pitch T_PITCH bytes) to `lds_t`.
+template <typename T, int D, int ROWS, int NTHREADS, int T_PITCH>
+__device__ __forceinline__ void stage_tile(char* lds, int pitch, char* lds_t, const T* src, int64_t row_stride,
+                                           int valid_rows, int tid) {
+  constexpr int NC = D * (int)sizeof(T) / 16;
+  constexpr int PER = Elt<T>::kPer16;
+#pragma unroll
+  for (int idx = tid; idx < ROWS * NC; idx += NTHREADS) {
+    const int r = idx / NC, c = idx % NC;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < valid_rows) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src + r * row_stride) + c * 16);
+    *reinterpret_cast<u32x4*>(lds + r * pitch + c * 16) = v;
+    if constexpr (T_PITCH > 0) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const uint16_t h16 = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          *reinterpret_cast<uint16_t*>(lds_t + (c * PER + e) * T_PITCH + r * 2) = h16;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) *reinterpret_cast<uint32_t*>(lds_t + (c * PER + e) * T_PITCH + r * 4) = v[e];
+      }
+    }
+  }
+}
+
+// Split 8 fp32 values into bf16 hi + lo parts (v ~= hi + lo to about 2^-16 relative).
+__device__ __forceinline__ void split_bf16x8(const float* v, u32x4& hi, u32x4& lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 hb = (__bf16)v[e];
+    h[e] = hb;
+    l[e] = (__bf16)(v[e] - (float)hb);
+  }
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, l);
+}
+
+}  // namespace skl

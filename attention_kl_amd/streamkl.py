@@ -1,0 +1,177 @@
+"""Python binding of libstreamkl.so (the C ABI in include/streamkl.h).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  torch supplies device memory and the current HIP stream.  When the
+library is missing, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libstreamkl.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "streamkl.h")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
+FP32, BF16 = 0, 1
+
+
+class StreamKLError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_I64x3 = ctypes.c_int64 * 3
+
+
+class Problem(ctypes.Structure):
+    """Mirror of streamkl_problem_t."""
+
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64),
+                ("d_t", ctypes.c_int32), ("d_s", ctypes.c_int32),
+                ("scale_t", ctypes.c_float), ("scale_s", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("stride_qt", _I64x3), ("stride_kt", _I64x3), ("stride_qs", _I64x3), ("stride_ks", _I64x3)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_P = ctypes.POINTER(Problem)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libstreamkl.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_kl_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.streamkl_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.streamkl_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.streamkl_bwd_dq.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.streamkl_bwd_dk.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        for f in ("streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_version"):
+            getattr(L, f).restype = ctypes.c_int
+        L.streamkl_status_string.argtypes = [ctypes.c_int]
+        L.streamkl_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Entry points declared in include/streamkl.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(streamkl_\w+)\s*\(", txt, re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().streamkl_status_string(status).decode()
+
+
+def version() -> int:
+    return lib().streamkl_version()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise StreamKLError(status, f"{what}: {status_string(status)}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
+                 scale_s: Optional[float] = None) -> Problem:
+    """Describe four [B, H, N, d] tensors (d unit-stride) as a streamkl_problem_t."""
+    import torch
+    for name, t in (("q_t", qt), ("k_t", kt), ("q_s", qs), ("k_s", ks)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d], got {tuple(t.shape)}")
+        if t.stride(-1) != 1 and t.shape[-1] > 1:
+            raise ValueError(f"{name}: the d axis must be contiguous")
+        if t.dtype != qt.dtype:
+            raise ValueError("all four inputs must share one dtype")
+    B, H, Nq, d_t = qt.shape
+    Nk = kt.shape[2]
+    d_s = qs.shape[3]
+    if tuple(kt.shape) != (B, H, Nk, d_t) or tuple(qs.shape) != (B, H, Nq, d_s) or tuple(ks.shape) != (B, H, Nk, d_s):
+        raise ValueError(f"shape mismatch: {tuple(qt.shape)} {tuple(kt.shape)} {tuple(qs.shape)} {tuple(ks.shape)}")
+    dt = {torch.bfloat16: BF16, torch.float32: FP32}.get(qt.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {qt.dtype}")
+    p = Problem()
+    p.B, p.H, p.Nq, p.Nk, p.d_t, p.d_s = B, H, Nq, Nk, d_t, d_s
+    p.scale_t = 1.0 / math.sqrt(d_t) if scale_t is None else scale_t
+    p.scale_s = 1.0 / math.sqrt(d_s) if scale_s is None else scale_s
+    p.causal = int(bool(causal))
+    p.dtype = dt
+    for f, t in (("stride_qt", qt), ("stride_kt", kt), ("stride_qs", qs), ("stride_ks", ks)):
+        getattr(p, f)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    return p
+
+
+def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None
+        ) -> Tuple["torch.Tensor", "torch.Tensor", "torch.Tensor"]:
+    """Per-row KL(P_t || P_s), LSE_t, LSE_s as float32 [B, H, Nq] (streamkl_fwd)."""
+    import torch
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    if out is None:
+        out = tuple(torch.empty((p.B, p.H, p.Nq), dtype=torch.float32, device=qt.device) for _ in range(3))
+    kl, lse_t, lse_s = out
+    _check(lib().streamkl_fwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(kl), _ptr(lse_t),
+                              _ptr(lse_s), _stream(stream)), "streamkl_fwd")
+    return kl, lse_t, lse_s
+
+
+def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads: bool = False,
+        scale_t=None, scale_s=None, out=None, stream=None):
+    """Gradients of sum_i g_i KL_i (streamkl_bwd): (dq_s, dk_s) or (dq_s, dk_s, dq_t, dk_t)."""
+    import torch
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    dev = qt.device
+    if out is None:
+        out = [torch.empty((p.B, p.H, p.Nq, p.d_s), dtype=torch.float32, device=dev),
+               torch.empty((p.B, p.H, p.Nk, p.d_s), dtype=torch.float32, device=dev)]
+        if teacher_grads:
+            out += [torch.empty((p.B, p.H, p.Nq, p.d_t), dtype=torch.float32, device=dev),
+                    torch.empty((p.B, p.H, p.Nk, p.d_t), dtype=torch.float32, device=dev)]
+    dq_s, dk_s = out[0], out[1]
+    dq_t, dk_t = (out[2], out[3]) if teacher_grads else (None, None)
+    _check(lib().streamkl_bwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
+                              _ptr(kl), _ptr(g), _ptr(dq_s), _ptr(dk_s), _ptr(dq_t), _ptr(dk_t), _stream(stream)),
+           "streamkl_bwd")
+    return tuple(out)
+
+
+def bwd_dq(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None):
+    """Student dQ only: the query-owner half of the backward (streamkl_bwd_dq)."""
+    import torch
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    if out is None:
+        out = torch.empty((p.B, p.H, p.Nq, p.d_s), dtype=torch.float32, device=qt.device)
+    _check(lib().streamkl_bwd_dq(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
+                                 _ptr(g), _ptr(out), _stream(stream)), "streamkl_bwd_dq")
+    return out
+
+
+def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None):
+    """Student dK only: the key-owner half of the backward (streamkl_bwd_dk)."""
+    import torch
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    if out is None:
+        out = torch.empty((p.B, p.H, p.Nk, p.d_s), dtype=torch.float32, device=qt.device)
+    _check(lib().streamkl_bwd_dk(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
+                                 _ptr(g), _ptr(out), _stream(stream)), "streamkl_bwd_dk")
+    return out

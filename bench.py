@@ -1,0 +1,220 @@
+"""Benchmark of the attention-KL hot path on one MI355X.
+
+One step = the whole path on one batch: the forward (per-row KL + both LSEs) and
+the student backward (dK_s then dQ_s), on the b1h32n32768d128 causal workload
+(teacher keys 1% scaled x4, independent student), bf16 inputs already resident in
+HBM.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+                  [--copy-calibrate]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+MI355X_PEAK_FP32_MFMA_TFLOPS = 157.3
+MI355X_HBM_GBS = 8000.0
+METRIC = "attention-KL fwd/bwd TFLOP/s and ms at N=32K, % of MFMA peak, extra HBM bytes"
+KERNEL_SOURCES = {"fwd": "attention_kl_amd/csrc/skl_fwd.hip", "bwd_dq": "attention_kl_amd/csrc/skl_bwd.hip",
+                  "bwd_dk": "attention_kl_amd/csrc/skl_bwd.hip"}
+
+
+def source_sha(kernel: str) -> str:
+    paths = [KERNEL_SOURCES[kernel], "attention_kl_amd/csrc/skl_device.hpp"]
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kernel_flops(w, kernel: str) -> float:
+    """Algorithmic MFMA flops of one launch.
+
+    fwd:    both logit products, 2 (d_t + d_s) per allowed pair.
+    bwd_dq: both logit products (the kernel has no other source of the logits) + dQ_s,
+            2 (d_t + 2 d_s) per pair.   bwd_dk: the same with dK_s.
+    The hi/lo split of dS and masked-tile work are not counted.
+    """
+    pairs = w.pairs_per_head() * w.B * w.H
+    if kernel == "fwd":
+        return 2.0 * pairs * (w.d_t + w.d_s)
+    return 2.0 * pairs * (w.d_t + 2 * w.d_s)
+
+
+def cpu_baseline(w, budget_rows: int):
+    """The float64 oracle timed on the host on a bounded sample of the same workload.
+
+    Sample: the last `budget_rows` query rows of head (0, 0) (each sees ~N keys), forward for
+    those rows and backward for the same rows with dK for the last `budget_rows` keys.
+    """
+    import numpy as np
+
+    import oracle
+    from attention_kl_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    hh = wl.head_f64(w, 0, 0)
+    g = wl.head_g(w, 0, 0)
+    rows = np.arange(w.Nq - budget_rows, w.Nq)
+    keys = np.arange(w.Nk - budget_rows, w.Nk)
+    t0 = time.perf_counter()
+    oracle.forward_head(*hh, w.scale_t, w.scale_s, w.causal, rows=rows)
+    t1 = time.perf_counter()
+    oracle.backward_head(*hh, w.scale_t, w.scale_s, w.causal, g, rows=rows, keys=keys)
+    t2 = time.perf_counter()
+    off = w.Nk - w.Nq
+    row_pairs = int(sum(min(w.Nk, i + off + 1) if w.causal else w.Nk for i in rows))
+    # pairs (i, j) with i in rows, j in keys, j allowed for i
+    rk = sum(max(0, min(w.Nk, i + off + 1) - keys[0]) if w.causal else len(keys) for i in rows)
+    fl_fwd = 2.0 * row_pairs * (w.d_t + w.d_s)
+    fl_bwd = 2.0 * row_pairs * (w.d_t + 2 * w.d_s) + 2.0 * rk * w.d_s
+    secs = t2 - t0
+    return {"value": (fl_fwd + fl_bwd) / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle on head (0,0): forward of the last {budget_rows} query rows, backward "
+                      f"(dQ_s of those rows, dK_s of the last {budget_rows} keys); {secs:.2f} s "
+                      f"(fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s)",
+            "seconds": secs}
+
+
+def load_traffic(kernel: str, workload: str):
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(workload, {}).get(kernel)
+        if not e or e.get("source_sha") != source_sha(kernel):
+            return None  # counters were taken on a different kernel
+        return float(e["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="synthetic config id (3 = b1h32n32768d128 causal)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; the path shards by heads with no exchange in the "
+              "forward, but no multi-GPU run is implemented or measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from attention_kl_amd import streamkl as S
+    from attention_kl_amd import workloads as wl
+
+    w = wl.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S.lib()  # fail loudly if the library is missing
+    bits = wl.full_bf16_bits(w) if w.dtype == "bf16" else None
+    if bits is not None:
+        qt, kt, qs, ks = (torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in bits)
+        del bits
+    else:
+        qt, kt, qs, ks = (torch.from_numpy(a).to(dev) for a in wl.full_f32(w))
+    g = torch.from_numpy(wl.full_g(w)).to(dev)
+    B, H = w.B, w.H
+    kl = torch.empty((B, H, w.Nq), dtype=torch.float32, device=dev)
+    lt = torch.empty_like(kl)
+    ls = torch.empty_like(kl)
+    dq = torch.empty((B, H, w.Nq, w.d_s), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, H, w.Nk, w.d_s), dtype=torch.float32, device=dev)
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        S.fwd(qt, kt, qs, ks, out=(kl, lt, ls), **kw)
+        if ev is not None:
+            ev[1].record()
+        S.bwd_dk(qt, kt, qs, ks, lt, ls, g, out=dk, **kw)
+        if ev is not None:
+            ev[2].record()
+        S.bwd_dq(qt, kt, qs, ks, lt, ls, g, out=dq, **kw)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.copy_calibrate:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    free0 = torch.cuda.mem_get_info()[0]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    extra_alloc = free0 - torch.cuda.mem_get_info()[0]
+    per = {"fwd": [], "bwd_dk": [], "bwd_dq": []}
+    for e in evs:
+        per["fwd"].append(e[0].elapsed_time(e[1]))
+        per["bwd_dk"].append(e[1].elapsed_time(e[2]))
+        per["bwd_dq"].append(e[2].elapsed_time(e[3]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+    kern = {}
+    for k, v in per.items():
+        ms = float(np.mean(v))
+        fl = kernel_flops(w, k)
+        kern[k] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                   "frac_of_bf16_peak": round(fl / ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4)}
+    fwd_fl, bwd_fl = w.fwd_flops(), w.bwd_flops()
+    fwd_ms = kern["fwd"]["ms"]
+    bwd_ms = kern["bwd_dk"]["ms"] + kern["bwd_dq"]["ms"]
+    dominant = max(kern, key=lambda k: kern[k]["ms"])
+    dom_fl = kernel_flops(w, dominant)
+    achieved = dom_fl / kern[dominant]["ms"] / 1e9
+    roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": MI355X_PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(dominant, w.name)}
+    value = (fwd_fl + bwd_fl) / step_ms / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded N(0,1) bf16 inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": B, "H": H, "N_Q": w.Nq, "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s,
+                   "causal": w.causal, "teacher_grads": False},
+        "fwd_ms": fwd_ms, "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(fwd_fl / fwd_ms / 1e9, 2), "bwd_tflops": round(bwd_fl / bwd_ms / 1e9, 2),
+        "fwd_frac_of_bf16_peak": round(fwd_fl / fwd_ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4),
+        "extra_hbm_bytes": 12 * B * H * w.Nq, "library_alloc_bytes": int(extra_alloc),
+        "materialised_bytes_avoided": 2 * 4 * w.pairs_per_head() * B * H,
+        "kernels": kern, "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

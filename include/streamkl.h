@@ -1,0 +1,123 @@
+/*
+ * streamkl.h — C ABI of the fused attention-KL primitive for AMD MI355X (gfx950).
+ *
+ * What is computed.  The StreamKL abstract ("StreamKL: Fast and Memory-Efficient
+ * KL Divergence for Boosting Attention Distillation", arXiv 2026; its sentences
+ * are cited as S1..S8 in reading order) defines the quantity as the KL
+ * divergence that attention distillation minimises between two attention
+ * distributions (S1), and asks that neither N_Q x N_K distribution be formed
+ * (S2, S3).  For every batch b, head h and query row i:
+ *
+ *   a_ij = scale_t * <q_t[i], k_t[j]>        b_ij = scale_s * <q_s[i], k_s[j]>
+ *   A_i  = { j < Nk : !causal || j <= i + Nk - Nq }   (bottom-right causal alignment)
+ *   P_t  = softmax_{A_i}(a_i.)               P_s  = softmax_{A_i}(b_i.)
+ *   KL_i = sum_{j in A_i} P_t,ij * (log P_t,ij - log P_s,ij)     (teacher || student)
+ *   LSE_t,i = log sum_{A_i} exp(a_ij)        LSE_s,i = log sum_{A_i} exp(b_ij)
+ *
+ * The forward is one streaming pass over key tiles (S4); the backward recomputes
+ * both probability tiles from the saved log-sum-exps (S5) and returns the
+ * gradients of L = sum_i g_i KL_i:
+ *
+ *   dS_s = g_i (P_s - P_t)                   dQ_s = scale_s dS_s K_s     dK_s = scale_s dS_s^T Q_s
+ *   dS_t = g_i P_t ((a - b) - (KL_i + LSE_t,i - LSE_s,i))
+ *                                            dQ_t = scale_t dS_t K_t     dK_t = scale_t dS_t^T Q_t
+ *
+ * Conventions shared by every entry point.
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates nothing, frees nothing and keeps no state: the only HBM it touches
+ *    beyond the inputs is the outputs the caller passes (S8: no O(Nq*Nk) buffer,
+ *    not even a workspace).
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous: the call returns after launch.  Kernel faults surface at the
+ *    caller's next synchronisation, as for any HIP launch.
+ *  - Inputs are read only.  Outputs are overwritten in full (never accumulated
+ *    into), so they need no zeroing.  Outputs must not alias inputs.
+ *  - Return value: STREAMKL_OK or an error code; nothing is launched when an
+ *    argument check fails.  Nothing is printed and nothing is thrown.
+ *  - Thread-safe: calls share no mutable state.  Results are bitwise
+ *    deterministic (no atomics; fixed reduction order).
+ */
+#ifndef STREAMKL_H
+#define STREAMKL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STREAMKL_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+  STREAMKL_FP32 = 0, /* inputs float32; products on fp32 MFMA                */
+  STREAMKL_BF16 = 1  /* inputs bfloat16; products on bf16 MFMA, fp32 accumulate */
+} streamkl_dtype_t;
+
+typedef enum {
+  STREAMKL_OK = 0,
+  STREAMKL_ERR_INVALID = 1,     /* bad argument: NULL pointer, negative size, Nk == 0 with rows to
+                                   compute, causal with Nq > Nk, non-positive or non-finite scale,
+                                   d stride != 1, only one of dq_t/dk_t given                       */
+  STREAMKL_ERR_UNSUPPORTED = 2, /* valid but not built: d_t or d_s not in {64, 128}, misaligned base
+                                   pointer or stride (16-byte alignment needed), dtype unknown      */
+  STREAMKL_ERR_LAUNCH = 3       /* the HIP launch itself failed (hipGetLastError after launch)     */
+} streamkl_status_t;
+
+/* Problem description.  Q/K tensors are [B, H, N, d] with the d axis contiguous;
+ * stride_*[0..2] are the element strides of the b, h and n axes (any order of
+ * axes in memory is allowed as long as d is unit-stride).  All four inputs share
+ * `dtype`.  Row statistics and gradients are dense and contiguous:
+ * kl, lse_t, lse_s, g are float32 [B, H, Nq]; dq_s [B, H, Nq, d_s], dk_s
+ * [B, H, Nk, d_s], dq_t [B, H, Nq, d_t], dk_t [B, H, Nk, d_t], all float32.   */
+typedef struct {
+  int64_t B, H, Nq, Nk;   /* B, H, Nq >= 0 (any zero = nothing to do, returns OK); Nk >= 1 when
+                             there are rows; causal needs Nq <= Nk                              */
+  int32_t d_t, d_s;       /* head dims of teacher and student: each 64 or 128                    */
+  float scale_t, scale_s; /* softmax scales (finite, > 0), usually 1/sqrt(d_t), 1/sqrt(d_s)      */
+  int32_t causal;         /* 0: every key; 1: key j allowed for row i iff j <= i + Nk - Nq      */
+  int32_t dtype;          /* streamkl_dtype_t                                                    */
+  int64_t stride_qt[3], stride_kt[3], stride_qs[3], stride_ks[3]; /* (b, h, n) strides, elements */
+} streamkl_problem_t;
+
+/* Forward (S4): KL_i, LSE_t,i, LSE_s,i for every row, float32 [B, H, Nq] each.
+ * One pass over the keys; per row only five running floats are kept.             */
+int streamkl_fwd(const streamkl_problem_t* p,
+                 const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                 float* kl, float* lse_t, float* lse_s,
+                 void* hip_stream);
+
+/* Backward (S5): gradients of sum_i g_i KL_i.  Needs the forward's lse_t, lse_s
+ * (and kl when teacher gradients are asked for; may be NULL otherwise) and the
+ * per-row weights g.  dq_s, dk_s are always written.  dq_t, dk_t: both NULL =
+ * student gradients only; both non-NULL = teacher gradients too; one of them
+ * NULL = STREAMKL_ERR_INVALID.  Launches the key-owner then the query-owner
+ * kernels (plus the teacher pair) on hip_stream.                                  */
+int streamkl_bwd(const streamkl_problem_t* p,
+                 const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                 const float* lse_t, const float* lse_s, const float* kl, const float* g,
+                 float* dq_s, float* dk_s, float* dq_t, float* dk_t,
+                 void* hip_stream);
+
+/* The two halves of streamkl_bwd for the student side, each one kernel launch,
+ * for callers (and profilers) that schedule them separately: the query-owner
+ * kernel writes dq_s, the key-owner kernel writes dk_s.  Same arguments and
+ * rules as streamkl_bwd.                                                          */
+int streamkl_bwd_dq(const streamkl_problem_t* p,
+                    const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                    const float* lse_t, const float* lse_s, const float* g,
+                    float* dq_s, void* hip_stream);
+int streamkl_bwd_dk(const streamkl_problem_t* p,
+                    const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                    const float* lse_t, const float* lse_s, const float* g,
+                    float* dk_s, void* hip_stream);
+
+/* Human-readable name of a status code (static storage; never NULL).            */
+const char* streamkl_status_string(int status);
+
+/* STREAMKL_VERSION of the built library.                                         */
+int streamkl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STREAMKL_H */

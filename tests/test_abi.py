@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header declares,
+and rejects bad arguments before any HIP call (no GPU needed: nothing is launched)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from attention_kl_amd import streamkl as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = S.declared_symbols()
+    assert {"streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_status_string",
+            "streamkl_version"} <= set(declared)
+    L = S.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+    assert S.version() == 10000
+
+
+def test_status_strings():
+    for st in (S.OK, S.ERR_INVALID, S.ERR_UNSUPPORTED, S.ERR_LAUNCH, 99):
+        assert S.status_string(st).startswith("STREAMKL")
+
+
+def _problem(**kw):
+    p = S.Problem()
+    p.B, p.H, p.Nq, p.Nk, p.d_t, p.d_s = 1, 1, 128, 128, 128, 128
+    p.scale_t = p.scale_s = 0.125
+    p.causal, p.dtype = 1, S.BF16
+    for f in ("stride_qt", "stride_kt", "stride_qs", "stride_ks"):
+        getattr(p, f)[:] = [128 * 128, 128 * 128, 128]
+    for k, v in kw.items():
+        if k.startswith("stride"):
+            getattr(p, k)[:] = v
+        else:
+            setattr(p, k, v)
+    return p
+
+
+# 16-byte aligned fake device addresses: argument checks never dereference them
+A = 0x10000
+PTRS = [A, A + 0x1000, A + 0x2000, A + 0x3000]
+OUTS = [A + 0x4000, A + 0x5000, A + 0x6000]
+
+
+def fwd_status(p, ptrs=PTRS, outs=OUTS):
+    return S.lib().streamkl_fwd(ctypes.byref(p) if p is not None else None, *ptrs, *outs, None)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(d_t=96), S.ERR_UNSUPPORTED),
+    (dict(d_s=32), S.ERR_UNSUPPORTED),
+    (dict(dtype=7), S.ERR_UNSUPPORTED),
+    (dict(Nq=-1), S.ERR_INVALID),
+    (dict(Nq=200, Nk=100), S.ERR_INVALID),  # causal needs Nq <= Nk
+    (dict(Nk=0), S.ERR_INVALID),
+    (dict(causal=2), S.ERR_INVALID),
+    (dict(scale_t=0.0), S.ERR_INVALID),
+    (dict(scale_s=float("nan")), S.ERR_INVALID),
+    (dict(scale_t=float("inf")), S.ERR_INVALID),
+    (dict(stride_qt=[1, 1, 3]), S.ERR_UNSUPPORTED),  # 6-byte row stride breaks 16-byte alignment
+    (dict(stride_ks=[-128, 128, 128]), S.ERR_INVALID),
+])
+def test_fwd_rejects_bad_problems(kw, expected):
+    assert fwd_status(_problem(**kw)) == expected
+
+
+def test_fwd_rejects_null_and_misaligned_pointers():
+    assert fwd_status(None) == S.ERR_INVALID
+    assert fwd_status(_problem(), ptrs=[A, 0, A, A]) == S.ERR_INVALID
+    assert fwd_status(_problem(), ptrs=[A + 2, A, A, A]) == S.ERR_UNSUPPORTED
+    assert fwd_status(_problem(), outs=[A, 0, A]) == S.ERR_INVALID
+    assert fwd_status(_problem(), outs=[A + 1, A, A]) == S.ERR_UNSUPPORTED
+
+
+def test_empty_problems_are_noops():
+    for kw in (dict(B=0), dict(H=0), dict(Nq=0), dict(Nq=0, Nk=0)):
+        assert fwd_status(_problem(**kw), ptrs=[0, 0, 0, 0], outs=[0, 0, 0]) == S.OK
+
+
+def test_bwd_argument_rules():
+    L = S.lib()
+    p = _problem()
+    st = [A + 0x7000, A + 0x8000, A + 0x9000, A + 0xA000]  # lse_t, lse_s, kl, g
+    # only one teacher output given
+    assert L.streamkl_bwd(ctypes.byref(p), *PTRS, *st, A + 0xB000, A + 0xC000, A + 0xD000, None, None) == \
+        S.ERR_INVALID
+    # teacher gradients need kl
+    assert L.streamkl_bwd(ctypes.byref(p), *PTRS, st[0], st[1], None, st[3], A + 0xB000, A + 0xC000, A + 0xD000,
+                          A + 0xE000, None) == S.ERR_INVALID
+    # missing g
+    assert L.streamkl_bwd(ctypes.byref(p), *PTRS, st[0], st[1], None, None, A + 0xB000, A + 0xC000, None, None,
+                          None) == S.ERR_INVALID
+    assert L.streamkl_bwd_dq(ctypes.byref(p), *PTRS, st[0], st[1], st[3], None, None) == S.ERR_INVALID
+    assert L.streamkl_bwd_dk(ctypes.byref(_problem(d_s=48)), *PTRS, st[0], st[1], st[3], A, None) == \
+        S.ERR_UNSUPPORTED
+    assert L.streamkl_bwd(ctypes.byref(_problem(B=0)), *([0] * 12), None) == S.OK
+
+
+def test_python_binding_validates_shapes():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        S.make_problem(q, torch.zeros(1, 1, 4, 32), q, q, False)
+    with pytest.raises(ValueError):
+        S.make_problem(q, q, q.double(), q, False)
+    p = S.make_problem(q, torch.zeros(1, 1, 6, 64), q, torch.zeros(1, 1, 6, 64), True)
+    assert (p.Nq, p.Nk, p.d_t, p.causal, p.dtype) == (4, 6, 64, 1, S.FP32)
+    assert abs(p.scale_t - 0.125) < 1e-9
+
+
+def test_product_path_has_no_fallback():
+    """The binding never imports the oracle and never computes on the host."""
+    src = open(os.path.join(ROOT, "attention_kl_amd", "streamkl.py")).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    assert "numpy" not in src
