@@ -19,7 +19,9 @@ LIB = os.path.join(PKG, "libstreamkl.so")
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in VGPRs: the softmax/KL VALU reads them with no v_accvgpr_read copies
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-result"]
 DEVICE_SOURCES = ["skl_fwd.hip", "skl_bwd.hip"]
 HOST_SOURCES = ["skl_api.cpp"]

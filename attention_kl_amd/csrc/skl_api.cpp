@@ -34,12 +34,17 @@ int check_problem(const streamkl_problem_t* p, bool* empty) {
   if (p->Nq > kMaxDim || p->Nk > kMaxDim || p->B > kMaxDim || p->H > kMaxDim || p->B * p->H > kMaxDim)
     return STREAMKL_ERR_UNSUPPORTED;
   const int64_t* strides[4] = {p->stride_qt, p->stride_kt, p->stride_qs, p->stride_ks};
+  const int64_t rows[4] = {p->Nq, p->Nk, p->Nq, p->Nk};
   const int es = elt_size(p->dtype);
-  for (const int64_t* s : strides)
+  for (int t = 0; t < 4; ++t) {
+    const int64_t* s = strides[t];
     for (int i = 0; i < 3; ++i) {
       if (s[i] < 0) return STREAMKL_ERR_INVALID;
       if ((s[i] * es) % 16 != 0) return STREAMKL_ERR_UNSUPPORTED;
     }
+    // tiles are read through 32-bit buffer offsets within one (b, h) slice
+    if ((rows[t] + 512) * s[2] * es > kMaxDim) return STREAMKL_ERR_UNSUPPORTED;
+  }
   return STREAMKL_OK;
 }
 

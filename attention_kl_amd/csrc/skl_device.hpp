@@ -64,6 +64,15 @@ __device__ __forceinline__ void mma_chunk<float>(f32x16& acc, const u32x4& a, co
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[e]), __uint_as_float(bv[e]), acc, 0, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets past the end return
+// zero instead of touching memory, so tile loads need no clamping or branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 lds_read8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
 

@@ -59,7 +59,9 @@ typedef enum {
                                    compute, causal with Nq > Nk, non-positive or non-finite scale,
                                    d stride != 1, only one of dq_t/dk_t given                       */
   STREAMKL_ERR_UNSUPPORTED = 2, /* valid but not built: d_t or d_s not in {64, 128}, misaligned base
-                                   pointer or stride (16-byte alignment needed), dtype unknown      */
+                                   pointer or stride (16-byte alignment needed), dtype unknown, or
+                                   one (b, h) slice spanning 2 GiB or more ((N + 512) * n-stride
+                                   * element size must stay below 2^31 bytes)                     */
   STREAMKL_ERR_LAUNCH = 3       /* the HIP launch itself failed (hipGetLastError after launch)     */
 } streamkl_status_t;
 
