@@ -9,12 +9,18 @@
 //   teacher  dS = g_i P_t ((a - b) - (KL_i + LSE_t,i - LSE_s,i))
 //   dQ = scale dS K,   dK = scale dS^T Q     (K, Q of the same side)
 //
-// Two kernels, each owning its output rows so there are no atomics and no
-// workspace: the query-owner kernel keeps 128 query rows in registers and
-// streams key tiles (dQ), the key-owner kernel keeps 128 keys in registers and
-// streams query tiles (dK).  Each recomputes both logit tiles.
+// One kernel template serves both halves.  Each workgroup owns 128 rows of the
+// output (query rows for dQ, key rows for dK) and keeps their Q or K slices in
+// registers as MFMA B operands; the other side streams through a double-buffered
+// LDS ring.  Owning the output rows means no atomics and no workspace.  Both
+// halves recompute both logit tiles.
 //
-// bf16: dS is fed to the MFMA as hi + lo bf16 parts (two products), so its
+// The logit tile is formed with the owned rows as columns, so each lane holds 16
+// streamed rows of one owned row; that register block is directly the A operand
+// of the gradient product (contraction over the streamed rows).  The B operand,
+// the streamed tile read with the streamed rows as the contraction index, comes
+// from the row-major LDS tile through transpose reads, so no transposed copy is
+// stored.  bf16: dS enters the MFMA as hi + lo bf16 parts (two products), so its
 // rounding contributes about 2^-16 relative instead of bf16's 2^-9.
 #include "skl_device.hpp"
 #include "skl_kernels.hpp"
@@ -32,22 +38,32 @@ template <typename T>
 struct BwdTile {
   static constexpr int BW = 128;                       // owned rows per workgroup (4 waves x 32)
   static constexpr int BS = sizeof(T) == 2 ? 64 : 32;  // streamed rows per LDS tile
+  static constexpr int NT = 256;
 };
 
-// Accumulate one 32x32 dS tile (register layout: lane = owned row, 16 streamed rows per
-// lane at acc_row(i, hf)) against the streamed operand X, held transposed in LDS
-// ([feature][streamed row], pitch PX bytes): out[db] += dS . X[:, 32db .. 32db+31].
+template <typename T, int DT, int DS, bool OWN_Q>
+constexpr int bwd_lds_bytes() {
+  return 2 * (TileRing<T, DT, DS, BwdTile<T>::BS, BwdTile<T>::NT>::BYTES + (OWN_Q ? 0 : 4 * BwdTile<T>::BS * 4));
+}
+
+// out[db] += dS . X[:, 32 db .. 32 db + 31] for one 32-row streamed subtile.  dS is in the
+// logit accumulator layout (lane = owned row, element i = streamed row acc_row(i, hf)); X is the
+// streamed tile, row-major in LDS at `xt` with pitch PX bytes.
 template <typename T, int DX, int PX>
-__device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const char* xT, int sub, int hf, int r32) {
+__device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const char* xt, int sub, int lane) {
+  const int hf = lane >> 5, r32 = lane & 31;
   if constexpr (sizeof(T) == 2) {
+    // transpose-read source lane: row 4*hf + (lane%16)/4 of each 16-row chunk, column 16*((lane/16)%2) + 4*(lane%4)
+    const int trow = 4 * hf + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       u32x4 hi, lo;
       split_bf16x8(ds + 8 * c, hi, lo);
 #pragma unroll
       for (int db = 0; db < DX / 32; ++db) {
-        const char* col = xT + (db * 32 + r32) * PX + (sub * 32 + 16 * c + 4 * hf) * 2;
-        const u32x2 p0 = lds_read8(col), p1 = lds_read8(col + 16);
+        const char* p = xt + (sub * 32 + 16 * c + trow) * PX + (32 * db + tcol) * 2;
+        const u32x2 p0 = lds_read_tr16(p), p1 = lds_read_tr16(p + 8 * PX);
         const u32x4 bop = {p0[0], p0[1], p1[0], p1[1]};
         mma_chunk<__bf16>(out[db], hi, bop);
         mma_chunk<__bf16>(out[db], lo, bop);
@@ -55,141 +71,38 @@ __device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const
     }
   } else {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-#pragma unroll
-      for (int db = 0; db < DX / 32; ++db) {
-        const u32x4 bop = lds_read16(xT + (db * 32 + r32) * PX + (sub * 32 + 8 * g4 + 4 * hf) * 4);
-        const uint32_t bv[4] = {bop[0], bop[1], bop[2], bop[3]};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ds[4 * g4 + e], __uint_as_float(bv[e]), out[db], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------------------------
-// Query-owner kernel: dQ of one side for 128 query rows.
-template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdArgs a) {
-  constexpr int BW = BwdTile<T>::BW, BK = BwdTile<T>::BS, NT = 256;
-  constexpr int DX = TEACHER ? DT : DS;
-  constexpr int PT = DT * (int)sizeof(T) + 16, PS = DS * (int)sizeof(T) + 16;
-  constexpr int PX = BK * (int)sizeof(T) + 16;  // pitch of the transposed tile
-  __shared__ __attribute__((aligned(16))) char lds[BK * (PT + PS) + DX * PX];
-  char* lds_kt = lds;
-  char* lds_ks = lds + BK * PT;
-  char* lds_xT = lds + BK * (PT + PS);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, r32 = lane & 31;
-  const int nbh = a.B * a.H;
-  const int nqb = (a.Nq + BW - 1) / BW;
-  const int bh = blockIdx.x % nbh;
-  const int qi = blockIdx.x / nbh;
-  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
-  const int b = bh / a.H, h = bh % a.H;
-  const int off = a.Nk - a.Nq;
-
-  const T* qt = reinterpret_cast<const T*>(a.qt) + b * a.sqt[0] + h * a.sqt[1];
-  const T* kt = reinterpret_cast<const T*>(a.kt) + b * a.skt[0] + h * a.skt[1];
-  const T* qs = reinterpret_cast<const T*>(a.qs) + b * a.sqs[0] + h * a.sqs[1];
-  const T* ks = reinterpret_cast<const T*>(a.ks) + b * a.sks[0] + h * a.sks[1];
-
-  const int q0w = qb * BW + wave * 32;
-  const int qrow = q0w + r32;
-  const bool qvalid = qrow < a.Nq;
-  u32x4 qt_r[DT * sizeof(T) / 32], qs_r[DS * sizeof(T) / 32];
-  load_row_regs<T, DT>(qt_r, qt + (int64_t)qrow * a.sqt[2], qvalid, hf);
-  load_row_regs<T, DS>(qs_r, qs + (int64_t)qrow * a.sqs[2], qvalid, hf);
-
-  const int64_t ro = (int64_t)bh * a.Nq + qrow;
-  const float lse2_t = qvalid ? a.lse_t[ro] * kLog2e : 0.f;
-  const float lse2_s = qvalid ? a.lse_s[ro] * kLog2e : 0.f;
-  const float gq = qvalid ? a.g[ro] : 0.f;
-  float cq = 0.f;  // teacher: KL_i + LSE_t,i - LSE_s,i = sum_j P_t (a - b)
-  if constexpr (TEACHER) cq = qvalid ? a.kl[ro] + a.lse_t[ro] - a.lse_s[ro] : 0.f;
-
-  f32x16 dacc[DX / 32];
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
-
-  const int q_last = min(a.Nq, (qb + 1) * BW) - 1;
-  const int kend = CAUSAL ? min(a.Nk, q_last + off + 1) : a.Nk;
-  const int ntiles = (kend + BK - 1) / BK;
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BK;
-    __syncthreads();
-    if constexpr (TEACHER) {
-      stage_tile<T, DT, BK, NT, PX>(lds_kt, PT, lds_xT, kt + (int64_t)k0 * a.skt[2], a.skt[2], a.Nk - k0, tid);
-      stage_tile<T, DS, BK, NT, 0>(lds_ks, PS, nullptr, ks + (int64_t)k0 * a.sks[2], a.sks[2], a.Nk - k0, tid);
-    } else {
-      stage_tile<T, DT, BK, NT, 0>(lds_kt, PT, nullptr, kt + (int64_t)k0 * a.skt[2], a.skt[2], a.Nk - k0, tid);
-      stage_tile<T, DS, BK, NT, PX>(lds_ks, PS, lds_xT, ks + (int64_t)k0 * a.sks[2], a.sks[2], a.Nk - k0, tid);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int sub = 0; sub < BK / 32; ++sub) {
-      const int kb = k0 + sub * 32;
-      if (kb >= a.Nk) break;
-      if (CAUSAL && kb > q0w + 31 + off) break;
-      f32x16 st = {}, ss = {};
-      tile_dot_lds_a<T, DT>(st, lds_kt + (sub * 32 + r32) * PT, hf, qt_r);
-      tile_dot_lds_a<T, DS>(ss, lds_ks + (sub * 32 + r32) * PS, hf, qs_r);
-      const bool need_mask = (kb + 31 >= a.Nk) || (CAUSAL && kb + 31 > q0w + off);
-      float ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pt = fast_exp2(fmaf(st[i], a.c_t, -lse2_t));
-        if constexpr (TEACHER) {
-          ds[i] = gq * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cq);
-        } else {
-          const float ps = fast_exp2(fmaf(ss[i], a.c_s, -lse2_s));
-          ds[i] = gq * (ps - pt);
-        }
-        if (need_mask) {
-          const int key = kb + acc_row(i, hf);
-          const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + off);
-          ds[i] = ok ? ds[i] : 0.f;
-        }
-      }
-      grad_product<T, DX, PX>(dacc, ds, lds_xT, sub, hf, r32);
-    }
-  }
-
-  const float scale = TEACHER ? a.scale_t : a.scale_s;
-  float* out = a.dq + (int64_t)bh * a.Nq * DX;
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) {
-#pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int q = q0w + acc_row(i, hf);
-      if (q < a.Nq) out[(int64_t)q * DX + db * 32 + r32] = scale * dacc[db][i];
+      const char* p = xt + (sub * 32 + acc_row(i, hf)) * PX + r32 * 4;
+#pragma unroll
+      for (int db = 0; db < DX / 32; ++db)
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ds[i], *reinterpret_cast<const float*>(p + db * 128), out[db],
+                                                        0, 0, 0);
     }
   }
 }
 
-// ----------------------------------------------------------------------------------------------
-// Key-owner kernel: dK of one side for 128 keys.
-template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER>
-__global__ __launch_bounds__(256) void bwd_dk_kernel(const BwdArgs a) {
-  constexpr int BW = BwdTile<T>::BW, BQ = BwdTile<T>::BS, NT = 256;
+// OWN_Q: the workgroup owns query rows and writes dQ; otherwise it owns key rows and writes dK.
+// TEACHER: gradients of the teacher side (dQ_t / dK_t) instead of the student side.
+template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER, bool OWN_Q>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2))) void bwd_kernel(
+    const BwdArgs a) {
+  constexpr int BW = BwdTile<T>::BW, BS = BwdTile<T>::BS, NT = BwdTile<T>::NT;
+  constexpr int NSUB = BS / 32;
   constexpr int DX = TEACHER ? DT : DS;
-  constexpr int PT = DT * (int)sizeof(T) + 16, PS = DS * (int)sizeof(T) + 16;
-  constexpr int PX = BQ * (int)sizeof(T) + 16;
-  __shared__ __attribute__((aligned(16))) char lds[BQ * (PT + PS) + DX * PX + 4 * BQ * 4];
-  char* lds_qt = lds;
-  char* lds_qs = lds + BQ * PT;
-  char* lds_xT = lds + BQ * (PT + PS);
-  float* st_lse_t = reinterpret_cast<float*>(lds + BQ * (PT + PS) + DX * PX);  // log2 units
-  float* st_lse_s = st_lse_t + BQ;
-  float* st_g = st_lse_s + BQ;
-  float* st_c = st_g + BQ;
+  using Ring = TileRing<T, DT, DS, BS, NT>;
+  constexpr int PT = Ring::PA, PS = Ring::PB;
+  constexpr int STAT = OWN_Q ? 0 : 4 * BS * 4;  // streamed-query statistics (key-owner kernel)
+  constexpr int SLOT = Ring::BYTES + STAT;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, r32 = lane & 31;
   const int nbh = a.B * a.H;
+  const int n_own = OWN_Q ? a.Nq : a.Nk, n_str = OWN_Q ? a.Nk : a.Nq;
+  const int nob = (n_own + BW - 1) / BW;
   const int bh = blockIdx.x % nbh;
-  const int kb_i = blockIdx.x / nbh;  // causal: low key blocks see the most queries; they go first
+  const int oi = blockIdx.x / nbh;
+  // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
+  const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
   const int b = bh / a.H, h = bh % a.H;
   const int off = a.Nk - a.Nq;
 
@@ -197,135 +110,204 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(const BwdArgs a) {
   const T* kt = reinterpret_cast<const T*>(a.kt) + b * a.skt[0] + h * a.skt[1];
   const T* qs = reinterpret_cast<const T*>(a.qs) + b * a.sqs[0] + h * a.sqs[1];
   const T* ks = reinterpret_cast<const T*>(a.ks) + b * a.sks[0] + h * a.sks[1];
+  const T* own_t = OWN_Q ? qt : kt;
+  const T* own_s = OWN_Q ? qs : ks;
+  const T* str_t = OWN_Q ? kt : qt;
+  const T* str_s = OWN_Q ? ks : qs;
+  const int64_t own_pt = OWN_Q ? a.sqt[2] : a.skt[2], own_ps = OWN_Q ? a.sqs[2] : a.sks[2];
+  const int64_t str_pt = OWN_Q ? a.skt[2] : a.sqt[2], str_ps = OWN_Q ? a.sks[2] : a.sqs[2];
 
-  const int k0wg = kb_i * BW;
-  const int k0w = k0wg + wave * 32;
-  const int krow = k0w + r32;
-  u32x4 kt_r[DT * sizeof(T) / 32], ks_r[DS * sizeof(T) / 32];
-  load_row_regs<T, DT>(kt_r, kt + (int64_t)krow * a.skt[2], krow < a.Nk, hf);
-  load_row_regs<T, DS>(ks_r, ks + (int64_t)krow * a.sks[2], krow < a.Nk, hf);
+  const int o0 = ob * BW;
+  const int o0w = o0 + wave * 32;
+  const int orow = o0w + r32;
+  const bool ovalid = orow < n_own;
+  u32x4 ot_r[DT * sizeof(T) / 32], os_r[DS * sizeof(T) / 32];
+  load_row_regs<T, DT>(ot_r, own_t + (int64_t)orow * own_pt, ovalid, hf);
+  load_row_regs<T, DS>(os_r, own_s + (int64_t)orow * own_ps, ovalid, hf);
 
-  f32x16 dacc[DX / 32];
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
-
-  // first query that may attend to this block's first key
-  const int qmin = CAUSAL ? max(0, k0wg - off) : 0;
-  const int tfirst = qmin / BQ;
-  const int ntiles = (a.Nq + BQ - 1) / BQ;
   const float* lse_t_bh = a.lse_t + (int64_t)bh * a.Nq;
   const float* lse_s_bh = a.lse_s + (int64_t)bh * a.Nq;
   const float* g_bh = a.g + (int64_t)bh * a.Nq;
   const float* kl_bh = TEACHER ? a.kl + (int64_t)bh * a.Nq : nullptr;
 
-  for (int t = tfirst; t < ntiles; ++t) {
-    const int q0 = t * BQ;
-    __syncthreads();
-    if constexpr (TEACHER) {
-      stage_tile<T, DT, BQ, NT, PX>(lds_qt, PT, lds_xT, qt + (int64_t)q0 * a.sqt[2], a.sqt[2], a.Nq - q0, tid);
-      stage_tile<T, DS, BQ, NT, 0>(lds_qs, PS, nullptr, qs + (int64_t)q0 * a.sqs[2], a.sqs[2], a.Nq - q0, tid);
-    } else {
-      stage_tile<T, DT, BQ, NT, 0>(lds_qt, PT, nullptr, qt + (int64_t)q0 * a.sqt[2], a.sqt[2], a.Nq - q0, tid);
-      stage_tile<T, DS, BQ, NT, PX>(lds_qs, PS, lds_xT, qs + (int64_t)q0 * a.sqs[2], a.sqs[2], a.Nq - q0, tid);
+  // query-owner: this lane's row statistics (log2 units), constant over the key stream
+  float own_lt = 0.f, own_ls = 0.f, own_g = 0.f, own_c = 0.f;
+  if constexpr (OWN_Q) {
+    if (ovalid) {
+      own_lt = lse_t_bh[orow] * kLog2e;
+      own_ls = lse_s_bh[orow] * kLog2e;
+      own_g = g_bh[orow];
+      if constexpr (TEACHER) own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
     }
-    if (tid < BQ) {
-      const int q = q0 + tid;
-      const bool v = q < a.Nq;
-      st_lse_t[tid] = v ? lse_t_bh[q] * kLog2e : 0.f;
-      st_lse_s[tid] = v ? lse_s_bh[q] * kLog2e : 0.f;
-      st_g[tid] = v ? g_bh[q] : 0.f;
-      if constexpr (TEACHER) st_c[tid] = v ? kl_bh[q] + lse_t_bh[q] - lse_s_bh[q] : 0.f;
+  }
+
+  // streamed range
+  int t_begin, t_end;
+  if constexpr (OWN_Q) {
+    const int q_last = min(a.Nq, o0 + BW) - 1;
+    const int kend = CAUSAL ? min(a.Nk, q_last + off + 1) : a.Nk;
+    t_begin = 0;
+    t_end = (kend + BS - 1) / BS;
+  } else {
+    const int qmin = CAUSAL ? max(0, o0 - off) : 0;  // first query that may see this block's first key
+    t_begin = qmin / BS;
+    t_end = (a.Nq + BS - 1) / BS;
+  }
+
+  Ring ring;
+  ring.init(reinterpret_cast<const char*>(str_t), str_pt * (int64_t)sizeof(T), reinterpret_cast<const char*>(str_s),
+            str_ps * (int64_t)sizeof(T), n_str, tid);
+  // key-owner: per-tile statistics of the streamed queries, prefetched with the tile
+  __amdgpu_buffer_rsrc_t r_lt, r_ls, r_g, r_kl;
+  float pf_lt = 0.f, pf_ls = 0.f, pf_g = 0.f, pf_kl = 0.f;
+  if constexpr (!OWN_Q) {
+    r_lt = make_rsrc(lse_t_bh, (uint32_t)a.Nq * 4u);
+    r_ls = make_rsrc(lse_s_bh, (uint32_t)a.Nq * 4u);
+    r_g = make_rsrc(g_bh, (uint32_t)a.Nq * 4u);
+    if constexpr (TEACHER) r_kl = make_rsrc(kl_bh, (uint32_t)a.Nq * 4u);
+  }
+  auto prefetch = [&](int t) {
+    ring.prefetch(t * BS);
+    if constexpr (!OWN_Q) {
+      if (tid < BS) {
+        const int so = t * BS * 4;
+        pf_lt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_lt, tid * 4, so, 0));
+        pf_ls = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ls, tid * 4, so, 0));
+        pf_g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_g, tid * 4, so, 0));
+        if constexpr (TEACHER)
+          pf_kl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_kl, tid * 4, so, 0));
+      }
     }
-    __syncthreads();
+  };
+  auto commit = [&](int t) {
+    char* slot = lds + (t & 1) * SLOT;
+    ring.commit(slot);
+    if constexpr (!OWN_Q) {
+      if (tid < BS) {
+        float* st = reinterpret_cast<float*>(slot + Ring::BYTES);
+        st[tid] = pf_lt * kLog2e;
+        st[BS + tid] = pf_ls * kLog2e;
+        st[2 * BS + tid] = pf_g;  // zero past the last query: those rows contribute nothing
+        st[3 * BS + tid] = pf_kl + pf_lt - pf_ls;
+      }
+    }
+  };
+
+  f32x16 dacc[DX / 32];
 #pragma unroll
-    for (int sub = 0; sub < BQ / 32; ++sub) {
-      const int qb = q0 + sub * 32;
-      if (qb >= a.Nq) break;
-      if (CAUSAL && k0w > qb + 31 + off) continue;  // every key of this wave is past these rows' reach
+  for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
+
+  if (t_begin < t_end) prefetch(t_begin);
+  // (slot t&1 last held tile t-2, whose reads all finished before the barrier that published t-1)
+  for (int t = t_begin; t < t_end; ++t) {
+    commit(t);
+    if (t + 1 < t_end) prefetch(t + 1);
+    __syncthreads();
+    const char* slot = lds + (t & 1) * SLOT;
+    const char* tile_t = slot;
+    const char* tile_s = slot + BS * PT;
+    const float* stats = reinterpret_cast<const float*>(slot + Ring::BYTES);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int sb = t * BS + sub * 32;  // first streamed row of this subtile
+      // allowed(q, k): k <= q + off when causal; classify the 32 x 32 block of this wave
+      bool skip, full;
+      if constexpr (OWN_Q) {
+        skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
+        full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
+      } else {
+        skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
+        full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
+      }
+      if (skip) continue;
       f32x16 st = {}, ss = {};
-      // S = Q K^T: rows = the tile's queries (LDS), columns = this wave's keys (registers)
-      tile_dot_lds_a<T, DT>(st, lds_qt + (sub * 32 + r32) * PT, hf, kt_r);
-      tile_dot_lds_a<T, DS>(ss, lds_qs + (sub * 32 + r32) * PS, hf, ks_r);
-      const bool need_mask = (qb + 31 >= a.Nq) || (CAUSAL && k0w + 31 > qb + off);
+      tile_dot_lds_a<T, DT>(st, tile_t + (sub * 32 + r32) * PT, hf, ot_r);
+      tile_dot_lds_a<T, DS>(ss, tile_s + (sub * 32 + r32) * PS, hf, os_r);
       float ds[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int ql = sub * 32 + 8 * g4 + 4 * hf;  // first of 4 consecutive tile queries
-        const f32x4 lt4 = *reinterpret_cast<const f32x4*>(st_lse_t + ql);
-        const f32x4 ls4 = *reinterpret_cast<const f32x4*>(st_lse_s + ql);
-        const f32x4 g4v = *reinterpret_cast<const f32x4*>(st_g + ql);
-        f32x4 c4 = {};
-        if constexpr (TEACHER) c4 = *reinterpret_cast<const f32x4*>(st_c + ql);
+        f32x4 lt4, ls4, gg4, cc4;
+        if constexpr (OWN_Q) {
+          lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
+          ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
+          gg4 = f32x4{own_g, own_g, own_g, own_g};
+          cc4 = f32x4{own_c, own_c, own_c, own_c};
+        } else {
+          const int ql = sub * 32 + 8 * g4 + 4 * hf;
+          lt4 = *reinterpret_cast<const f32x4*>(stats + ql);
+          ls4 = *reinterpret_cast<const f32x4*>(stats + BS + ql);
+          gg4 = *reinterpret_cast<const f32x4*>(stats + 2 * BS + ql);
+          cc4 = TEACHER ? *reinterpret_cast<const f32x4*>(stats + 3 * BS + ql) : f32x4{};
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
           const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
           float v;
           if constexpr (TEACHER) {
-            v = g4v[e] * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - c4[e]);
+            v = gg4[e] * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
           } else {
             const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
-            v = g4v[e] * (ps - pt);
+            v = gg4[e] * (ps - pt);
           }
-          if (need_mask) {
-            const int q = q0 + ql + e;
-            const bool ok = q < a.Nq && (!CAUSAL || krow <= q + off);
+          if (!full) {
+            const int sr = sb + acc_row(i, hf);
+            const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
             v = ok ? v : 0.f;
           }
           ds[i] = v;
         }
       }
-      grad_product<T, DX, PX>(dacc, ds, lds_xT, sub, hf, r32);
+      if constexpr (TEACHER)
+        grad_product<T, DX, PT>(dacc, ds, tile_t, sub, lane);
+      else
+        grad_product<T, DX, PS>(dacc, ds, tile_s, sub, lane);
     }
   }
 
   const float scale = TEACHER ? a.scale_t : a.scale_s;
-  float* out = a.dk + (int64_t)bh * a.Nk * DX;
+  float* out = (OWN_Q ? a.dq : a.dk) + (int64_t)bh * n_own * DX;
 #pragma unroll
   for (int db = 0; db < DX / 32; ++db) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int k = k0w + acc_row(i, hf);
-      if (k < a.Nk) out[(int64_t)k * DX + db * 32 + r32] = scale * dacc[db][i];
+      const int r = o0w + acc_row(i, hf);
+      if (r < n_own) out[(int64_t)r * DX + db * 32 + r32] = scale * dacc[db][i];
     }
   }
 }
 
 // ----------------------------------------------------------------------------------------------
-template <typename T, int DT, int DS, bool C, bool TE>
-static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
-  const int64_t nblk = (int64_t)((a.Nq + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * a.H;
+template <typename T, int DT, int DS, bool C, bool TE, bool OWN_Q>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const int n_own = OWN_Q ? a.Nq : a.Nk;
+  const int64_t nblk = (int64_t)((n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * a.H;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, DT, DS, C, TE>), dim3((unsigned)nblk), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename T, int DT, int DS, bool C, bool TE>
-static hipError_t launch_dk_t(const BwdArgs& a, hipStream_t s) {
-  const int64_t nblk = (int64_t)((a.Nk + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * a.H;
-  if (nblk <= 0) return hipSuccess;
-  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dk_kernel<T, DT, DS, C, TE>), dim3((unsigned)nblk), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <bool DQ, typename T, int DT, int DS>
-static hipError_t bwd_ct(const BwdArgs& a, bool causal, bool teacher, hipStream_t s) {
-  if (DQ) {
-    if (causal) return teacher ? launch_dq_t<T, DT, DS, true, true>(a, s) : launch_dq_t<T, DT, DS, true, false>(a, s);
-    return teacher ? launch_dq_t<T, DT, DS, false, true>(a, s) : launch_dq_t<T, DT, DS, false, false>(a, s);
+  constexpr int lds = bwd_lds_bytes<T, DT, DS, OWN_Q>();
+  auto kern = bwd_kernel<T, DT, DS, C, TE, OWN_Q>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
   }
-  if (causal) return teacher ? launch_dk_t<T, DT, DS, true, true>(a, s) : launch_dk_t<T, DT, DS, true, false>(a, s);
-  return teacher ? launch_dk_t<T, DT, DS, false, true>(a, s) : launch_dk_t<T, DT, DS, false, false>(a, s);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(BwdTile<T>::NT), lds, s, a);
+  return hipGetLastError();
 }
 
-template <bool DQ, typename T>
+template <bool OWN_Q, typename T, int DT, int DS>
+static hipError_t bwd_ct(const BwdArgs& a, bool causal, bool teacher, hipStream_t s) {
+  if (causal)
+    return teacher ? launch_bwd_t<T, DT, DS, true, true, OWN_Q>(a, s) : launch_bwd_t<T, DT, DS, true, false, OWN_Q>(a, s);
+  return teacher ? launch_bwd_t<T, DT, DS, false, true, OWN_Q>(a, s) : launch_bwd_t<T, DT, DS, false, false, OWN_Q>(a, s);
+}
+
+template <bool OWN_Q, typename T>
 static hipError_t bwd_d(const BwdArgs& a, int dt, int ds, bool causal, bool teacher, hipStream_t s) {
-  if (dt == 128 && ds == 128) return bwd_ct<DQ, T, 128, 128>(a, causal, teacher, s);
-  if (dt == 128 && ds == 64) return bwd_ct<DQ, T, 128, 64>(a, causal, teacher, s);
-  if (dt == 64 && ds == 128) return bwd_ct<DQ, T, 64, 128>(a, causal, teacher, s);
-  if (dt == 64 && ds == 64) return bwd_ct<DQ, T, 64, 64>(a, causal, teacher, s);
+  if (dt == 128 && ds == 128) return bwd_ct<OWN_Q, T, 128, 128>(a, causal, teacher, s);
+  if (dt == 128 && ds == 64) return bwd_ct<OWN_Q, T, 128, 64>(a, causal, teacher, s);
+  if (dt == 64 && ds == 128) return bwd_ct<OWN_Q, T, 64, 128>(a, causal, teacher, s);
+  if (dt == 64 && ds == 64) return bwd_ct<OWN_Q, T, 64, 64>(a, causal, teacher, s);
   return hipErrorInvalidValue;
 }
 

@@ -137,6 +137,69 @@ __device__ __forceinline__ void stage_tile(char* lds, int pitch, char* lds_t, co
   }
 }
 
+// Register-prefetched, double-buffered LDS ring for a tile of ROWS rows of two row-major
+// tensors A (DA features) and B (DB features) of element type T.  Rows are read with buffer
+// loads (zero past `bytes` of each tensor), so no load needs a bounds branch.  Layout of one
+// ring slot: A rows at pitch PA, then B rows at pitch PB, both padded by 16 bytes.
+template <typename T, int DA, int DB, int ROWS, int NT>
+struct TileRing {
+  static constexpr int PA = DA * (int)sizeof(T) + 16, PB = DB * (int)sizeof(T) + 16;
+  static constexpr int NCA = DA * (int)sizeof(T) / 16, NCB = DB * (int)sizeof(T) / 16;
+  static constexpr int NLA = ROWS * NCA / NT, NLB = ROWS * NCB / NT;
+  static constexpr int BYTES = ROWS * (PA + PB);
+  static_assert(ROWS * NCA % NT == 0 && ROWS * NCB % NT == 0, "tile must split evenly over the workgroup");
+
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int pitch_a, pitch_b;  // global row pitch in bytes
+  int vo_a[NLA], vo_b[NLB], lo_a[NLA], lo_b[NLB];
+  u32x4 pa[NLA], pb[NLB];
+
+  __device__ __forceinline__ void init(const char* a, int64_t a_pitch, const char* b, int64_t b_pitch, int nrows,
+                                       int tid) {
+    pitch_a = (int)a_pitch;
+    pitch_b = (int)b_pitch;
+    ra = make_rsrc(a, (uint32_t)((nrows - 1) * a_pitch + DA * (int)sizeof(T)));
+    rb = make_rsrc(b, (uint32_t)((nrows - 1) * b_pitch + DB * (int)sizeof(T)));
+#pragma unroll
+    for (int j = 0; j < NLA; ++j) {
+      const int idx = tid + j * NT, r = idx / NCA, c = idx % NCA;
+      vo_a[j] = r * pitch_a + c * 16;
+      lo_a[j] = r * PA + c * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < NLB; ++j) {
+      const int idx = tid + j * NT, r = idx / NCB, c = idx % NCB;
+      vo_b[j] = r * pitch_b + c * 16;
+      lo_b[j] = ROWS * PA + r * PB + c * 16;
+    }
+  }
+  // Global -> registers for the tile starting at row `row0`.
+  __device__ __forceinline__ void prefetch(int row0) {
+    const int sa = row0 * pitch_a, sb = row0 * pitch_b;
+#pragma unroll
+    for (int j = 0; j < NLA; ++j) pa[j] = buffer_load16(ra, vo_a[j], sa);
+#pragma unroll
+    for (int j = 0; j < NLB; ++j) pb[j] = buffer_load16(rb, vo_b[j], sb);
+  }
+  // Registers -> LDS slot at `base`.
+  __device__ __forceinline__ void commit(char* base) {
+#pragma unroll
+    for (int j = 0; j < NLA; ++j) *reinterpret_cast<u32x4*>(base + lo_a[j]) = pa[j];
+#pragma unroll
+    for (int j = 0; j < NLB; ++j) *reinterpret_cast<u32x4*>(base + lo_b[j]) = pb[j];
+  }
+};
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, source
+// lane r supplies the address of 4 consecutive 16-bit elements; result lane i receives
+// element i%4 of source lanes i/4, i/4+4, i/4+8, i/4+12.  Pointing source lane r at row
+// R0 + r/4, column C0 + 4(r%4) of a row-major tile hands lane i rows R0..R0+3 of column C0 + i.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Split 8 fp32 values into bf16 hi + lo parts (v ~= hi + lo to about 2^-16 relative).
 __device__ __forceinline__ void split_bf16x8(const float* v, u32x4& hi, u32x4& lo) {
   bf16x8 h, l;
