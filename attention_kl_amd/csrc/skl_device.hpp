@@ -190,6 +190,88 @@ struct TileRing {
   }
 };
 
+// ---------------------------------------------------------------------------------------------
+// Swizzled LDS tiles filled by buffer->LDS DMA (buffer_load_dwordx4 ... lds).
+//
+// A tile holds ROWS rows of RB bytes, unpadded; logical 16-byte chunk c of row r is stored at
+// physical chunk c ^ swz(r).  One DMA instruction writes 64 lanes x 16 bytes contiguously at the
+// wave's LDS address, so the swizzle is applied on the global side: each lane fetches the logical
+// chunk that belongs at its physical slot.  swz makes both access patterns used here
+// conflict-free for RB >= 256: 16 consecutive rows reading one logical chunk (MFMA operand reads),
+// and the transpose read (rows R0..R0+3, R0 % 4 == 0, chunks C0 and C0+1, C0 even).
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (RB >= 256)
+    return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
+  else
+    return (r >> 1) & 7;  // 128-byte rows: two rows share one 256-byte bank window
+}
+
+template <int ROWS, int RB, int NT>
+struct DmaTile {
+  static constexpr int BYTES = ROWS * RB;
+  static constexpr int NW = NT / 64;
+  static constexpr int NI = BYTES / (NW * 1024);  // DMA instructions per wave per tile
+  static_assert(BYTES % (NW * 1024) == 0, "tile must split into whole 1 KB wave writes");
+  int vo[NI];  // per-lane global byte offset inside the tile (relative to its first row)
+
+  __device__ __forceinline__ void init(int64_t pitch, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int o = (j * NW + wave) * 1024 + 16 * lane;
+      const int pr = o / RB, pc = (o % RB) / 16;
+      vo[j] = pr * (int)pitch + ((pc ^ swz<RB>(pr)) * 16);
+    }
+  }
+  // Queue the tile whose first row sits at byte offset `soff` of the buffer into LDS at `dst`.
+  // Issued as inline asm so that the compiler does not track these LDS writes: callers order
+  // them with explicit vmcnt waits and barriers (the destination slot is never read while a DMA
+  // into it can be in flight).  The asm has no output register.
+  __device__ __forceinline__ void issue(const u32x4& rsrc, int soff, char* dst, int wave) const {
+    const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)dst);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * 1024));
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(m0v), "v"(vo[j]), "s"(rsrc), "s"(soff)
+                   : "memory", "m0");
+    }
+  }
+};
+
+// Raw buffer descriptor words (base, stride 0, num_records = bytes, gfx9 data-format word)
+// for DMA issued from inline asm.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Wait until at most N buffer loads (including LDS DMA) of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Per-lane LDS byte offsets of the MFMA operand chunks of row `row` of a swizzled tile: chunk
+// 2c + hf for step c (the same chunk-to-k mapping as the register operands).
+template <int RB, int NSTEP>
+__device__ __forceinline__ void swz_operand_offsets(int* off, int row, int hf) {
+  const int s = swz<RB>(row) ^ hf;  // (2c + hf) ^ swz == 2c ^ (hf ^ swz)
+#pragma unroll
+  for (int c = 0; c < NSTEP; ++c) off[c] = row * RB + (((2 * c) ^ s) << 4);
+}
+
+// 32x32 logit tile from a swizzled LDS tile (A rows) and register B rows.
+template <typename T, int D>
+__device__ __forceinline__ void tile_dot_swz(f32x16& acc, const char* tile, const int* off, const u32x4* b_regs) {
+  constexpr int NC = D * (int)sizeof(T) / 16;
+#pragma unroll
+  for (int c = 0; c < NC / 2; ++c) mma_chunk<T>(acc, lds_read16(tile + off[c]), b_regs[c]);
+}
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, source
 // lane r supplies the address of 4 consecutive 16-bit elements; result lane i receives
 // element i%4 of source lanes i/4, i/4+4, i/4+8, i/4+12.  Pointing source lane r at row

@@ -29,49 +29,13 @@
 
 namespace skl {
 
-// Scheduling hint for one pipeline step: spread the MFMAs of the next subtile
-// (with their LDS operand reads one step ahead) through the VALU work of the
-// current one, so a single wavefront keeps the matrix core and the VALU busy.
-#ifndef SKL_FWD_SCHED
-#define SKL_FWD_SCHED 1
-#endif
-#if SKL_FWD_SCHED == 1
-#define SKL_FWD_INTERLEAVE()                                          \
-  do {                                                                \
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                \
-    _Pragma("unroll") for (int _k = 0; _k < 16; ++_k) {               \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              \
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);              \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              \
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);              \
-    }                                                                 \
-  } while (0)
-#elif SKL_FWD_SCHED == 2
-#define SKL_FWD_INTERLEAVE()                                          \
-  do {                                                                \
-    _Pragma("unroll") for (int _k = 0; _k < 16; ++_k) {               \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              \
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);             \
-    }                                                                 \
-  } while (0)
-#else
-#define SKL_FWD_INTERLEAVE() \
-  do {                       \
-  } while (0)
-#endif
-
 template <typename T>
 struct FwdTile {
-  static constexpr int BQ = 128;                       // query rows per workgroup
-  static constexpr int BK = sizeof(T) == 2 ? 64 : 32;  // keys per LDS tile
+  static constexpr int BQ = 128;  // query rows per workgroup (4 wavefronts x 32)
+  static constexpr int BK = 32;   // keys per LDS tile (one 32 x 32 logit block per wavefront)
+  static constexpr int NBUF = 3;  // LDS ring depth: tiles t+1 and t+2 are in flight while t is used
   static constexpr int NT = 256;
 };
-
-template <typename T, int DT, int DS>
-constexpr int fwd_lds_bytes() {
-  return 2 * FwdTile<T>::BK * ((DT + DS) * (int)sizeof(T) + 32);
-}
 
 // Per-lane running state of one query row over the keys this lane half sees.
 struct RowState {
@@ -110,16 +74,19 @@ __device__ __forceinline__ void online_update(RowState& s, const f32x16& st, con
 }
 
 template <typename T, int DT, int DS, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2))) void fwd_kernel(const FwdArgs a) {
-  constexpr int BQ = FwdTile<T>::BQ, BK = FwdTile<T>::BK, NT = FwdTile<T>::NT;
-  constexpr int NSUB = BK / 32;
-  constexpr int PT = DT * (int)sizeof(T) + 16;  // padded LDS row pitch (bytes)
-  constexpr int PS = DS * (int)sizeof(T) + 16;
-  constexpr int TILE = BK * (PT + PS);  // bytes of one K_t + K_s tile in LDS
-  constexpr int NCT = DT * (int)sizeof(T) / 16, NCS = DS * (int)sizeof(T) / 16;  // 16-byte chunks per row
-  constexpr int NLT = BK * NCT / NT, NLS = BK * NCS / NT;  // chunks per thread per tile
-  static_assert(BK * NCT % NT == 0 && BK * NCS % NT == 0, "tile must split evenly over the workgroup");
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1, 3))) void fwd_kernel(
+    const FwdArgs a) {
+  constexpr int BQ = FwdTile<T>::BQ, BK = FwdTile<T>::BK, NBUF = FwdTile<T>::NBUF, NT = FwdTile<T>::NT;
+  constexpr int RBT = DT * (int)sizeof(T), RBS = DS * (int)sizeof(T);  // row bytes
+  constexpr int TILE = BK * (RBT + RBS);                                  // one K_t + K_s tile
+  constexpr int NCT = RBT / 16, NCS = RBS / 16;                           // 16-byte chunks per row
+  using DmaT = DmaTile<BK, RBT, NT>;
+  using DmaS = DmaTile<BK, RBS, NT>;
+  constexpr int NI = DmaT::NI + DmaS::NI;  // DMA instructions per thread per tile
+  // one array per ring slot: distinct objects let the compiler see that a DMA into one slot never
+  // aliases reads of another, so it adds no wait beyond the explicit ones below
+  __shared__ __attribute__((aligned(1024))) char slot0[TILE], slot1[TILE], slot2[TILE];
+  static_assert(NBUF == 3, "one named array per ring slot");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, r32 = lane & 31;
   const int nbh = a.B * a.H;
@@ -148,121 +115,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   const int q_last = min(a.Nq, q0 + BQ) - 1;
   const int kend = CAUSAL ? min(a.Nk, q_last + off + 1) : a.Nk;
   const int ntiles = (kend + BK - 1) / BK;
-  // tiles whose every key is allowed for every row of the workgroup
-  const int t_full = min(ntiles, (CAUSAL ? min(a.Nk, q0 + off + 1) : a.Nk) / BK);
 
-  // ---- K tile prefetch: registers one tile ahead, through buffer loads that return zero past
-  // the last key (a scalar tile offset plus a loop-invariant per-lane offset: no address math)
-  const __amdgpu_buffer_rsrc_t rk_t = make_rsrc(kt, (uint32_t)((a.Nk - 1) * kt_pitch + DT * (int)sizeof(T)));
-  const __amdgpu_buffer_rsrc_t rk_s = make_rsrc(ks, (uint32_t)((a.Nk - 1) * ks_pitch + DS * (int)sizeof(T)));
-  int vo_t[NLT], vo_s[NLS];
-#pragma unroll
-  for (int j = 0; j < NLT; ++j) {
-    const int idx = tid + j * NT;
-    vo_t[j] = (idx / NCT) * (int)kt_pitch + (idx % NCT) * 16;
-  }
-#pragma unroll
-  for (int j = 0; j < NLS; ++j) {
-    const int idx = tid + j * NT;
-    vo_s[j] = (idx / NCS) * (int)ks_pitch + (idx % NCS) * 16;
-  }
-  u32x4 pf_t[NLT], pf_s[NLS];
-  auto prefetch = [&](int tile) {
-    const int so_t = tile * BK * (int)kt_pitch, so_s = tile * BK * (int)ks_pitch;
-#pragma unroll
-    for (int j = 0; j < NLT; ++j) pf_t[j] = buffer_load16(rk_t, vo_t[j], so_t);
-#pragma unroll
-    for (int j = 0; j < NLS; ++j) pf_s[j] = buffer_load16(rk_s, vo_s[j], so_s);
+  // K tiles: buffer->LDS DMA (zero past the last key) into a NBUF-deep ring, two tiles ahead
+  const u32x4 rk_t = rsrc_words(kt, (uint32_t)((a.Nk - 1) * kt_pitch + RBT));
+  const u32x4 rk_s = rsrc_words(ks, (uint32_t)((a.Nk - 1) * ks_pitch + RBS));
+  DmaT dma_t;
+  DmaS dma_s;
+  dma_t.init(kt_pitch, wave, lane);
+  dma_s.init(ks_pitch, wave, lane);
+  auto slot_ptr = [&](int slot) -> char* { return slot == 0 ? slot0 : (slot == 1 ? slot1 : slot2); };
+  auto issue = [&](int tile, int slot) {
+    dma_t.issue(rk_t, tile * BK * (int)kt_pitch, slot_ptr(slot), wave);
+    dma_s.issue(rk_s, tile * BK * (int)ks_pitch, slot_ptr(slot) + BK * RBT, wave);
   };
-  auto commit = [&](int tile) {
-    char* base = lds + (tile & 1) * TILE;
-#pragma unroll
-    for (int j = 0; j < NLT; ++j) {
-      const int idx = tid + j * NT, r = idx / NCT, c = idx % NCT;
-      *reinterpret_cast<u32x4*>(base + r * PT + c * 16) = pf_t[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NLS; ++j) {
-      const int idx = tid + j * NT, r = idx / NCS, c = idx % NCS;
-      *reinterpret_cast<u32x4*>(base + BK * PT + r * PS + c * 16) = pf_s[j];
-    }
-  };
-  auto logits = [&](f32x16& st, f32x16& ss, int tile, int sub) {
-    const char* base = lds + (tile & 1) * TILE;
-    st = f32x16{};
-    ss = f32x16{};
-    tile_dot_lds_a<T, DT>(st, base + (sub * 32 + r32) * PT, hf, qt_r);
-    tile_dot_lds_a<T, DS>(ss, base + BK * PT + (sub * 32 + r32) * PS, hf, qs_r);
-  };
-  auto update_full = [&](const f32x16& st, const f32x16& ss) {
-    float dif[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dif[i] = fmaf(ss[i], -a.ratio, st[i]);
-    online_update(rs, st, ss, dif, a.c_t, a.c_s);
-  };
+  // this lane's operand chunk offsets (row r32 of a tile), loop-invariant
+  int off_t[NCT / 2], off_s[NCS / 2];
+  swz_operand_offsets<RBT, NCT / 2>(off_t, r32, hf);
+  swz_operand_offsets<RBS, NCS / 2>(off_s, r32, hf);
 
-  if (ntiles > 0) prefetch(0);
-
-  // ---- pipelined loop over the fully allowed tiles.  Each step is straight-line code that issues
-  // the MFMAs of the next key subtile and runs the exp/VALU update of the current one.
-  if (t_full > 0) {
-    commit(0);
-    if (ntiles > 1) prefetch(1);
-    __syncthreads();
-    f32x16 cur_t, cur_s, nxt_t, nxt_s;
-    logits(cur_t, cur_s, 0, 0);
-    for (int t = 0; t < t_full; ++t) {
+  // The compiler cannot see the DMAs in the hardware's vmcnt; retire every load of its own now,
+  // so that none of its waits lands inside the loop, where it would also drain the DMA ring.
+  wait_vmcnt<0>();
+  issue(0, 0);
+  issue(1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
+  // One step per tile; the loop is unrolled by the ring depth so every LDS address is a
+  // per-lane base plus an immediate.
+  for (int t0 = 0; t0 < ntiles; t0 += NBUF) {
 #pragma unroll
-      for (int sub = 1; sub < NSUB; ++sub) {
-        logits(nxt_t, nxt_s, t, sub);
-        SKL_FWD_INTERLEAVE();
-        update_full(cur_t, cur_s);
-        cur_t = nxt_t;
-        cur_s = nxt_s;
+    for (int u = 0; u < NBUF; ++u) {
+      const int t = t0 + u;
+      if (t < ntiles) {
+        wait_vmcnt<NI>();  // tile t has landed (tile t+1 may still be in flight)
+        __syncthreads();   // ... for every wave; and every wave is done with tile t-1
+        issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
+        const char* tile = slot_ptr(u);
+        const int kb = t * BK;
+        const bool skip = CAUSAL && kb > q0w + 31 + off;  // no row of this wavefront reaches these keys
+        if (!skip) {
+          f32x16 st = {}, ss = {};
+          tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
+          tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
+          float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
+#pragma unroll
+          for (int i = 0; i < 16; ++i) dif[i] = fmaf(ss[i], -a.ratio, st[i]);
+          const bool full = kb + 31 < a.Nk && (!CAUSAL || kb + 31 <= q0w + off);
+          // two separate calls: the unmasked path never merges with the masked one, so the
+          // logit registers are not copied on every step
+          if (full) {
+            online_update(rs, st, ss, dif, a.c_t, a.c_s);
+          } else {
+            f32x16 mt, ms;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb + acc_row(i, hf);
+              const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + off);
+              mt[i] = ok ? st[i] : -INFINITY;
+              ms[i] = ok ? ss[i] : -INFINITY;
+            }
+            online_update(rs, mt, ms, dif, a.c_t, a.c_s);
+          }
+        }
       }
-      // publish tile t+1 (its buffer last held tile t-1, whose reads ended before the previous
-      // barrier).  Unconditional so the step stays one basic block: past the last tile the
-      // prefetch returns zeros and the commit fills a buffer no wave reads.
-      commit(t + 1);
-      prefetch(t + 2);
-      __syncthreads();
-      // first subtile of tile t+1; past the last full tile the result is discarded
-      logits(nxt_t, nxt_s, t + 1, 0);
-      SKL_FWD_INTERLEAVE();
-      update_full(cur_t, cur_s);
-      cur_t = nxt_t;
-      cur_s = nxt_s;
     }
   }
-
-  // ---- masked tail: causal diagonal tiles and the ragged end
-  // (the pipelined loop already published tile t_full; buffer t&1 of a later tile last held tile
-  // t-2, whose reads all finished before the barrier that published tile t-1)
-  for (int t = t_full; t < ntiles; ++t) {
-    if (t > t_full || t_full == 0) {
-      commit(t);
-      if (t + 1 < ntiles) prefetch(t + 1);
-      __syncthreads();
-    }
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      const int kb = t * BK + sub * 32;
-      if (kb >= a.Nk) break;
-      if (CAUSAL && kb > q0w + 31 + off) break;  // no row of this wavefront reaches these keys
-      f32x16 st, ss;
-      logits(st, ss, t, sub);
-      float dif[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dif[i] = fmaf(ss[i], -a.ratio, st[i]);
-        const int key = kb + acc_row(i, hf);
-        const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + off);
-        st[i] = ok ? st[i] : -INFINITY;
-        ss[i] = ok ? ss[i] : -INFINITY;
-      }
-      online_update(rs, st, ss, dif, a.c_t, a.c_s);
-    }
-  }
+  wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS when it exits
 
   // Merge the two half-row states (disjoint key subsets) of each query row.
   const float o_mt = __shfl_xor(rs.m_t, 32), o_lt = __shfl_xor(rs.l_t, 32), o_acc = __shfl_xor(rs.acc, 32);
@@ -289,14 +205,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const int64_t nblk = nqb * a.B * a.H;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  constexpr int lds = fwd_lds_bytes<T, DT, DS>();
-  auto kern = fwd_kernel<T, DT, DS, C>;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(FwdTile<T>::NT), lds, s, a);
+  hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s, a);
   return hipGetLastError();
 }
 
