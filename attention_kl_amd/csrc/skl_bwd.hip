@@ -36,34 +36,46 @@ __device__ __forceinline__ float scaled_diff(float a, float sa, float b, float s
 
 template <typename T>
 struct BwdTile {
-  static constexpr int BW = 128;                       // owned rows per workgroup (4 waves x 32)
-  static constexpr int BS = sizeof(T) == 2 ? 64 : 32;  // streamed rows per LDS tile
+  static constexpr int BW = 128;  // owned rows per workgroup (4 waves x 32)
+  static constexpr int BS = 32;   // streamed rows per LDS tile (one 32 x 32 block per wave)
+  static constexpr int NBUF = 3;  // LDS ring depth: tiles t+1, t+2 in flight while t is used
   static constexpr int NT = 256;
 };
 
-template <typename T, int DT, int DS, bool OWN_Q>
-constexpr int bwd_lds_bytes() {
-  return 2 * (TileRing<T, DT, DS, BwdTile<T>::BS, BwdTile<T>::NT>::BYTES + (OWN_Q ? 0 : 4 * BwdTile<T>::BS * 4));
+// Per-lane byte offsets, inside a swizzled streamed tile of RB-byte rows, of the transpose-read
+// sources of the gradient product: pass s in {0, 1} covers rows 8s + 4 hf + (lane%16)/4 (plus 16c
+// for chunk c, an immediate), column 32 db + 16 ((lane/16)%2) + 4 (lane%4).
+template <int RB, int DX>
+__device__ __forceinline__ void tr_offsets(int (*off)[DX / 32], int lane) {
+  const int trow = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // element column inside a 32-wide block
+#pragma unroll
+  for (int sp = 0; sp < 2; ++sp) {
+    const int row = trow + 8 * sp;
+#pragma unroll
+    for (int db = 0; db < DX / 32; ++db) {
+      const int chunk = 4 * db + (tcol >> 3);
+      off[sp][db] = row * RB + ((chunk ^ swz<RB>(row)) << 4) + (tcol & 7) * 2;
+    }
+  }
 }
 
-// out[db] += dS . X[:, 32 db .. 32 db + 31] for one 32-row streamed subtile.  dS is in the
-// logit accumulator layout (lane = owned row, element i = streamed row acc_row(i, hf)); X is the
-// streamed tile, row-major in LDS at `xt` with pitch PX bytes.
-template <typename T, int DX, int PX>
-__device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const char* xt, int sub, int lane) {
+// out[db] += dS . X[:, 32 db .. 32 db + 31] for one 32-row streamed tile.  dS is in the logit
+// accumulator layout (lane = owned row, element i = streamed row acc_row(i, hf)); X is the
+// streamed tile of the side being differentiated, row-major and swizzled in LDS at `xt`.
+template <typename T, int DX, int RB>
+__device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const char* xt, const int (*toff)[DX / 32],
+                                             int lane) {
   const int hf = lane >> 5, r32 = lane & 31;
   if constexpr (sizeof(T) == 2) {
-    // transpose-read source lane: row 4*hf + (lane%16)/4 of each 16-row chunk, column 16*((lane/16)%2) + 4*(lane%4)
-    const int trow = 4 * hf + ((lane & 15) >> 2);
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       u32x4 hi, lo;
       split_bf16x8(ds + 8 * c, hi, lo);
 #pragma unroll
       for (int db = 0; db < DX / 32; ++db) {
-        const char* p = xt + (sub * 32 + 16 * c + trow) * PX + (32 * db + tcol) * 2;
-        const u32x2 p0 = lds_read_tr16(p), p1 = lds_read_tr16(p + 8 * PX);
+        const u32x2 p0 = lds_read_tr16(xt + toff[0][db] + 16 * c * RB);
+        const u32x2 p1 = lds_read_tr16(xt + toff[1][db] + 16 * c * RB);
         const u32x4 bop = {p0[0], p0[1], p1[0], p1[1]};
         mma_chunk<__bf16>(out[db], hi, bop);
         mma_chunk<__bf16>(out[db], lo, bop);
@@ -72,11 +84,14 @@ __device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const char* p = xt + (sub * 32 + acc_row(i, hf)) * PX + r32 * 4;
+      const int row = acc_row(i, hf);
 #pragma unroll
-      for (int db = 0; db < DX / 32; ++db)
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ds[i], *reinterpret_cast<const float*>(p + db * 128), out[db],
-                                                        0, 0, 0);
+      for (int db = 0; db < DX / 32; ++db) {
+        const int col = 32 * db + r32;  // fp32 element column; 4 per 16-byte chunk
+        const float x = *reinterpret_cast<const float*>(xt + row * RB + ((((col >> 2) ^ swz<RB>(row))) << 4) +
+                                                        (col & 3) * 4);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ds[i], x, out[db], 0, 0, 0);
+      }
     }
   }
 }
@@ -86,14 +101,20 @@ __device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const
 template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER, bool OWN_Q>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2))) void bwd_kernel(
     const BwdArgs a) {
-  constexpr int BW = BwdTile<T>::BW, BS = BwdTile<T>::BS, NT = BwdTile<T>::NT;
-  constexpr int NSUB = BS / 32;
+  constexpr int BW = BwdTile<T>::BW, BS = BwdTile<T>::BS, NBUF = BwdTile<T>::NBUF, NT = BwdTile<T>::NT;
   constexpr int DX = TEACHER ? DT : DS;
-  using Ring = TileRing<T, DT, DS, BS, NT>;
-  constexpr int PT = Ring::PA, PS = Ring::PB;
-  constexpr int STAT = OWN_Q ? 0 : 4 * BS * 4;  // streamed-query statistics (key-owner kernel)
-  constexpr int SLOT = Ring::BYTES + STAT;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int RBT = DT * (int)sizeof(T), RBS = DS * (int)sizeof(T), RBX = TEACHER ? RBT : RBS;
+  constexpr int NCT = RBT / 16, NCS = RBS / 16;
+  constexpr int TILE = BS * (RBT + RBS);
+  constexpr int STAT = OWN_Q ? 0 : 4 * 256;  // raw lse_t, lse_s, g, kl of the streamed queries (64 slots each)
+  constexpr int SLOT = TILE + STAT;
+  using DmaT = DmaTile<BS, RBT, NT>;
+  using DmaS = DmaTile<BS, RBS, NT>;
+  constexpr int NI = DmaT::NI + DmaS::NI;  // tile DMA instructions per thread per tile
+  constexpr int NIS = OWN_Q ? 0 : (TEACHER ? 4 : 3);  // statistics DMA instructions (wave 0 only)
+  __shared__ __attribute__((aligned(1024))) char slot0[SLOT], slot1[SLOT], slot2[SLOT];
+  static_assert(NBUF == 3, "one named array per ring slot");
+  __shared__ __attribute__((aligned(16))) float wst[OWN_Q ? 1 : 4][4][32];  // per-wave converted statistics
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, r32 = lane & 31;
   const int nbh = a.B * a.H;
@@ -115,13 +136,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   const T* str_t = OWN_Q ? kt : qt;
   const T* str_s = OWN_Q ? ks : qs;
   const int64_t own_pt = OWN_Q ? a.sqt[2] : a.skt[2], own_ps = OWN_Q ? a.sqs[2] : a.sks[2];
-  const int64_t str_pt = OWN_Q ? a.skt[2] : a.sqt[2], str_ps = OWN_Q ? a.sks[2] : a.sqs[2];
+  const int64_t str_pt = (OWN_Q ? a.skt[2] : a.sqt[2]) * (int64_t)sizeof(T);
+  const int64_t str_ps = (OWN_Q ? a.sks[2] : a.sqs[2]) * (int64_t)sizeof(T);
 
   const int o0 = ob * BW;
   const int o0w = o0 + wave * 32;
   const int orow = o0w + r32;
   const bool ovalid = orow < n_own;
-  u32x4 ot_r[DT * sizeof(T) / 32], os_r[DS * sizeof(T) / 32];
+  u32x4 ot_r[NCT / 2], os_r[NCS / 2];
   load_row_regs<T, DT>(ot_r, own_t + (int64_t)orow * own_pt, ovalid, hf);
   load_row_regs<T, DS>(os_r, own_s + (int64_t)orow * own_ps, ovalid, hf);
 
@@ -154,116 +176,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     t_end = (a.Nq + BS - 1) / BS;
   }
 
-  Ring ring;
-  ring.init(reinterpret_cast<const char*>(str_t), str_pt * (int64_t)sizeof(T), reinterpret_cast<const char*>(str_s),
-            str_ps * (int64_t)sizeof(T), n_str, tid);
-  // key-owner: per-tile statistics of the streamed queries, prefetched with the tile
-  __amdgpu_buffer_rsrc_t r_lt, r_ls, r_g, r_kl;
-  float pf_lt = 0.f, pf_ls = 0.f, pf_g = 0.f, pf_kl = 0.f;
+  // ---- streamed tiles: buffer->LDS DMA into a 3-slot ring, two tiles ahead
+  const u32x4 rs_t = rsrc_words(str_t, (uint32_t)((n_str - 1) * str_pt + RBT));
+  const u32x4 rs_s = rsrc_words(str_s, (uint32_t)((n_str - 1) * str_ps + RBS));
+  u32x4 rst[4];
   if constexpr (!OWN_Q) {
-    r_lt = make_rsrc(lse_t_bh, (uint32_t)a.Nq * 4u);
-    r_ls = make_rsrc(lse_s_bh, (uint32_t)a.Nq * 4u);
-    r_g = make_rsrc(g_bh, (uint32_t)a.Nq * 4u);
-    if constexpr (TEACHER) r_kl = make_rsrc(kl_bh, (uint32_t)a.Nq * 4u);
+    rst[0] = rsrc_words(lse_t_bh, (uint32_t)a.Nq * 4u);
+    rst[1] = rsrc_words(lse_s_bh, (uint32_t)a.Nq * 4u);
+    rst[2] = rsrc_words(g_bh, (uint32_t)a.Nq * 4u);
+    rst[3] = TEACHER ? rsrc_words(kl_bh, (uint32_t)a.Nq * 4u) : rst[2];
   }
-  auto prefetch = [&](int t) {
-    ring.prefetch(t * BS);
+  DmaT dma_t;
+  DmaS dma_s;
+  dma_t.init(str_pt, wave, lane);
+  dma_s.init(str_ps, wave, lane);
+  auto slot_ptr = [&](int u) -> char* { return u == 0 ? slot0 : (u == 1 ? slot1 : slot2); };
+  auto issue = [&](int t, int u) {
+    char* sl = slot_ptr(u);
+    const bool whole = (t + 1) * BS <= n_str;
+    dma_t.issue(rs_t, t * BS * (int)str_pt, whole, sl, wave);
+    dma_s.issue(rs_s, t * BS * (int)str_ps, whole, sl + BS * RBT, wave);
     if constexpr (!OWN_Q) {
-      if (tid < BS) {
-        const int so = t * BS * 4;
-        pf_lt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_lt, tid * 4, so, 0));
-        pf_ls = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ls, tid * 4, so, 0));
-        pf_g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_g, tid * 4, so, 0));
-        if constexpr (TEACHER)
-          pf_kl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_kl, tid * 4, so, 0));
+      if (wave == 0) {
+        const int vo = (t * BS + lane) * 4;  // lanes 32..63 fetch the next tile's rows: unused
+#pragma unroll
+        for (int k = 0; k < NIS; ++k) dma_dword(rst[k], vo, sl + TILE + k * 256);
       }
     }
   };
-  auto commit = [&](int t) {
-    char* slot = lds + (t & 1) * SLOT;
-    ring.commit(slot);
-    if constexpr (!OWN_Q) {
-      if (tid < BS) {
-        float* st = reinterpret_cast<float*>(slot + Ring::BYTES);
-        st[tid] = pf_lt * kLog2e;
-        st[BS + tid] = pf_ls * kLog2e;
-        st[2 * BS + tid] = pf_g;  // zero past the last query: those rows contribute nothing
-        st[3 * BS + tid] = pf_kl + pf_lt - pf_ls;
-      }
+  auto wait_tile = [&]() {  // this wave's DMA for the oldest in-flight tile has landed
+    if constexpr (NIS > 0) {
+      if (wave == 0)
+        wait_vmcnt<NI + NIS>();
+      else
+        wait_vmcnt<NI>();
+    } else {
+      wait_vmcnt<NI>();
     }
   };
+
+  int off_t[NCT / 2], off_s[NCS / 2];  // recompute operand offsets (row r32 of a tile)
+  swz_operand_offsets<RBT, NCT / 2>(off_t, r32, hf);
+  swz_operand_offsets<RBS, NCS / 2>(off_s, r32, hf);
+  int toff[2][DX / 32];  // transpose-read offsets of the gradient product
+  tr_offsets<RBX, DX>(toff, lane);
 
   f32x16 dacc[DX / 32];
 #pragma unroll
   for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
 
-  if (t_begin < t_end) prefetch(t_begin);
-  // (slot t&1 last held tile t-2, whose reads all finished before the barrier that published t-1)
-  for (int t = t_begin; t < t_end; ++t) {
-    commit(t);
-    if (t + 1 < t_end) prefetch(t + 1);
-    __syncthreads();
-    const char* slot = lds + (t & 1) * SLOT;
-    const char* tile_t = slot;
-    const char* tile_s = slot + BS * PT;
-    const float* stats = reinterpret_cast<const float*>(slot + Ring::BYTES);
+  wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
+  issue(t_begin, 0);
+  issue(t_begin + 1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
+  for (int t0 = t_begin; t0 < t_end; t0 += NBUF) {
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      const int sb = t * BS + sub * 32;  // first streamed row of this subtile
-      // allowed(q, k): k <= q + off when causal; classify the 32 x 32 block of this wave
-      bool skip, full;
-      if constexpr (OWN_Q) {
-        skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
-        full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
-      } else {
-        skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
-        full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
-      }
-      if (skip) continue;
-      f32x16 st = {}, ss = {};
-      tile_dot_lds_a<T, DT>(st, tile_t + (sub * 32 + r32) * PT, hf, ot_r);
-      tile_dot_lds_a<T, DS>(ss, tile_s + (sub * 32 + r32) * PS, hf, os_r);
-      float ds[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 lt4, ls4, gg4, cc4;
+    for (int u = 0; u < NBUF; ++u) {
+      const int t = t0 + u;
+      if (t < t_end) {
+        wait_tile();
+        __syncthreads();               // tile t visible to all; tile t-1 no longer read
+        issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
+        const char* sl = slot_ptr(u);
+        const int sb = t * BS;  // first streamed row of this tile
+        bool skip, full;
         if constexpr (OWN_Q) {
-          lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
-          ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
-          gg4 = f32x4{own_g, own_g, own_g, own_g};
-          cc4 = f32x4{own_c, own_c, own_c, own_c};
+          skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
+          full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
         } else {
-          const int ql = sub * 32 + 8 * g4 + 4 * hf;
-          lt4 = *reinterpret_cast<const f32x4*>(stats + ql);
-          ls4 = *reinterpret_cast<const f32x4*>(stats + BS + ql);
-          gg4 = *reinterpret_cast<const f32x4*>(stats + 2 * BS + ql);
-          cc4 = TEACHER ? *reinterpret_cast<const f32x4*>(stats + 3 * BS + ql) : f32x4{};
+          skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
+          full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
         }
+        if (!skip) {
+          if constexpr (!OWN_Q) {  // statistics of the 32 streamed queries, converted once per wave
+            if (hf == 0) {
+              const float* raw = reinterpret_cast<const float*>(sl + TILE);
+              const float lt = raw[r32], ls = raw[64 + r32];
+              wst[wave][0][r32] = lt * kLog2e;
+              wst[wave][1][r32] = ls * kLog2e;
+              wst[wave][2][r32] = raw[128 + r32];
+              if constexpr (TEACHER) wst[wave][3][r32] = raw[192 + r32] + lt - ls;
+            }
+          }
+          f32x16 st = {}, ss = {};
+          tile_dot_swz<T, DT>(st, sl, off_t, ot_r);
+          tile_dot_swz<T, DS>(ss, sl + BS * RBT, off_s, os_r);
+          float ds[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
-          float v;
-          if constexpr (TEACHER) {
-            v = gg4[e] * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
-          } else {
-            const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
-            v = gg4[e] * (ps - pt);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 lt4, ls4, gg4, cc4;
+            if constexpr (OWN_Q) {
+              lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
+              ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
+              gg4 = f32x4{own_g, own_g, own_g, own_g};
+              cc4 = f32x4{own_c, own_c, own_c, own_c};
+            } else {
+              const int ql = 8 * g4 + 4 * hf;
+              lt4 = *reinterpret_cast<const f32x4*>(&wst[wave][0][ql]);
+              ls4 = *reinterpret_cast<const f32x4*>(&wst[wave][1][ql]);
+              gg4 = *reinterpret_cast<const f32x4*>(&wst[wave][2][ql]);
+              cc4 = TEACHER ? *reinterpret_cast<const f32x4*>(&wst[wave][3][ql]) : f32x4{};
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * g4 + e;
+              const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
+              float v;
+              if constexpr (TEACHER) {
+                v = gg4[e] * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
+              } else {
+                const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
+                v = gg4[e] * (ps - pt);
+              }
+              ds[i] = v;
+            }
           }
           if (!full) {
-            const int sr = sb + acc_row(i, hf);
-            const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
-            v = ok ? v : 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int sr = sb + acc_row(i, hf);
+              const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
+              ds[i] = ok ? ds[i] : 0.f;
+            }
           }
-          ds[i] = v;
+          grad_product<T, DX, RBX>(dacc, ds, TEACHER ? sl : sl + BS * RBT, toff, lane);
         }
       }
-      if constexpr (TEACHER)
-        grad_product<T, DX, PT>(dacc, ds, tile_t, sub, lane);
-      else
-        grad_product<T, DX, PS>(dacc, ds, tile_s, sub, lane);
     }
   }
+  wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS when it exits
 
   const float scale = TEACHER ? a.scale_t : a.scale_s;
   float* out = (OWN_Q ? a.dq : a.dk) + (int64_t)bh * n_own * DX;
@@ -284,14 +324,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int64_t nblk = (int64_t)((n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * a.H;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  constexpr int lds = bwd_lds_bytes<T, DT, DS, OWN_Q>();
-  auto kern = bwd_kernel<T, DT, DS, C, TE, OWN_Q>;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(BwdTile<T>::NT), lds, s, a);
+  hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, OWN_Q>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s, a);
   return hipGetLastError();
 }
 

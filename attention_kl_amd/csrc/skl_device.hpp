@@ -29,17 +29,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // masked so far still rescales by exp2(0) = 1 instead of exp2(-inf + inf) = NaN.
 constexpr float kMaxInit = -1.0e30f;
 
-template <typename T>
-struct Elt;
-template <>
-struct Elt<__bf16> {
-  static constexpr int kPer16 = 8;  // elements per 16-byte chunk
-};
-template <>
-struct Elt<float> {
-  static constexpr int kPer16 = 4;
-};
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -64,38 +53,10 @@ __device__ __forceinline__ void mma_chunk<float>(f32x16& acc, const u32x4& a, co
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[e]), __uint_as_float(bv[e]), acc, 0, 0, 0);
 }
 
-// Raw buffer resource over `bytes` bytes at `base`: loads at offsets past the end return
-// zero instead of touching memory, so tile loads need no clamping or branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
 __device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 lds_read8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Row of the 32x32 accumulator held in register i by lane half hf.
 __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
-
-// 32x32 tile product S = rows(A) . rows(B)^T over D features, A rows read from LDS
-// (row pitch `pitch` bytes, first row = lane's m row already applied in `a_row`) and
-// B rows held in registers as D*sizeof(T)/32 chunks.
-template <typename T, int D>
-__device__ __forceinline__ void tile_dot_lds_a(f32x16& acc, const char* a_row, int hf, const u32x4* b_regs) {
-  constexpr int NC = D * (int)sizeof(T) / 16;
-#pragma unroll
-  for (int c = 0; c < NC / 2; ++c) mma_chunk<T>(acc, lds_read16(a_row + (2 * c + hf) * 16), b_regs[c]);
-}
-
-// Same product with the A operand in registers and B rows from LDS.
-template <typename T, int D>
-__device__ __forceinline__ void tile_dot_lds_b(f32x16& acc, const u32x4* a_regs, const char* b_row, int hf) {
-  constexpr int NC = D * (int)sizeof(T) / 16;
-#pragma unroll
-  for (int c = 0; c < NC / 2; ++c) mma_chunk<T>(acc, a_regs[c], lds_read16(b_row + (2 * c + hf) * 16));
-}
 
 // Load one row's operand chunks (2c + hf) from global memory, or zeros past the end.
 template <typename T, int D>
@@ -107,88 +68,6 @@ __device__ __forceinline__ void load_row_regs(u32x4* regs, const T* row, bool va
     regs[c] = valid ? *reinterpret_cast<const u32x4*>(p + (2 * c + hf) * 16) : u32x4{0u, 0u, 0u, 0u};
   }
 }
-
-// Cooperative copy of a tile of `rows` rows (D features each) from global memory to LDS
-// (row pitch `pitch` bytes); rows at or past `valid_rows` are zero-filled.  When T_PITCH > 0
-// the tile is also written transposed ([feature][row], pitch T_PITCH bytes) to `lds_t`.
-template <typename T, int D, int ROWS, int NTHREADS, int T_PITCH>
-__device__ __forceinline__ void stage_tile(char* lds, int pitch, char* lds_t, const T* src, int64_t row_stride,
-                                           int valid_rows, int tid) {
-  constexpr int NC = D * (int)sizeof(T) / 16;
-  constexpr int PER = Elt<T>::kPer16;
-#pragma unroll
-  for (int idx = tid; idx < ROWS * NC; idx += NTHREADS) {
-    const int r = idx / NC, c = idx % NC;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < valid_rows) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src + r * row_stride) + c * 16);
-    *reinterpret_cast<u32x4*>(lds + r * pitch + c * 16) = v;
-    if constexpr (T_PITCH > 0) {
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          const uint16_t h16 = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-          *reinterpret_cast<uint16_t*>(lds_t + (c * PER + e) * T_PITCH + r * 2) = h16;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < PER; ++e) *reinterpret_cast<uint32_t*>(lds_t + (c * PER + e) * T_PITCH + r * 4) = v[e];
-      }
-    }
-  }
-}
-
-// Register-prefetched, double-buffered LDS ring for a tile of ROWS rows of two row-major
-// tensors A (DA features) and B (DB features) of element type T.  Rows are read with buffer
-// loads (zero past `bytes` of each tensor), so no load needs a bounds branch.  Layout of one
-// ring slot: A rows at pitch PA, then B rows at pitch PB, both padded by 16 bytes.
-template <typename T, int DA, int DB, int ROWS, int NT>
-struct TileRing {
-  static constexpr int PA = DA * (int)sizeof(T) + 16, PB = DB * (int)sizeof(T) + 16;
-  static constexpr int NCA = DA * (int)sizeof(T) / 16, NCB = DB * (int)sizeof(T) / 16;
-  static constexpr int NLA = ROWS * NCA / NT, NLB = ROWS * NCB / NT;
-  static constexpr int BYTES = ROWS * (PA + PB);
-  static_assert(ROWS * NCA % NT == 0 && ROWS * NCB % NT == 0, "tile must split evenly over the workgroup");
-
-  __amdgpu_buffer_rsrc_t ra, rb;
-  int pitch_a, pitch_b;  // global row pitch in bytes
-  int vo_a[NLA], vo_b[NLB], lo_a[NLA], lo_b[NLB];
-  u32x4 pa[NLA], pb[NLB];
-
-  __device__ __forceinline__ void init(const char* a, int64_t a_pitch, const char* b, int64_t b_pitch, int nrows,
-                                       int tid) {
-    pitch_a = (int)a_pitch;
-    pitch_b = (int)b_pitch;
-    ra = make_rsrc(a, (uint32_t)((nrows - 1) * a_pitch + DA * (int)sizeof(T)));
-    rb = make_rsrc(b, (uint32_t)((nrows - 1) * b_pitch + DB * (int)sizeof(T)));
-#pragma unroll
-    for (int j = 0; j < NLA; ++j) {
-      const int idx = tid + j * NT, r = idx / NCA, c = idx % NCA;
-      vo_a[j] = r * pitch_a + c * 16;
-      lo_a[j] = r * PA + c * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < NLB; ++j) {
-      const int idx = tid + j * NT, r = idx / NCB, c = idx % NCB;
-      vo_b[j] = r * pitch_b + c * 16;
-      lo_b[j] = ROWS * PA + r * PB + c * 16;
-    }
-  }
-  // Global -> registers for the tile starting at row `row0`.
-  __device__ __forceinline__ void prefetch(int row0) {
-    const int sa = row0 * pitch_a, sb = row0 * pitch_b;
-#pragma unroll
-    for (int j = 0; j < NLA; ++j) pa[j] = buffer_load16(ra, vo_a[j], sa);
-#pragma unroll
-    for (int j = 0; j < NLB; ++j) pb[j] = buffer_load16(rb, vo_b[j], sb);
-  }
-  // Registers -> LDS slot at `base`.
-  __device__ __forceinline__ void commit(char* base) {
-#pragma unroll
-    for (int j = 0; j < NLA; ++j) *reinterpret_cast<u32x4*>(base + lo_a[j]) = pa[j];
-#pragma unroll
-    for (int j = 0; j < NLB; ++j) *reinterpret_cast<u32x4*>(base + lo_b[j]) = pb[j];
-  }
-};
 
 // ---------------------------------------------------------------------------------------------
 // Swizzled LDS tiles filled by buffer->LDS DMA (buffer_load_dwordx4 ... lds).
@@ -223,22 +102,51 @@ struct DmaTile {
       vo[j] = pr * (int)pitch + ((pc ^ swz<RB>(pr)) * 16);
     }
   }
-  // Queue the tile whose first row sits at byte offset `soff` of the buffer into LDS at `dst`.
+  // Queue the tile whose first row sits at byte offset `toff` of the buffer into LDS at `dst`.
   // Issued as inline asm so that the compiler does not track these LDS writes: callers order
   // them with explicit vmcnt waits and barriers (the destination slot is never read while a DMA
   // into it can be in flight).  The asm has no output register.
-  __device__ __forceinline__ void issue(const u32x4& rsrc, int soff, char* dst, int wave) const {
+  //
+  // Only the VGPR offset of a buffer access is range-checked against num_records; the SGPR
+  // offset is added after the check.  A tile that lies wholly inside the buffer (`whole`, a
+  // wave-uniform flag) passes toff in the SGPR; any other tile (the ragged last one, or one past
+  // the end) adds it to the VGPR offset, so its rows beyond the buffer arrive as zeros and no
+  // byte outside the buffer is read.  The two asm strings differ so the branches stay separate.
+  __device__ __forceinline__ void issue(const u32x4& rsrc, int toff, bool whole, char* dst, int wave) const {
     const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)dst);
+    if (whole) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * 1024));
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :
-                   : "s"(m0v), "v"(vo[j]), "s"(rsrc), "s"(soff)
-                   : "memory", "m0");
+      for (int j = 0; j < NI; ++j) {
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * 1024));
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds ; whole tile"
+                     :
+                     : "s"(m0v), "v"(vo[j]), "s"(rsrc), "s"(toff)
+                     : "memory", "m0");
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * 1024));
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds ; checked tile"
+                     :
+                     : "s"(m0v), "v"(vo[j] + toff), "s"(rsrc), "s"(0)
+                     : "memory", "m0");
+      }
     }
   }
 };
+
+// One dword per lane from byte offset `voff` of the buffer into LDS at `dst` + 4 * lane (inline
+// asm, untracked like DmaTile::issue).  The whole offset is range-checked: past num_records the
+// lane writes zero.
+__device__ __forceinline__ void dma_dword(const u32x4& rsrc, int voff, char* dst) {
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)dst));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(0)
+               : "memory", "m0");
+}
 
 // Raw buffer descriptor words (base, stride 0, num_records = bytes, gfx9 data-format word)
 // for DMA issued from inline asm.
