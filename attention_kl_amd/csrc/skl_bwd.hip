@@ -9,11 +9,11 @@
 //   teacher  dS = g_i P_t ((a - b) - (KL_i + LSE_t,i - LSE_s,i))
 //   dQ = scale dS K,   dK = scale dS^T Q     (K, Q of the same side)
 //
-// One kernel template serves both halves.  Each workgroup owns 128 rows of the
-// output (query rows for dQ, key rows for dK) and keeps their Q or K slices in
-// registers as MFMA B operands; the other side streams through a double-buffered
-// LDS ring.  Owning the output rows means no atomics and no workspace.  Both
-// halves recompute both logit tiles.
+// One kernel template serves both halves.  Each wave owns 32 rows of the output
+// (query rows for dQ, key rows for dK) and keeps their Q or K slices in registers
+// as MFMA B operands; the other side streams through a 4-slot LDS ring filled by
+// buffer->LDS DMA.  Owning the output rows means no atomics and no workspace.
+// Both halves recompute both logit tiles.
 //
 // The logit tile is formed with the owned rows as columns, so each lane holds 16
 // streamed rows of one owned row; that register block is directly the A operand
@@ -22,6 +22,14 @@
 // from the row-major LDS tile through transpose reads, so no transposed copy is
 // stored.  bf16: dS enters the MFMA as hi + lo bf16 parts (two products), so its
 // rounding contributes about 2^-16 relative instead of bf16's 2^-9.
+//
+// Per streamed tile s a wave runs a matrix phase, M(s) = gradient product of
+// tile s-1 then the two logit products of tile s, and a vector phase, V(s) = the
+// probabilities and dS of tile s.  bf16 workgroups have eight waves in two
+// groups, one wave of each group per SIMD; group 1 starts one phase late and
+// every phase ends at a workgroup barrier, so on every SIMD one wave is in its
+// matrix phase while the other is in its vector phase (ping-pong) and the matrix
+// cores and the vector ALUs work at the same time.
 #include "skl_device.hpp"
 #include "skl_kernels.hpp"
 
@@ -36,10 +44,36 @@ __device__ __forceinline__ float scaled_diff(float a, float sa, float b, float s
 
 template <typename T>
 struct BwdTile {
-  static constexpr int BW = 128;  // owned rows per workgroup (4 waves x 32)
-  static constexpr int BS = 32;   // streamed rows per LDS tile (one 32 x 32 block per wave)
-  static constexpr int NBUF = 3;  // LDS ring depth: tiles t+1, t+2 in flight while t is used
-  static constexpr int NT = 256;
+  static constexpr int NG = sizeof(T) == 2 ? 2 : 1;  // wave groups (two: ping-pong)
+  static constexpr int NW = 4 * NG;                  // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int BW = 32 * NW;  // owned rows per workgroup (32 per wave)
+  static constexpr int BS = 32;       // streamed rows per LDS tile
+  // LDS ring: tile s is read in phases 2s..2s+3 (ping-pong) or in step s (one group), while the
+  // next PD = NBUF - 2 tiles are in flight
+  static constexpr int NBUF = 4;
+  static constexpr int PD = NBUF - 2;
+};
+
+// dS of one 32 x 32 tile in the accumulator layout, kept from a vector phase to the next matrix
+// phase as the gradient product's A operand: bf16 hi + lo chunks, or fp32 values.
+template <typename T>
+struct DsTile;
+template <>
+struct DsTile<__bf16> {
+  u32x4 hi[2], lo[2];
+  __device__ __forceinline__ void set(const float* v) {
+    split_bf16x8(v, hi[0], lo[0]);
+    split_bf16x8(v + 8, hi[1], lo[1]);
+  }
+};
+template <>
+struct DsTile<float> {
+  float v[16];
+  __device__ __forceinline__ void set(const float* x) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = x[i];
+  }
 };
 
 // Per-lane byte offsets, inside a swizzled streamed tile of RB-byte rows, of the transpose-read
@@ -60,28 +94,42 @@ __device__ __forceinline__ void tr_offsets(int (*off)[DX / 32], int lane) {
   }
 }
 
+// Gradient-product B operands of chunk c (streamed rows 16c .. 16c + 15) of the streamed tile X
+// at `xt` (row-major, swizzled): columns 32 db .. 32 db + 31 for each db, through transpose reads.
+template <int DX, int RB>
+__device__ __forceinline__ void grad_operands(u32x4* bop, const char* xt, const int (*toff)[DX / 32], int c) {
+#pragma unroll
+  for (int db = 0; db < DX / 32; ++db) {
+    const u32x2 p0 = lds_read_tr16(xt + toff[0][db] + 16 * c * RB);
+    const u32x2 p1 = lds_read_tr16(xt + toff[1][db] + 16 * c * RB);
+    bop[db] = u32x4{p0[0], p0[1], p1[0], p1[1]};
+  }
+}
+// out[db] += dS[:, chunk c] . B[db]: hi parts into every accumulator, then lo parts, so no MFMA
+// waits on the one just before it.
+template <int DX>
+__device__ __forceinline__ void grad_mma(f32x16* out, const DsTile<__bf16>& ds, int c, const u32x4* bop) {
+#pragma unroll
+  for (int db = 0; db < DX / 32; ++db) mma_chunk<__bf16>(out[db], ds.hi[c], bop[db]);
+#pragma unroll
+  for (int db = 0; db < DX / 32; ++db) mma_chunk<__bf16>(out[db], ds.lo[c], bop[db]);
+}
+
 // out[db] += dS . X[:, 32 db .. 32 db + 31] for one 32-row streamed tile.  dS is in the logit
 // accumulator layout (lane = owned row, element i = streamed row acc_row(i, hf)); X is the
 // streamed tile of the side being differentiated, row-major and swizzled in LDS at `xt`.
 template <typename T, int DX, int RB>
-__device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const char* xt, const int (*toff)[DX / 32],
-                                             int lane) {
-  const int hf = lane >> 5, r32 = lane & 31;
+__device__ __forceinline__ void grad_product(f32x16* out, const DsTile<T>& ds, const char* xt,
+                                             const int (*toff)[DX / 32], int lane) {
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      u32x4 hi, lo;
-      split_bf16x8(ds + 8 * c, hi, lo);
-#pragma unroll
-      for (int db = 0; db < DX / 32; ++db) {
-        const u32x2 p0 = lds_read_tr16(xt + toff[0][db] + 16 * c * RB);
-        const u32x2 p1 = lds_read_tr16(xt + toff[1][db] + 16 * c * RB);
-        const u32x4 bop = {p0[0], p0[1], p1[0], p1[1]};
-        mma_chunk<__bf16>(out[db], hi, bop);
-        mma_chunk<__bf16>(out[db], lo, bop);
-      }
+      u32x4 bop[DX / 32];
+      grad_operands<DX, RB>(bop, xt, toff, c);
+      grad_mma<DX>(out, ds, c, bop);
     }
   } else {
+    const int hf = lane >> 5, r32 = lane & 31;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = acc_row(i, hf);
@@ -90,18 +138,42 @@ __device__ __forceinline__ void grad_product(f32x16* out, const float* ds, const
         const int col = 32 * db + r32;  // fp32 element column; 4 per 16-byte chunk
         const float x = *reinterpret_cast<const float*>(xt + row * RB + ((((col >> 2) ^ swz<RB>(row))) << 4) +
                                                         (col & 3) * 4);
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ds[i], x, out[db], 0, 0, 0);
+        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ds.v[i], x, out[db], 0, 0, 0);
       }
     }
+  }
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding, N wave-uniform
+// and below 16.
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;
   }
 }
 
 // OWN_Q: the workgroup owns query rows and writes dQ; otherwise it owns key rows and writes dK.
 // TEACHER: gradients of the teacher side (dQ_t / dK_t) instead of the student side.
 template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER, bool OWN_Q>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2))) void bwd_kernel(
-    const BwdArgs a) {
-  constexpr int BW = BwdTile<T>::BW, BS = BwdTile<T>::BS, NBUF = BwdTile<T>::NBUF, NT = BwdTile<T>::NT;
+__global__ __launch_bounds__(BwdTile<T>::NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2))) void
+bwd_kernel(const BwdArgs a) {
+  using C = BwdTile<T>;
+  constexpr int NG = C::NG, NW = C::NW, NT = C::NT, BW = C::BW, BS = C::BS, NBUF = C::NBUF, PD = C::PD;
   constexpr int DX = TEACHER ? DT : DS;
   constexpr int RBT = DT * (int)sizeof(T), RBS = DS * (int)sizeof(T), RBX = TEACHER ? RBT : RBS;
   constexpr int NCT = RBT / 16, NCS = RBS / 16;
@@ -110,13 +182,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   constexpr int SLOT = TILE + STAT;
   using DmaT = DmaTile<BS, RBT, NT>;
   using DmaS = DmaTile<BS, RBS, NT>;
-  constexpr int NI = DmaT::NI + DmaS::NI;  // tile DMA instructions per thread per tile
+  constexpr int NI = DmaT::NI + DmaS::NI;             // tile DMA instructions per wave per tile
   constexpr int NIS = OWN_Q ? 0 : (TEACHER ? 4 : 3);  // statistics DMA instructions (wave 0 only)
-  __shared__ __attribute__((aligned(1024))) char slot0[SLOT], slot1[SLOT], slot2[SLOT];
-  static_assert(NBUF == 3, "one named array per ring slot");
-  __shared__ __attribute__((aligned(16))) float wst[OWN_Q ? 1 : 4][4][32];  // per-wave converted statistics
+  constexpr int NRG = 4 * (DX / 32);                       // bf16 gradient product: LDS reads = MFMAs
+  constexpr int NRL = (RBT + RBS) / 32;                    // bf16 logit products: LDS reads = MFMAs
+  static_assert(SLOT % 256 == 0, "ring slots start on a 256-byte bank window");
+  __shared__ __attribute__((aligned(1024))) char ring[NBUF][SLOT];
+  // converted statistics (log2 units) of the streamed queries: per ring slot in the ping-pong (one
+  // wave of group 1 per statistic converts them a phase before use), per wave otherwise
+  constexpr bool CSLOT = !OWN_Q && NG == 2;
+  __shared__ __attribute__((aligned(16))) float cst[CSLOT ? NBUF : 1][4][32];
+  __shared__ __attribute__((aligned(16))) float wst[(!OWN_Q && NG == 1) ? NW : 1][4][32];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, r32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
+  // wave index in a scalar register: every branch on it (and on the group) is a scalar branch, so a
+  // barrier inside one is executed only by the waves that take it
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = NG == 2 ? (wave >> 2) : 0;
   const int nbh = a.B * a.H;
   const int n_own = OWN_Q ? a.Nq : a.Nk, n_str = OWN_Q ? a.Nk : a.Nq;
   const int nob = (n_own + BW - 1) / BW;
@@ -163,7 +245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     }
   }
 
-  // streamed range
+  // streamed range of the workgroup: tiles t_begin .. t_begin + ntile - 1 (ntile >= 1)
   int t_begin, t_end;
   if constexpr (OWN_Q) {
     const int q_last = min(a.Nq, o0 + BW) - 1;
@@ -175,8 +257,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     t_begin = qmin / BS;
     t_end = (a.Nq + BS - 1) / BS;
   }
+  const int ntile = t_end - t_begin;
 
-  // ---- streamed tiles: buffer->LDS DMA into a 3-slot ring, two tiles ahead
+  // ---- streamed tiles: buffer->LDS DMA into the ring, two tiles ahead
   const u32x4 rs_t = rsrc_words(str_t, (uint32_t)((n_str - 1) * str_pt + RBT));
   const u32x4 rs_s = rsrc_words(str_s, (uint32_t)((n_str - 1) * str_ps + RBS));
   u32x4 rst[4];
@@ -190,8 +273,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   DmaS dma_s;
   dma_t.init(str_pt, wave, lane);
   dma_s.init(str_ps, wave, lane);
-  auto slot_ptr = [&](int u) -> char* { return u == 0 ? slot0 : (u == 1 ? slot1 : slot2); };
-  auto issue = [&](int t, int u) {
+  auto slot_ptr = [&](int u) -> char* { return ring[u]; };
+  auto issue = [&](int s, int u) {  // tile s of the workgroup's stream into ring slot u
+    const int t = t_begin + s;
     char* sl = slot_ptr(u);
     const bool whole = (t + 1) * BS <= n_str;
     dma_t.issue(rs_t, t * BS * (int)str_pt, whole, sl, wave);
@@ -204,18 +288,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
       }
     }
   };
-  auto wait_tile = [&]() {  // this wave's DMA for the oldest in-flight tile has landed
+  // this wave's DMA of the older of its two newest tiles has landed (the newest may be in flight)
+  auto wait_tile = [&]() {
     if constexpr (NIS > 0) {
       if (wave == 0)
-        wait_vmcnt<NI + NIS>();
+        wait_vmcnt<(PD - 1) * (NI + NIS)>();
       else
-        wait_vmcnt<NI>();
+        wait_vmcnt<(PD - 1) * NI>();
     } else {
-      wait_vmcnt<NI>();
+      wait_vmcnt<(PD - 1) * NI>();
+    }
+  };
+  auto tile_state = [&](int s, bool& skip, bool& full) {
+    const int sb = (t_begin + s) * BS;  // first streamed row of the tile
+    if constexpr (OWN_Q) {
+      skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
+      full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
+    } else {
+      skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
+      full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
     }
   };
 
-  int off_t[NCT / 2], off_s[NCS / 2];  // recompute operand offsets (row r32 of a tile)
+  int off_t[NCT / 2], off_s[NCS / 2];  // logit-product operand offsets (row r32 of a tile)
   swz_operand_offsets<RBT, NCT / 2>(off_t, r32, hf);
   swz_operand_offsets<RBS, NCS / 2>(off_s, r32, hf);
   int toff[2][DX / 32];  // transpose-read offsets of the gradient product
@@ -224,81 +319,179 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   f32x16 dacc[DX / 32];
 #pragma unroll
   for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
+  f32x16 st = {}, ss = {};
+  DsTile<T> dsr;  // dS of the last tile through the vector phase, for the gradient product
+  {
+    float z[16] = {};
+    dsr.set(z);
+  }
 
-  wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
-  issue(t_begin, 0);
-  issue(t_begin + 1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
-  for (int t0 = t_begin; t0 < t_end; t0 += NBUF) {
+  // Ping-pong, key owner: wave 4 + k of group 1 converts statistic k of the tile in slot u.
+  auto convert_stats = [&](int u, const char* sl) {
+    if constexpr (CSLOT) {
+      const int k = wave - 4;
+      if (k < (TEACHER ? 4 : 3) && hf == 0) {
+        const float* raw = reinterpret_cast<const float*>(sl + TILE);
+        float v;
+        if (k == 0)
+          v = raw[r32] * kLog2e;
+        else if (k == 1)
+          v = raw[64 + r32] * kLog2e;
+        else if (k == 2)
+          v = raw[128 + r32];
+        else
+          v = raw[192 + r32] + raw[r32] - raw[64 + r32];
+        cst[u][k][r32] = v;
+      }
+    }
+  };
+
+  // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
+  auto vector_phase = [&](int s, int u, const char* sl) {
+    bool skip, full;
+    tile_state(s, skip, full);
+    if (NG == 1 && skip) return;  // ping-pong: a skipped tile goes through the masked path (all zero)
+    if constexpr (!OWN_Q && !CSLOT) {  // statistics of the 32 streamed queries, converted once per wave
+      if (hf == 0) {
+        const float* raw = reinterpret_cast<const float*>(sl + TILE);
+        const float lt = raw[r32], ls = raw[64 + r32];
+        wst[wave][0][r32] = lt * kLog2e;
+        wst[wave][1][r32] = ls * kLog2e;
+        wst[wave][2][r32] = raw[128 + r32];
+        if constexpr (TEACHER) wst[wave][3][r32] = raw[192 + r32] + lt - ls;
+      }
+    }
+    const int sb = (t_begin + s) * BS;
+    float ds[16];
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int t = t0 + u;
-      if (t < t_end) {
-        wait_tile();
-        __syncthreads();               // tile t visible to all; tile t-1 no longer read
-        issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
-        const char* sl = slot_ptr(u);
-        const int sb = t * BS;  // first streamed row of this tile
-        bool skip, full;
-        if constexpr (OWN_Q) {
-          skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
-          full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f32x4 lt4, ls4, gg4, cc4;
+      if constexpr (OWN_Q) {
+        lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
+        ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
+        gg4 = f32x4{own_g, own_g, own_g, own_g};
+        cc4 = f32x4{own_c, own_c, own_c, own_c};
+      } else {
+        const int ql = 8 * g4 + 4 * hf;
+        const float(*cs)[32] = CSLOT ? cst[u] : wst[CSLOT ? 0 : wave];
+        lt4 = *reinterpret_cast<const f32x4*>(&cs[0][ql]);
+        ls4 = *reinterpret_cast<const f32x4*>(&cs[1][ql]);
+        gg4 = *reinterpret_cast<const f32x4*>(&cs[2][ql]);
+        cc4 = TEACHER ? *reinterpret_cast<const f32x4*>(&cs[3][ql]) : f32x4{};
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g4 + e;
+        const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
+        float v;
+        if constexpr (TEACHER) {
+          v = gg4[e] * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
         } else {
-          skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
-          full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
+          const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
+          v = gg4[e] * (ps - pt);
         }
-        if (!skip) {
-          if constexpr (!OWN_Q) {  // statistics of the 32 streamed queries, converted once per wave
-            if (hf == 0) {
-              const float* raw = reinterpret_cast<const float*>(sl + TILE);
-              const float lt = raw[r32], ls = raw[64 + r32];
-              wst[wave][0][r32] = lt * kLog2e;
-              wst[wave][1][r32] = ls * kLog2e;
-              wst[wave][2][r32] = raw[128 + r32];
-              if constexpr (TEACHER) wst[wave][3][r32] = raw[192 + r32] + lt - ls;
-            }
-          }
-          f32x16 st = {}, ss = {};
-          tile_dot_swz<T, DT>(st, sl, off_t, ot_r);
-          tile_dot_swz<T, DS>(ss, sl + BS * RBT, off_s, os_r);
-          float ds[16];
+        ds[i] = v;
+      }
+    }
+    if (!full) {
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            f32x4 lt4, ls4, gg4, cc4;
-            if constexpr (OWN_Q) {
-              lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
-              ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
-              gg4 = f32x4{own_g, own_g, own_g, own_g};
-              cc4 = f32x4{own_c, own_c, own_c, own_c};
-            } else {
-              const int ql = 8 * g4 + 4 * hf;
-              lt4 = *reinterpret_cast<const f32x4*>(&wst[wave][0][ql]);
-              ls4 = *reinterpret_cast<const f32x4*>(&wst[wave][1][ql]);
-              gg4 = *reinterpret_cast<const f32x4*>(&wst[wave][2][ql]);
-              cc4 = TEACHER ? *reinterpret_cast<const f32x4*>(&wst[wave][3][ql]) : f32x4{};
-            }
+      for (int i = 0; i < 16; ++i) {
+        const int sr = sb + acc_row(i, hf);
+        const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
+        ds[i] = ok ? ds[i] : 0.f;
+      }
+    }
+    dsr.set(ds);
+  };
+  // Matrix-core work of tile s (ring slot at sl): the gradient product, and the two logit products.
+  auto grad_phase = [&](int s, const char* sl) {
+    bool skip, full;
+    tile_state(s, skip, full);
+    if (!skip) grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sl : sl + BS * RBT, toff, lane);
+  };
+  auto logit_phase = [&](int s, const char* sl) {
+    bool skip, full;
+    tile_state(s, skip, full);
+    if (!skip) {
+      st = f32x16{};
+      ss = f32x16{};
+      tile_dot2_swz<T, DT, DS>(st, ss, sl, sl + BS * RBT, off_t, off_s, ot_r, os_r);
+      if constexpr (sizeof(T) == 2) sched_read_ahead<NRL, 4>();
+    }
+  };
+  // Matrix phase of the ping-pong: gradient product of tile s-1 (slot sp), logit products of
+  // tile s (slot sc), as one straight run of LDS reads and MFMAs so that the reads for the logit
+  // products go out while the gradient MFMAs still run.  It has no branches: a tile that a wave
+  // skips has an all-zero dS (its vector phase masks every element), at s = 0 the gradient
+  // product adds a zero dS times ring slot 3 (zero-filled before the first barrier; tile 3 only
+  // arrives in phase 2), and at s = ntile the logit products (of a tile that has landed, so
+  // finite) are not used.  Those cost under one percent of the MFMA work of a causal problem and
+  // keep a single register assignment for the accumulators.
+  auto matrix_phase = [&](const char* sp, const char* sc) {
+    grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sp : sp + BS * RBT, toff, lane);
+    st = f32x16{};
+    ss = f32x16{};
+    tile_dot2_swz<T, DT, DS>(st, ss, sc, sc + BS * RBT, off_t, off_s, ot_r, os_r);
+    if constexpr (sizeof(T) == 2) sched_read_ahead<NRG + NRL, 6>();
+  };
+
+  if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
+    static_assert(TILE % 16 == 0, "slot fill");
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * g4 + e;
-              const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
-              float v;
-              if constexpr (TEACHER) {
-                v = gg4[e] * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
-              } else {
-                const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
-                v = gg4[e] * (ps - pt);
-              }
-              ds[i] = v;
-            }
-          }
-          if (!full) {
+    for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
+  }
+  wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int sr = sb + acc_row(i, hf);
-              const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
-              ds[i] = ok ? ds[i] : 0.f;
-            }
+  for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
+  wait_tile();
+  __syncthreads();
+  if constexpr (NG == 2) {
+    // Ring protocol (phases p = 0, 1, ...; tile s is read from phase 2s to 2s+3): tile s+PD is
+    // issued at the start of phase 2s into the slot of tile s-2, and each wave waits for its share
+    // of tile s+1 at the end of phase 2s+1, before that phase's barrier.  The last slot, read by
+    // the s = 0 gradient product, first receives a tile in phase 2.
+    if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
+      issue(PD, PD);
+      convert_stats(0, ring[0]);
+      __syncthreads();
+    }
+    for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int s = s0 + u;
+        if (s <= ntile) {
+          // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
+          if (grp == 0) issue(s + PD, (u + PD) % NBUF);
+          matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
+          if (grp == 1) wait_tile();
+          __syncthreads();
+          // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
+          if (s < ntile) {
+            if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
+            vector_phase(s, u, slot_ptr(u));
+            if (grp == 1) convert_stats((u + 1) % NBUF, slot_ptr((u + 1) % NBUF));  // tile s+1 landed
+            if (grp == 0) wait_tile();
+            __syncthreads();
+          } else if (grp == 0) {
+            __syncthreads();  // group 0's last phase, matching group 1's late start
           }
-          grad_product<T, DX, RBX>(dacc, ds, TEACHER ? sl : sl + BS * RBT, toff, lane);
+        }
+      }
+    }
+  } else {
+    // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
+    // and tile s+1 waited for at its end.
+    for (int s0 = 0; s0 < ntile; s0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int s = s0 + u;
+        if (s < ntile) {
+          issue(s + PD, (u + PD) % NBUF);
+          logit_phase(s, slot_ptr(u));
+          vector_phase(s, u, slot_ptr(u));
+          grad_phase(s, slot_ptr(u));
+          wait_tile();
+          __syncthreads();
         }
       }
     }

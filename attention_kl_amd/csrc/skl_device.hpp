@@ -73,31 +73,36 @@ __device__ __forceinline__ void load_row_regs(u32x4* regs, const T* row, bool va
 // Swizzled LDS tiles filled by buffer->LDS DMA (buffer_load_dwordx4 ... lds).
 //
 // A tile holds ROWS rows of RB bytes, unpadded; logical 16-byte chunk c of row r is stored at
-// physical chunk c ^ swz(r).  One DMA instruction writes 64 lanes x 16 bytes contiguously at the
-// wave's LDS address, so the swizzle is applied on the global side: each lane fetches the logical
-// chunk that belongs at its physical slot.  swz makes both access patterns used here
-// conflict-free for RB >= 256: 16 consecutive rows reading one logical chunk (MFMA operand reads),
-// and the transpose read (rows R0..R0+3, R0 % 4 == 0, chunks C0 and C0+1, C0 even).
+// physical chunk c ^ swz(r).  One DMA instruction writes up to 64 lanes x 16 bytes contiguously at
+// the wave's LDS address, so the swizzle is applied on the global side: each lane fetches the
+// logical chunk that belongs at its physical slot.  Rows start on a 256-byte bank window (RB >= 256)
+// or share one two to a window (RB == 128).  swz keeps both access patterns used here free of bank
+// conflicts:
+//  - MFMA operand reads (ds_read_b128, 16 lanes per cycle): 16 consecutive rows, one logical chunk;
+//  - transpose reads (ds_read_b64_tr_b16, 32 lanes per cycle): rows R..R+3 (R % 4 == 0) times the
+//    four logical chunks 4m..4m+3, so the four rows must land in four different 4-chunk blocks.
 template <int RB>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (RB >= 256)
-    return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
+    return 4 * (r & 3) + ((r >> 2) & 3);
   else
-    return (r >> 1) & 7;  // 128-byte rows: two rows share one 256-byte bank window
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
 template <int ROWS, int RB, int NT>
 struct DmaTile {
   static constexpr int BYTES = ROWS * RB;
   static constexpr int NW = NT / 64;
-  static constexpr int NI = BYTES / (NW * 1024);  // DMA instructions per wave per tile
-  static_assert(BYTES % (NW * 1024) == 0, "tile must split into whole 1 KB wave writes");
+  static constexpr int CH = BYTES / NW < 1024 ? BYTES / NW : 1024;  // bytes per wave per instruction
+  static constexpr int LPW = CH / 16;                               // lanes taking part
+  static constexpr int NI = BYTES / (NW * CH);                      // DMA instructions per wave per tile
+  static_assert(CH % 256 == 0 && BYTES % (NW * CH) == 0, "tile must split into whole wave writes");
   int vo[NI];  // per-lane global byte offset inside the tile (relative to its first row)
 
   __device__ __forceinline__ void init(int64_t pitch, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int o = (j * NW + wave) * 1024 + 16 * lane;
+      const int o = (j * NW + wave) * CH + 16 * (lane % LPW);
       const int pr = o / RB, pc = (o % RB) / 16;
       vo[j] = pr * (int)pitch + ((pc ^ swz<RB>(pr)) * 16);
     }
@@ -114,23 +119,27 @@ struct DmaTile {
   // byte outside the buffer is read.  The two asm strings differ so the branches stay separate.
   __device__ __forceinline__ void issue(const u32x4& rsrc, int toff, bool whole, char* dst, int wave) const {
     const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)dst);
+    const bool on = LPW == 64 || (int)(threadIdx.x & 63) < LPW;  // lanes past LPW stay masked off
+    const int stoff = __builtin_amdgcn_readfirstlane(toff);       // wave-uniform: keep it in an SGPR
     if (whole) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * 1024));
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds ; whole tile"
-                     :
-                     : "s"(m0v), "v"(vo[j]), "s"(rsrc), "s"(toff)
-                     : "memory", "m0");
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * CH));
+        if (on)
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds ; whole tile"
+                       :
+                       : "s"(m0v), "v"(vo[j]), "s"(rsrc), "s"(stoff)
+                       : "memory", "m0");
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * 1024));
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds ; checked tile"
-                     :
-                     : "s"(m0v), "v"(vo[j] + toff), "s"(rsrc), "s"(0)
-                     : "memory", "m0");
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)((j * NW + wave) * CH));
+        if (on)
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds ; checked tile"
+                       :
+                       : "s"(m0v), "v"(vo[j] + toff), "s"(rsrc), "s"(0)
+                       : "memory", "m0");
       }
     }
   }
@@ -178,6 +187,38 @@ __device__ __forceinline__ void tile_dot_swz(f32x16& acc, const char* tile, cons
   constexpr int NC = D * (int)sizeof(T) / 16;
 #pragma unroll
   for (int c = 0; c < NC / 2; ++c) mma_chunk<T>(acc, lds_read16(tile + off[c]), b_regs[c]);
+}
+
+// Scheduling groups for a straight run of N LDS operand reads feeding N MFMAs: the first P reads
+// go out before any MFMA, then each pair of MFMAs is followed by the next pair of reads, so every
+// read is issued about P MFMAs before its consumer.  Only instructions of the enclosing basic block
+// are affected.
+template <int N, int P>
+__device__ __forceinline__ void sched_read_ahead() {
+  static_assert(P <= N && (N - P) % 2 == 0, "read-ahead pattern");
+  __builtin_amdgcn_sched_group_barrier(0x100, P, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < (N - P) / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
+}
+
+// Both 32x32 logit tiles of one step: st from the DT-feature rows at `tt`, ss from the DS-feature
+// rows at `ts`, the two accumulation chains interleaved so that neither MFMA waits on its
+// predecessor's result.  Operand reads: DT*sizeof(T)/32 + DS*sizeof(T)/32 ds_read_b128.
+template <typename T, int DT, int DS>
+__device__ __forceinline__ void tile_dot2_swz(f32x16& st, f32x16& ss, const char* tt, const char* ts,
+                                              const int* off_t, const int* off_s, const u32x4* bt,
+                                              const u32x4* bs) {
+  constexpr int NT2 = DT * (int)sizeof(T) / 32, NS2 = DS * (int)sizeof(T) / 32;
+  constexpr int NM = NT2 > NS2 ? NT2 : NS2;
+#pragma unroll
+  for (int c = 0; c < NM; ++c) {
+    if (c < NT2) mma_chunk<T>(st, lds_read16(tt + off_t[c]), bt[c]);
+    if (c < NS2) mma_chunk<T>(ss, lds_read16(ts + off_s[c]), bs[c]);
+  }
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, source
