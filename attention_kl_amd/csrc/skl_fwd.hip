@@ -18,12 +18,11 @@
 // lane halves of a row keep separate running states over disjoint key subsets
 // and are merged once at the end, so the key loop needs no cross-lane traffic.
 //
-// Schedule: key tiles are prefetched from HBM/L2 into registers one tile ahead
-// and written to a double-buffered LDS ring (one barrier per tile).  Tiles that
-// are fully allowed for every row of the workgroup run a software pipeline: the
-// MFMAs of key subtile s+1 are issued in the same basic block as the exp/VALU
-// work of subtile s, so the matrix cores and the VALU overlap.  The few tiles on
-// the causal diagonal or past the ragged end run a separate masked loop.
+// Schedule: 32-key tiles reach LDS by buffer->LDS DMA into a 3-slot ring, two
+// tiles ahead, one barrier per tile; three workgroups share a CU, so while one
+// wavefront waits on its MFMAs the others run their exp/VALU work.  Keys a row
+// may not see (causal diagonal, ragged end) are set to -inf in the logit tile
+// under a wave-uniform branch, then every tile takes the same update.
 #include "skl_device.hpp"
 #include "skl_kernels.hpp"
 
@@ -43,25 +42,39 @@ struct RowState {
   float l_t, l_s, acc;
 };
 
+// max(a, b, c) as one v_max3_f32.  Logits here are finite or -inf, never NaN, so the NaN
+// quieting the compiler puts in front of fmaxf (one extra VALU op per operand that is not
+// known to be quiet, such as an MFMA result) is not needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Online update with one 32-key subtile: st/ss are the raw (unscaled) logits of this
 // lane's 16 keys; masked keys are -inf in st/ss, dif = (a - b) / scale_t is finite.
 __device__ __forceinline__ void online_update(RowState& s, const f32x16& st, const f32x16& ss, const float* dif,
                                               float c_t, float c_s) {
-  float mx = fmaxf(st[0], st[1]), my = fmaxf(ss[0], ss[1]);
+  float mx = max3(st[0], st[1], st[2]), my = max3(ss[0], ss[1], ss[2]);
 #pragma unroll
-  for (int i = 2; i < 16; ++i) {
-    mx = fmaxf(mx, st[i]);
-    my = fmaxf(my, ss[i]);
+  for (int i = 3; i < 15; i += 2) {
+    mx = max3(mx, st[i], st[i + 1]);
+    my = max3(my, ss[i], ss[i + 1]);
   }
-  const float mt_new = fmaxf(s.m_t, mx * c_t);
-  const float ms_new = fmaxf(s.m_s, my * c_s);
+  mx = max3(mx, st[15], mx);
+  my = max3(my, ss[15], my);
+  const float mt_new = max3(s.m_t, mx * c_t, s.m_t);
+  const float ms_new = max3(s.m_s, my * c_s, s.m_s);
   const float al_t = fast_exp2(s.m_t - mt_new);
   const float al_s = fast_exp2(s.m_s - ms_new);
   s.m_t = mt_new;
   s.m_s = ms_new;
-  float pt = 0.f, ps = 0.f, pa = 0.f;
+  // partial sums of this subtile, started from its first key
+  float pt = fast_exp2(fmaf(st[0], c_t, -mt_new));
+  float ps = fast_exp2(fmaf(ss[0], c_s, -ms_new));
+  float pa = pt * dif[0];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 1; i < 16; ++i) {
     const float e = fast_exp2(fmaf(st[i], c_t, -mt_new));
     const float f = fast_exp2(fmaf(ss[i], c_s, -ms_new));
     pt += e;
@@ -88,7 +101,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   __shared__ __attribute__((aligned(1024))) char slot0[TILE], slot1[TILE], slot2[TILE];
   static_assert(NBUF == 3, "one named array per ring slot");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, r32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: per-wave tests branch on SCC
   const int nbh = a.B * a.H;
   const int nqb = (a.Nq + BQ - 1) / BQ;
   const int bh = blockIdx.x % nbh;
@@ -140,42 +154,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   issue(0, 0);
   issue(1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
   // One step per tile; the loop is unrolled by the ring depth so every LDS address is a
-  // per-lane base plus an immediate.
-  for (int t0 = 0; t0 < ntiles; t0 += NBUF) {
+  // per-lane base plus an immediate.  The tile count is rounded up to a multiple of the ring
+  // depth: the extra tiles lie past every row's last key, so they are fully masked and leave the
+  // state unchanged, and the unrolled body needs no guard (whose join would copy the state).
+  const int ntiles_pad = (ntiles + NBUF - 1) / NBUF * NBUF;
+  for (int t0 = 0; t0 < ntiles_pad; t0 += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       const int t = t0 + u;
-      if (t < ntiles) {
+      {
         wait_vmcnt<NI>();  // tile t has landed (tile t+1 may still be in flight)
         __syncthreads();   // ... for every wave; and every wave is done with tile t-1
         issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
         const char* tile = slot_ptr(u);
         const int kb = t * BK;
-        const bool skip = CAUSAL && kb > q0w + 31 + off;  // no row of this wavefront reaches these keys
-        if (!skip) {
-          f32x16 st = {}, ss = {};
-          tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
-          tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
-          float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
+        f32x16 st = {}, ss = {};
+        tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
+        tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
+        float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
 #pragma unroll
-          for (int i = 0; i < 16; ++i) dif[i] = fmaf(ss[i], -a.ratio, st[i]);
-          const bool full = kb + 31 < a.Nk && (!CAUSAL || kb + 31 <= q0w + off);
-          // two separate calls: the unmasked path never merges with the masked one, so the
-          // logit registers are not copied on every step
-          if (full) {
-            online_update(rs, st, ss, dif, a.c_t, a.c_s);
-          } else {
-            f32x16 mt, ms;
+        for (int i = 0; i < 16; ++i) {
+          dif[i] = fmaf(ss[i], -a.ratio, st[i]);
+          // pin dif here, ahead of the masking branch: then no unmasked logit outlives the branch
+          // and the masking below rewrites st/ss in place instead of copying them on every tile
+          asm volatile("" : "+v"(dif[i]));
+        }
+        // A tile that no row of this wavefront reaches (causal) goes through the masked path too:
+        // with every key at -inf the update leaves the state bit for bit unchanged, and the loop
+        // keeps one definition of the state (no copies at a join).  Such tiles are under 1% of
+        // a causal problem's.
+        const bool full = t < ntiles && kb + 31 < a.Nk && (!CAUSAL || kb + 31 <= q0w + off);
+        if (!full) {  // in place, so the update below has one copy of its state
+          asm volatile("");  // keep this a branch: the compiler would otherwise select on every tile
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kb + acc_row(i, hf);
-              const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + off);
-              mt[i] = ok ? st[i] : -INFINITY;
-              ms[i] = ok ? ss[i] : -INFINITY;
-            }
-            online_update(rs, mt, ms, dif, a.c_t, a.c_s);
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + acc_row(i, hf);
+            const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + off);
+            st[i] = ok ? st[i] : -INFINITY;
+            ss[i] = ok ? ss[i] : -INFINITY;
           }
         }
+        online_update(rs, st, ss, dif, a.c_t, a.c_s);
+        // the new state exists before the next barrier: keeps each tile's update in its own step
+        asm volatile("" ::"v"(rs.m_t), "v"(rs.m_s), "v"(rs.l_t), "v"(rs.l_s), "v"(rs.acc));
       }
     }
   }
