@@ -157,10 +157,11 @@ int streamkl_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, 
   bool empty = false;
   int st = check_bwd(p, q_t, k_t, q_s, k_s, lse_t, lse_s, g, &empty);
   if (st != STREAMKL_OK) return st;
-  if ((dq_t == nullptr) != (dk_t == nullptr)) return STREAMKL_ERR_INVALID;
+  if ((dq_t == nullptr) != (dk_t == nullptr) || (dq_s == nullptr) != (dk_s == nullptr)) return STREAMKL_ERR_INVALID;
   if (empty) return STREAMKL_OK;
-  const bool teacher = dq_t != nullptr;
-  if ((st = check_f32(dq_s)) != STREAMKL_OK || (st = check_f32(dk_s)) != STREAMKL_OK) return st;
+  const bool teacher = dq_t != nullptr, student = dq_s != nullptr;
+  if (!teacher && !student) return STREAMKL_ERR_INVALID;  // no gradient asked for
+  if (student && ((st = check_f32(dq_s)) != STREAMKL_OK || (st = check_f32(dk_s)) != STREAMKL_OK)) return st;
   if (teacher) {
     if ((st = check_f32(dq_t)) != STREAMKL_OK || (st = check_f32(dk_t)) != STREAMKL_OK ||
         (st = check_f32(kl)) != STREAMKL_OK)
@@ -169,10 +170,12 @@ int streamkl_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, 
   const hipStream_t s = (hipStream_t)hip_stream;
   const bool causal = p->causal != 0;
   skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g);
-  a.dq = dq_s;
-  a.dk = dk_s;
-  if ((st = to_status(skl::launch_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
-  if ((st = to_status(skl::launch_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
+  if (student) {
+    a.dq = dq_s;
+    a.dk = dk_s;
+    if ((st = to_status(skl::launch_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
+    if ((st = to_status(skl::launch_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
+  }
   if (teacher) {
     a.dq = dq_t;
     a.dk = dk_t;

@@ -1,0 +1,98 @@
+"""Attention-KL distillation loss on the StreamKL primitive, with torch autograd.
+
+StreamKL abstract (arXiv 2026), S1: attention distillation trains one attention
+distribution to match another by minimising their KL divergence; S3: the
+primitive is meant to sit inside such a training loop.  This module is that
+glue, and only glue: the forward calls ``streamkl_fwd``, the backward calls
+``streamkl_bwd``; every number is computed by the library's kernels.
+
+The primitive returns the per-query-row divergence KL_i (float32 [B, H, N_Q]).
+Whatever reduction the caller applies to it with torch operations (a sum, a
+mean, a weighted sum, ...) reaches the backward as the per-row weight
+g_i = dL/dKL_i, which is exactly the ``g`` of the C ABI, so every loss that is
+a function of the rows is supported without special cases.
+
+Directions (the pages fix none, S1):
+  "forward"    KL(P_t || P_s)  teacher first, the primitive as defined
+  "reverse"    KL(P_s || P_t)  the primitive with the two sides exchanged; the
+               gradients of the student then come from the primitive's
+               teacher-gradient path
+  "symmetric"  KL(P_t || P_s) + KL(P_s || P_t)
+
+Gradients with respect to the teacher inputs are computed only when one of them
+requires grad.  The library returns float32 gradients; autograd needs them in
+the dtype of the input, so bf16 inputs receive bf16-rounded gradients (a relative
+rounding of at most 2^-9 per element, on top of the kernels' own error).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import streamkl as S
+
+DIRECTIONS = ("forward", "reverse", "symmetric")
+REDUCTIONS = ("none", "sum", "mean", "batchmean")
+
+
+class StreamKLFunction(torch.autograd.Function):
+    """Per-row KL(P_t || P_s) with its backward on the library.  Inputs [B, H, N, d]."""
+
+    @staticmethod
+    def forward(ctx, qt, kt, qs, ks, causal: bool, scale_t: Optional[float], scale_s: Optional[float]):
+        kl, lse_t, lse_s = S.fwd(qt, kt, qs, ks, causal=causal, scale_t=scale_t, scale_s=scale_s)
+        ctx.save_for_backward(qt, kt, qs, ks, kl, lse_t, lse_s)
+        ctx.cfg = (bool(causal), scale_t, scale_s)
+        return kl
+
+    @staticmethod
+    def backward(ctx, g):
+        qt, kt, qs, ks, kl, lse_t, lse_s = ctx.saved_tensors
+        causal, scale_t, scale_s = ctx.cfg
+        need_t = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        need_s = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
+        if not (need_t or need_s):
+            return (None,) * 7
+        g = g.to(torch.float32).contiguous()  # the upstream gradient may be a broadcast view
+        dq_s, dk_s, dq_t, dk_t = S.bwd(qt, kt, qs, ks, lse_t, lse_s, g, causal=causal,
+                                       kl=kl if need_t else None, teacher_grads=need_t, student_grads=need_s,
+                                       scale_t=scale_t, scale_s=scale_s)
+
+        def cast(grad, like, needed):
+            return grad.to(like.dtype) if (needed and grad is not None) else None
+
+        return (cast(dq_t, qt, ctx.needs_input_grad[0]), cast(dk_t, kt, ctx.needs_input_grad[1]),
+                cast(dq_s, qs, ctx.needs_input_grad[2]), cast(dk_s, ks, ctx.needs_input_grad[3]),
+                None, None, None)
+
+
+def attention_kl(qt, kt, qs, ks, *, causal: bool = False, scale_t: Optional[float] = None,
+                 scale_s: Optional[float] = None, direction: str = "forward", reduction: str = "none"):
+    """Attention-KL divergence between teacher (qt, kt) and student (qs, ks) attention rows.
+
+    Shapes [B, H, N_Q, d_t], [B, H, N_K, d_t], [B, H, N_Q, d_s], [B, H, N_K, d_s], bf16 or float32,
+    d unit-stride.  Softmax scales default to 1/sqrt(d) per side.
+
+    reduction: "none" -> per-row float32 [B, H, N_Q]; "sum" -> sum over rows; "mean" -> mean over
+    all B*H*N_Q rows; "batchmean" -> sum divided by B (per-sample divergence summed over heads
+    and rows).
+    """
+    if direction not in DIRECTIONS:
+        raise ValueError(f"direction must be one of {DIRECTIONS}, got {direction!r}")
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {REDUCTIONS}, got {reduction!r}")
+    if direction == "forward":
+        kl = StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s)
+    elif direction == "reverse":
+        kl = StreamKLFunction.apply(qs, ks, qt, kt, causal, scale_s, scale_t)
+    else:
+        kl = (StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s)
+              + StreamKLFunction.apply(qs, ks, qt, kt, causal, scale_s, scale_t))
+    if reduction == "none":
+        return kl
+    if reduction == "sum":
+        return kl.sum()
+    if reduction == "mean":
+        return kl.mean()
+    return kl.sum() / kl.shape[0]

@@ -136,23 +136,27 @@ def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, s
 
 
 def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads: bool = False,
-        scale_t=None, scale_s=None, out=None, stream=None):
-    """Gradients of sum_i g_i KL_i (streamkl_bwd): (dq_s, dk_s) or (dq_s, dk_s, dq_t, dk_t)."""
+        student_grads: bool = True, scale_t=None, scale_s=None, out=None, stream=None):
+    """Gradients of sum_i g_i KL_i (streamkl_bwd): (dq_s, dk_s, dq_t, dk_t), the pairs not asked for
+    returned as None (student pair by default, teacher pair with teacher_grads=True)."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
     dev = qt.device
     if out is None:
-        out = [torch.empty((p.B, p.H, p.Nq, p.d_s), dtype=torch.float32, device=dev),
-               torch.empty((p.B, p.H, p.Nk, p.d_s), dtype=torch.float32, device=dev)]
+        out = [None, None, None, None]
+        if student_grads:
+            out[0] = torch.empty((p.B, p.H, p.Nq, p.d_s), dtype=torch.float32, device=dev)
+            out[1] = torch.empty((p.B, p.H, p.Nk, p.d_s), dtype=torch.float32, device=dev)
         if teacher_grads:
-            out += [torch.empty((p.B, p.H, p.Nq, p.d_t), dtype=torch.float32, device=dev),
-                    torch.empty((p.B, p.H, p.Nk, p.d_t), dtype=torch.float32, device=dev)]
-    dq_s, dk_s = out[0], out[1]
+            out[2] = torch.empty((p.B, p.H, p.Nq, p.d_t), dtype=torch.float32, device=dev)
+            out[3] = torch.empty((p.B, p.H, p.Nk, p.d_t), dtype=torch.float32, device=dev)
+    out = list(out) + [None] * (4 - len(out))
+    dq_s, dk_s = (out[0], out[1]) if student_grads else (None, None)
     dq_t, dk_t = (out[2], out[3]) if teacher_grads else (None, None)
     _check(lib().streamkl_bwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
                               _ptr(kl), _ptr(g), _ptr(dq_s), _ptr(dk_s), _ptr(dq_t), _ptr(dk_t), _stream(stream)),
            "streamkl_bwd")
-    return tuple(out)
+    return dq_s, dk_s, dq_t, dk_t
 
 
 def bwd_dq(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None):

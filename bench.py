@@ -161,6 +161,35 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int = 
     return ent
 
 
+def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3):
+    """The same step (forward, student dQ and dK) through torch autograd: sum_i g_i KL_i .backward().
+
+    Beyond the raw kernels it pays for autograd bookkeeping, output allocation and the cast of
+    the float32 gradients to the bf16 dtype of the inputs.
+    """
+    import torch
+    from attention_kl_amd.loss import attention_kl
+    qs_ = qs.detach().requires_grad_(True)
+    ks_ = ks.detach().requires_grad_(True)
+
+    def run():
+        qs_.grad = ks_.grad = None
+        kl = attention_kl(qt, kt, qs_, ks_, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+        (kl * g).sum().backward()
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": round(ms, 4), "overhead_ms": round(ms - raw_ms, 4), "steps": steps,
+            "what": "attention_kl(...) then (kl * g).sum().backward(), bf16 gradients into q_s, k_s"}
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-pmc":
         # python bench.py --ingest-pmc <fetch counter csv> <write counter csv> [workload id]
@@ -175,6 +204,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="synthetic config id (3 = b1h32n32768d128 causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=12288)
+    ap.add_argument("--no-autograd", action="store_true",
+                    help="skip timing the same step through the torch autograd wrapper (attention_kl_amd.loss)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -276,6 +307,8 @@ def main():
         "kernels": kern, "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
+    if not args.no_autograd:
+        out["autograd"] = autograd_step(w, qt, kt, qs, ks, g, step_ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)

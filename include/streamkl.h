@@ -57,7 +57,8 @@ typedef enum {
   STREAMKL_OK = 0,
   STREAMKL_ERR_INVALID = 1,     /* bad argument: NULL pointer, negative size, Nk == 0 with rows to
                                    compute, causal with Nq > Nk, non-positive or non-finite scale,
-                                   d stride != 1, only one of dq_t/dk_t given                       */
+                                   d stride != 1, only one pointer of a gradient pair given, or no
+                                   gradient asked for                                               */
   STREAMKL_ERR_UNSUPPORTED = 2, /* valid but not built: d_t or d_s not in {64, 128}, misaligned base
                                    pointer or stride (16-byte alignment needed), dtype unknown, or
                                    one (b, h) slice spanning 2 GiB or more ((N + 512) * n-stride
@@ -90,10 +91,11 @@ int streamkl_fwd(const streamkl_problem_t* p,
 
 /* Backward (S5): gradients of sum_i g_i KL_i.  Needs the forward's lse_t, lse_s
  * (and kl when teacher gradients are asked for; may be NULL otherwise) and the
- * per-row weights g.  dq_s, dk_s are always written.  dq_t, dk_t: both NULL =
- * student gradients only; both non-NULL = teacher gradients too; one of them
- * NULL = STREAMKL_ERR_INVALID.  Launches the key-owner then the query-owner
- * kernels (plus the teacher pair) on hip_stream.                                  */
+ * per-row weights g.  Outputs come in pairs, each pair both NULL (not computed)
+ * or both non-NULL (written): dq_s, dk_s the student gradients, dq_t, dk_t the
+ * teacher gradients.  One pointer of a pair NULL, or both pairs NULL, =
+ * STREAMKL_ERR_INVALID.  Launches, for each pair asked for, the key-owner then
+ * the query-owner kernel on hip_stream (student pair first).                     */
 int streamkl_bwd(const streamkl_problem_t* p,
                  const void* q_t, const void* k_t, const void* q_s, const void* k_s,
                  const float* lse_t, const float* lse_s, const float* kl, const float* g,

@@ -98,6 +98,14 @@ def test_bwd_argument_rules():
     # missing g
     assert L.streamkl_bwd(ctypes.byref(p), *PTRS, st[0], st[1], None, None, A + 0xB000, A + 0xC000, None, None,
                           None) == S.ERR_INVALID
+    # only one student output given; no gradient asked for at all
+    assert L.streamkl_bwd(ctypes.byref(p), *PTRS, st[0], st[1], None, st[3], A + 0xB000, None, None, None,
+                          None) == S.ERR_INVALID
+    assert L.streamkl_bwd(ctypes.byref(p), *PTRS, st[0], st[1], None, st[3], None, None, None, None,
+                          None) == S.ERR_INVALID
+    # teacher gradients alone still need kl
+    assert L.streamkl_bwd(ctypes.byref(p), *PTRS, st[0], st[1], None, st[3], None, None, A + 0xB000, A + 0xC000,
+                          None) == S.ERR_INVALID
     assert L.streamkl_bwd_dq(ctypes.byref(p), *PTRS, st[0], st[1], st[3], None, None) == S.ERR_INVALID
     assert L.streamkl_bwd_dk(ctypes.byref(_problem(d_s=48)), *PTRS, st[0], st[1], st[3], A, None) == \
         S.ERR_UNSUPPORTED

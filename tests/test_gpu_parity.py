@@ -26,7 +26,7 @@ def _run_gpu(w, dev_in, teacher=False):
     grads = S.bwd(qt, kt, qs, ks, lt, ls, g, causal=w.causal, kl=kl, teacher_grads=teacher,
                   scale_t=w.scale_t, scale_s=w.scale_s)
     torch.cuda.synchronize()
-    return (kl.cpu().numpy(), lt.cpu().numpy(), ls.cpu().numpy()), [x.cpu().numpy() for x in grads]
+    return (kl.cpu().numpy(), lt.cpu().numpy(), ls.cpu().numpy()), [x.cpu().numpy() for x in grads if x is not None]
 
 
 def _check_full(w, teacher=False):
@@ -162,7 +162,7 @@ def _sampled(w, heads, rows, keys):
     qt, kt, qs, ks = dev_in
     kl, lt, ls = S.fwd(qt, kt, qs, ks, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
     g = torch.from_numpy(wl.full_g(w)).cuda()
-    dq, dk = S.bwd(qt, kt, qs, ks, lt, ls, g, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    dq, dk, _, _ = S.bwd(qt, kt, qs, ks, lt, ls, g, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
     torch.cuda.synchronize()
     rt = rtol_of(w)
     # properties over every row
