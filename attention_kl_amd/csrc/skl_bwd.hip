@@ -235,12 +235,11 @@ bwd_kernel(const BwdArgs a) {
   const float* kl_bh = TEACHER ? a.kl + (int64_t)bh * a.Nq : nullptr;
 
   // query-owner: this lane's row statistics (log2 units), constant over the key stream
-  float own_lt = 0.f, own_ls = 0.f, own_g = 0.f, own_c = 0.f;
+  float own_lt = 0.f, own_ls = 0.f, own_c = 0.f;
   if constexpr (OWN_Q) {
     if (ovalid) {
       own_lt = lse_t_bh[orow] * kLog2e;
       own_ls = lse_s_bh[orow] * kLog2e;
-      own_g = g_bh[orow];
       if constexpr (TEACHER) own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
     }
   }
@@ -369,7 +368,7 @@ bwd_kernel(const BwdArgs a) {
       if constexpr (OWN_Q) {
         lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
         ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
-        gg4 = f32x4{own_g, own_g, own_g, own_g};
+        gg4 = f32x4{1.f, 1.f, 1.f, 1.f};  // the row weight g is constant along the stream: applied at the store
         cc4 = f32x4{own_c, own_c, own_c, own_c};
       } else {
         const int ql = 8 * g4 + 4 * hf;
@@ -500,12 +499,19 @@ bwd_kernel(const BwdArgs a) {
 
   const float scale = TEACHER ? a.scale_t : a.scale_s;
   float* out = (OWN_Q ? a.dq : a.dk) + (int64_t)bh * n_own * DX;
+  // query owner: dS was formed without the row weight (it is one factor per output row)
+  float rscale[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = o0w + acc_row(i, hf);
+    rscale[i] = OWN_Q ? (r < n_own ? scale * g_bh[r] : 0.f) : scale;
+  }
 #pragma unroll
   for (int db = 0; db < DX / 32; ++db) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = o0w + acc_row(i, hf);
-      if (r < n_own) out[(int64_t)r * DX + db * 32 + r32] = scale * dacc[db][i];
+      if (r < n_own) out[(int64_t)r * DX + db * 32 + r32] = rscale[i] * dacc[db][i];
     }
   }
 }
