@@ -325,13 +325,15 @@ bwd_kernel(const BwdArgs a) {
     dsr.set(z);
   }
 
-  // Ping-pong, key owner: wave 4 + k of group 1 converts statistic k of the tile in slot u.
-  auto convert_stats = [&](int u, const char* sl) {
+  // Ping-pong, key owner: wave 4 + k of group 1 converts statistic k of the tile in slot u, in two
+  // halves around its vector phase: the LDS reads go out first and the converted value is stored
+  // at the end, so their latency hides behind the dS work instead of delaying this wave's barrier.
+  auto stats_load = [&](const char* sl) -> float {
+    float v = 0.f;
     if constexpr (CSLOT) {
       const int k = wave - 4;
       if (k < (TEACHER ? 4 : 3) && hf == 0) {
         const float* raw = reinterpret_cast<const float*>(sl + TILE);
-        float v;
         if (k == 0)
           v = raw[r32] * kLog2e;
         else if (k == 1)
@@ -340,10 +342,17 @@ bwd_kernel(const BwdArgs a) {
           v = raw[128 + r32];
         else
           v = raw[192 + r32] + raw[r32] - raw[64 + r32];
-        cst[u][k][r32] = v;
       }
     }
+    return v;
   };
+  auto stats_store = [&](int u, float v) {
+    if constexpr (CSLOT) {
+      const int k = wave - 4;
+      if (k < (TEACHER ? 4 : 3) && hf == 0) cst[u][k][r32] = v;
+    }
+  };
+  auto convert_stats = [&](int u, const char* sl) { stats_store(u, stats_load(sl)); };
 
   // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
   auto vector_phase = [&](int s, int u, const char* sl) {
@@ -466,9 +475,13 @@ bwd_kernel(const BwdArgs a) {
           __syncthreads();
           // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
           if (s < ntile) {
-            if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
+            float cv = 0.f;
+            if (grp == 1) {
+              issue(s + PD + 1, (u + PD + 1) % NBUF);
+              cv = stats_load(slot_ptr((u + 1) % NBUF));  // tile s+1 landed in the last phase
+            }
             vector_phase(s, u, slot_ptr(u));
-            if (grp == 1) convert_stats((u + 1) % NBUF, slot_ptr((u + 1) % NBUF));  // tile s+1 landed
+            if (grp == 1) stats_store((u + 1) % NBUF, cv);
             if (grp == 0) wait_tile();
             __syncthreads();
           } else if (grp == 0) {
