@@ -33,6 +33,8 @@ int check_problem(const streamkl_problem_t* p, bool* empty) {
   if (p->causal && p->Nq > p->Nk) return STREAMKL_ERR_INVALID;
   if (p->Nq > kMaxDim || p->Nk > kMaxDim || p->B > kMaxDim || p->H > kMaxDim || p->B * p->H > kMaxDim)
     return STREAMKL_ERR_UNSUPPORTED;
+  for (const int64_t hk : {p->Hk_t, p->Hk_s})  // key heads per side: 0 (= H) or a divisor of H
+    if (hk < 0 || hk > p->H || (hk > 0 && p->H % hk != 0)) return STREAMKL_ERR_INVALID;
   const int64_t* strides[4] = {p->stride_qt, p->stride_kt, p->stride_qs, p->stride_ks};
   const int64_t rows[4] = {p->Nq, p->Nk, p->Nq, p->Nk};
   const int es = elt_size(p->dtype);
@@ -74,6 +76,8 @@ void fill_common(A& a, const streamkl_problem_t* p, const void* qt, const void* 
   }
   a.B = (int32_t)p->B;
   a.H = (int32_t)p->H;
+  a.gt = (int32_t)(p->Hk_t > 0 ? p->H / p->Hk_t : 1);
+  a.gs = (int32_t)(p->Hk_s > 0 ? p->H / p->Hk_s : 1);
   a.Nq = (int32_t)p->Nq;
   a.Nk = (int32_t)p->Nk;
   a.c_t = p->scale_t * 1.4426950408889634f;

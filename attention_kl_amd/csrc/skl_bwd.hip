@@ -169,7 +169,10 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 
 // OWN_Q: the workgroup owns query rows and writes dQ; otherwise it owns key rows and writes dK.
 // TEACHER: gradients of the teacher side (dQ_t / dK_t) instead of the student side.
-template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER, bool OWN_Q>
+// GRP (key owner only): several query heads read each key head of the gradient's side.  It is a
+// template flag, not just the run-time count, so that the one-head kernel has no pass loop around
+// its tile loop: with one, the compiler schedules the tile loop's LDS reads less far ahead.
+template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER, bool OWN_Q, bool GRP>
 __global__ __launch_bounds__(BwdTile<T>::NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2))) void
 bwd_kernel(const BwdArgs a) {
   using C = BwdTile<T>;
@@ -199,24 +202,23 @@ bwd_kernel(const BwdArgs a) {
   // barrier inside one is executed only by the waves that take it
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = NG == 2 ? (wave >> 2) : 0;
-  const int nbh = a.B * a.H;
+  // Heads: query head h reads teacher key head h / gt and student key head h / gs.  A query-owner
+  // workgroup serves one query head.  A key-owner workgroup owns key rows of one key head of the
+  // gradient's side and makes one pass over the stream of each of the GX query heads that read it,
+  // accumulating its dK rows over the passes.
+  static_assert(!(OWN_Q && GRP), "a query-owner workgroup serves one query head");
+  const int GX = GRP ? (TEACHER ? a.gt : a.gs) : 1;
+  const int HX = GRP ? a.H / GX : a.H;  // heads of the owned rows
+  const int nbh = a.B * HX;
   const int n_own = OWN_Q ? a.Nq : a.Nk, n_str = OWN_Q ? a.Nk : a.Nq;
   const int nob = (n_own + BW - 1) / BW;
-  const int bh = blockIdx.x % nbh;
+  const int bh = blockIdx.x % nbh;  // (batch, owned head)
   const int oi = blockIdx.x / nbh;
   // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
   const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
-  const int b = bh / a.H, h = bh % a.H;
+  const int b = bh / HX, ho = bh % HX;
   const int off = a.Nk - a.Nq;
 
-  const T* qt = reinterpret_cast<const T*>(a.qt) + b * a.sqt[0] + h * a.sqt[1];
-  const T* kt = reinterpret_cast<const T*>(a.kt) + b * a.skt[0] + h * a.skt[1];
-  const T* qs = reinterpret_cast<const T*>(a.qs) + b * a.sqs[0] + h * a.sqs[1];
-  const T* ks = reinterpret_cast<const T*>(a.ks) + b * a.sks[0] + h * a.sks[1];
-  const T* own_t = OWN_Q ? qt : kt;
-  const T* own_s = OWN_Q ? qs : ks;
-  const T* str_t = OWN_Q ? kt : qt;
-  const T* str_s = OWN_Q ? ks : qs;
   const int64_t own_pt = OWN_Q ? a.sqt[2] : a.skt[2], own_ps = OWN_Q ? a.sqs[2] : a.sks[2];
   const int64_t str_pt = (OWN_Q ? a.skt[2] : a.sqt[2]) * (int64_t)sizeof(T);
   const int64_t str_ps = (OWN_Q ? a.sks[2] : a.sqs[2]) * (int64_t)sizeof(T);
@@ -226,23 +228,34 @@ bwd_kernel(const BwdArgs a) {
   const int orow = o0w + r32;
   const bool ovalid = orow < n_own;
   u32x4 ot_r[NCT / 2], os_r[NCS / 2];
-  load_row_regs<T, DT>(ot_r, own_t + (int64_t)orow * own_pt, ovalid, hf);
-  load_row_regs<T, DS>(os_r, own_s + (int64_t)orow * own_ps, ovalid, hf);
 
-  const float* lse_t_bh = a.lse_t + (int64_t)bh * a.Nq;
-  const float* lse_s_bh = a.lse_s + (int64_t)bh * a.Nq;
-  const float* g_bh = a.g + (int64_t)bh * a.Nq;
-  const float* kl_bh = TEACHER ? a.kl + (int64_t)bh * a.Nq : nullptr;
+  // Per query head hq (one pass): the streamed operands, this wave's owned rows of both sides (the
+  // other side's key head can change from pass to pass), and the row statistics of head hq.
+  const T *str_t, *str_s;
+  const float *lse_t_bh, *lse_s_bh, *g_bh, *kl_bh;
+  auto set_head = [&](const BwdArgs& A, int hq) {
+    const T* qt = reinterpret_cast<const T*>(A.qt) + b * A.sqt[0] + hq * A.sqt[1];
+    const T* kt = reinterpret_cast<const T*>(A.kt) + b * A.skt[0] + (hq / A.gt) * A.skt[1];
+    const T* qs = reinterpret_cast<const T*>(A.qs) + b * A.sqs[0] + hq * A.sqs[1];
+    const T* ks = reinterpret_cast<const T*>(A.ks) + b * A.sks[0] + (hq / A.gs) * A.sks[1];
+    str_t = OWN_Q ? kt : qt;
+    str_s = OWN_Q ? ks : qs;
+    // the row offsets are formed from an opaque copy of orow in every pass: computed once before the
+    // pass loop instead, they would hold registers through the tile loop that its LDS reads need
+    int row = orow;
+    asm volatile("" : "+v"(row));
+    const bool valid = row < n_own;
+    load_row_regs<T, DT>(ot_r, (OWN_Q ? qt : kt) + (int64_t)row * own_pt, valid, hf);
+    load_row_regs<T, DS>(os_r, (OWN_Q ? qs : ks) + (int64_t)row * own_ps, valid, hf);
+    const int64_t r0 = ((int64_t)b * A.H + hq) * A.Nq;
+    lse_t_bh = A.lse_t + r0;
+    lse_s_bh = A.lse_s + r0;
+    g_bh = A.g + r0;
+    kl_bh = TEACHER ? A.kl + r0 : nullptr;
+  };
 
   // query-owner: this lane's row statistics (log2 units), constant over the key stream
   float own_lt = 0.f, own_ls = 0.f, own_c = 0.f;
-  if constexpr (OWN_Q) {
-    if (ovalid) {
-      own_lt = lse_t_bh[orow] * kLog2e;
-      own_ls = lse_s_bh[orow] * kLog2e;
-      if constexpr (TEACHER) own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
-    }
-  }
 
   // streamed range of the workgroup: tiles t_begin .. t_begin + ntile - 1 (ntile >= 1)
   int t_begin, t_end;
@@ -259,15 +272,17 @@ bwd_kernel(const BwdArgs a) {
   const int ntile = t_end - t_begin;
 
   // ---- streamed tiles: buffer->LDS DMA into the ring, two tiles ahead
-  const u32x4 rs_t = rsrc_words(str_t, (uint32_t)((n_str - 1) * str_pt + RBT));
-  const u32x4 rs_s = rsrc_words(str_s, (uint32_t)((n_str - 1) * str_ps + RBS));
-  u32x4 rst[4];
-  if constexpr (!OWN_Q) {
-    rst[0] = rsrc_words(lse_t_bh, (uint32_t)a.Nq * 4u);
-    rst[1] = rsrc_words(lse_s_bh, (uint32_t)a.Nq * 4u);
-    rst[2] = rsrc_words(g_bh, (uint32_t)a.Nq * 4u);
-    rst[3] = TEACHER ? rsrc_words(kl_bh, (uint32_t)a.Nq * 4u) : rst[2];
-  }
+  u32x4 rs_t, rs_s, rst[4];
+  auto set_rsrc = [&]() {  // buffer descriptors of the current head's streamed rows and statistics
+    rs_t = rsrc_words(str_t, (uint32_t)((n_str - 1) * str_pt + RBT));
+    rs_s = rsrc_words(str_s, (uint32_t)((n_str - 1) * str_ps + RBS));
+    if constexpr (!OWN_Q) {
+      rst[0] = rsrc_words(lse_t_bh, (uint32_t)a.Nq * 4u);
+      rst[1] = rsrc_words(lse_s_bh, (uint32_t)a.Nq * 4u);
+      rst[2] = rsrc_words(g_bh, (uint32_t)a.Nq * 4u);
+      rst[3] = TEACHER ? rsrc_words(kl_bh, (uint32_t)a.Nq * 4u) : rst[2];
+    }
+  };
   DmaT dma_t;
   DmaS dma_s;
   dma_t.init(str_pt, wave, lane);
@@ -320,10 +335,6 @@ bwd_kernel(const BwdArgs a) {
   for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
   f32x16 st = {}, ss = {};
   DsTile<T> dsr;  // dS of the last tile through the vector phase, for the gradient product
-  {
-    float z[16] = {};
-    dsr.set(z);
-  }
 
   // Ping-pong, key owner: wave 4 + k of group 1 converts statistic k of the tile in slot u, in two
   // halves around its vector phase: the LDS reads go out first and the converted value is stored
@@ -443,72 +454,88 @@ bwd_kernel(const BwdArgs a) {
     if constexpr (sizeof(T) == 2) sched_read_ahead<NRG + NRL, 6>();
   };
 
-  if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
-    static_assert(TILE % 16 == 0, "slot fill");
-#pragma unroll
-    for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
-  }
-  wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
-#pragma unroll
-  for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
-  wait_tile();
-  __syncthreads();
-  if constexpr (NG == 2) {
-    // Ring protocol (phases p = 0, 1, ...; tile s is read from phase 2s to 2s+3): tile s+PD is
-    // issued at the start of phase 2s into the slot of tile s-2, and each wave waits for its share
-    // of tile s+1 at the end of phase 2s+1, before that phase's barrier.  The last slot, read by
-    // the s = 0 gradient product, first receives a tile in phase 2.
-    if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
-      issue(PD, PD);
-      convert_stats(0, ring[0]);
-      __syncthreads();
+  for (int pass = 0; pass < GX; ++pass) {
+    set_head(a, ho * GX + pass);
+    set_rsrc();
+    if constexpr (OWN_Q) {
+      if (ovalid) {
+        own_lt = lse_t_bh[orow] * kLog2e;
+        own_ls = lse_s_bh[orow] * kLog2e;
+        if constexpr (TEACHER) own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
+      }
     }
-    for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
+    {
+      float z[16] = {};
+      dsr.set(z);
+    }
+    if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
+      static_assert(TILE % 16 == 0, "slot fill");
 #pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        const int s = s0 + u;
-        if (s <= ntile) {
-          // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
-          if (grp == 0) issue(s + PD, (u + PD) % NBUF);
-          matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
-          if (grp == 1) wait_tile();
-          __syncthreads();
-          // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
-          if (s < ntile) {
-            float cv = 0.f;
-            if (grp == 1) {
-              issue(s + PD + 1, (u + PD + 1) % NBUF);
-              cv = stats_load(slot_ptr((u + 1) % NBUF));  // tile s+1 landed in the last phase
-            }
-            vector_phase(s, u, slot_ptr(u));
-            if (grp == 1) stats_store((u + 1) % NBUF, cv);
-            if (grp == 0) wait_tile();
+      for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
+    }
+    wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
+#pragma unroll
+    for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
+    wait_tile();
+    __syncthreads();
+    if constexpr (NG == 2) {
+      // Ring protocol (phases p = 0, 1, ...; tile s is read from phase 2s to 2s+3): tile s+PD is
+      // issued at the start of phase 2s into the slot of tile s-2, and each wave waits for its share
+      // of tile s+1 at the end of phase 2s+1, before that phase's barrier.  The last slot, read by
+      // the s = 0 gradient product, first receives a tile in phase 2.
+      if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
+        issue(PD, PD);
+        convert_stats(0, ring[0]);
+        __syncthreads();
+      }
+      for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          const int s = s0 + u;
+          if (s <= ntile) {
+            // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
+            if (grp == 0) issue(s + PD, (u + PD) % NBUF);
+            matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
+            if (grp == 1) wait_tile();
             __syncthreads();
-          } else if (grp == 0) {
-            __syncthreads();  // group 0's last phase, matching group 1's late start
+            // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
+            if (s < ntile) {
+              float cv = 0.f;
+              if (grp == 1) {
+                issue(s + PD + 1, (u + PD + 1) % NBUF);
+                cv = stats_load(slot_ptr((u + 1) % NBUF));  // tile s+1 landed in the last phase
+              }
+              vector_phase(s, u, slot_ptr(u));
+              if (grp == 1) stats_store((u + 1) % NBUF, cv);
+              if (grp == 0) wait_tile();
+              __syncthreads();
+            } else if (grp == 0) {
+              __syncthreads();  // group 0's last phase, matching group 1's late start
+            }
+          }
+        }
+      }
+    } else {
+      // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
+      // and tile s+1 waited for at its end.
+      for (int s0 = 0; s0 < ntile; s0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          const int s = s0 + u;
+          if (s < ntile) {
+            issue(s + PD, (u + PD) % NBUF);
+            logit_phase(s, slot_ptr(u));
+            vector_phase(s, u, slot_ptr(u));
+            grad_phase(s, slot_ptr(u));
+            wait_tile();
+            __syncthreads();
           }
         }
       }
     }
-  } else {
-    // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
-    // and tile s+1 waited for at its end.
-    for (int s0 = 0; s0 < ntile; s0 += NBUF) {
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        const int s = s0 + u;
-        if (s < ntile) {
-          issue(s + PD, (u + PD) % NBUF);
-          logit_phase(s, slot_ptr(u));
-          vector_phase(s, u, slot_ptr(u));
-          grad_phase(s, slot_ptr(u));
-          wait_tile();
-          __syncthreads();
-        }
-      }
-    }
+    wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
+    if (pass + 1 < GX) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
   }
-  wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS when it exits
 
   const float scale = TEACHER ? a.scale_t : a.scale_s;
   float* out = (OWN_Q ? a.dq : a.dk) + (int64_t)bh * n_own * DX;
@@ -533,10 +560,20 @@ bwd_kernel(const BwdArgs a) {
 template <typename T, int DT, int DS, bool C, bool TE, bool OWN_Q>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int n_own = OWN_Q ? a.Nq : a.Nk;
-  const int64_t nblk = (int64_t)((n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * a.H;
+  // owned heads: query heads, or the key heads of the gradient's side
+  const int gx = OWN_Q ? 1 : (TE ? a.gt : a.gs);
+  const int64_t nblk = (int64_t)((n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * (a.H / gx);
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, OWN_Q>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s, a);
+  if constexpr (!OWN_Q) {
+    if (gx > 1) {
+      hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, false, true>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s,
+                         a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, OWN_Q, false>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -112,9 +112,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   const int off = a.Nk - a.Nq;
 
   const T* qt = reinterpret_cast<const T*>(a.qt) + b * a.sqt[0] + h * a.sqt[1];
-  const char* kt = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.kt) + b * a.skt[0] + h * a.skt[1]);
+  // grouped-query attention: query head h reads key head h / g of each side
+  const char* kt =
+      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.kt) + b * a.skt[0] + (h / a.gt) * a.skt[1]);
   const T* qs = reinterpret_cast<const T*>(a.qs) + b * a.sqs[0] + h * a.sqs[1];
-  const char* ks = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.ks) + b * a.sks[0] + h * a.sks[1]);
+  const char* ks =
+      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.ks) + b * a.sks[0] + (h / a.gs) * a.sks[1]);
   const int64_t kt_pitch = a.skt[2] * (int64_t)sizeof(T), ks_pitch = a.sks[2] * (int64_t)sizeof(T);
 
   const int q0 = qb * BQ;

@@ -14,8 +14,9 @@ struct FwdArgs {
   float* kl;
   float* lse_t;
   float* lse_s;
-  int64_t sqt[3], skt[3], sqs[3], sks[3];  // (b, h, n) element strides
+  int64_t sqt[3], skt[3], sqs[3], sks[3];  // (b, h, n) element strides; K strides per key head
   int32_t B, H, Nq, Nk;
+  int32_t gt, gs;   // query heads per key head (teacher, student): query head h reads key head h / g
   float c_t, c_s;   // scale * log2(e): logits enter exp2 in these units
   float ratio;      // scale_s / scale_t
   float scale_t;
@@ -31,9 +32,10 @@ struct BwdArgs {
   const float* kl;  // read only for teacher gradients
   const float* g;
   float* dq;  // query-owner kernel output [B,H,Nq,d_side]
-  float* dk;  // key-owner kernel output   [B,H,Nk,d_side]
+  float* dk;  // key-owner kernel output   [B,Hk_side,Nk,d_side]
   int64_t sqt[3], skt[3], sqs[3], sks[3];
   int32_t B, H, Nq, Nk;
+  int32_t gt, gs;  // query heads per key head (teacher, student)
   float c_t, c_s;            // scale * log2(e)
   float scale_t, scale_s;
 };

@@ -36,7 +36,8 @@ class Problem(ctypes.Structure):
                 ("d_t", ctypes.c_int32), ("d_s", ctypes.c_int32),
                 ("scale_t", ctypes.c_float), ("scale_s", ctypes.c_float),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("stride_qt", _I64x3), ("stride_kt", _I64x3), ("stride_qs", _I64x3), ("stride_ks", _I64x3)]
+                ("stride_qt", _I64x3), ("stride_kt", _I64x3), ("stride_qs", _I64x3), ("stride_ks", _I64x3),
+                ("Hk_t", ctypes.c_int64), ("Hk_s", ctypes.c_int64)]
 
 
 _lib = None
@@ -94,7 +95,10 @@ def _stream(stream) -> Optional[int]:
 
 def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
                  scale_s: Optional[float] = None) -> Problem:
-    """Describe four [B, H, N, d] tensors (d unit-stride) as a streamkl_problem_t."""
+    """Describe q [B, H, Nq, d] and k [B, Hk, Nk, d] tensors (d unit-stride) as a streamkl_problem_t.
+
+    Each side's key-head count Hk (k.shape[1]) must divide H: query head h reads key head
+    h // (H // Hk) of that side (grouped-query attention; Hk == H is one key head per query head)."""
     import torch
     for name, t in (("q_t", qt), ("k_t", kt), ("q_s", qs), ("k_s", ks)):
         if t.dim() != 4:
@@ -104,15 +108,20 @@ def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
         if t.dtype != qt.dtype:
             raise ValueError("all four inputs must share one dtype")
     B, H, Nq, d_t = qt.shape
-    Nk = kt.shape[2]
-    d_s = qs.shape[3]
-    if tuple(kt.shape) != (B, H, Nk, d_t) or tuple(qs.shape) != (B, H, Nq, d_s) or tuple(ks.shape) != (B, H, Nk, d_s):
+    Hk_t, Nk = kt.shape[1], kt.shape[2]
+    Hk_s, d_s = ks.shape[1], qs.shape[3]
+    if (tuple(kt.shape) != (B, Hk_t, Nk, d_t) or tuple(qs.shape) != (B, H, Nq, d_s)
+            or tuple(ks.shape) != (B, Hk_s, Nk, d_s)):
         raise ValueError(f"shape mismatch: {tuple(qt.shape)} {tuple(kt.shape)} {tuple(qs.shape)} {tuple(ks.shape)}")
+    for name, hk in (("k_t", Hk_t), ("k_s", Hk_s)):
+        if H > 0 and (hk < 1 or H % hk != 0):
+            raise ValueError(f"{name} has {hk} heads, which does not divide the {H} query heads")
     dt = {torch.bfloat16: BF16, torch.float32: FP32}.get(qt.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {qt.dtype}")
     p = Problem()
     p.B, p.H, p.Nq, p.Nk, p.d_t, p.d_s = B, H, Nq, Nk, d_t, d_s
+    p.Hk_t, p.Hk_s = Hk_t, Hk_s
     p.scale_t = 1.0 / math.sqrt(d_t) if scale_t is None else scale_t
     p.scale_s = 1.0 / math.sqrt(d_s) if scale_s is None else scale_s
     p.causal = int(bool(causal))
@@ -146,10 +155,10 @@ def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads
         out = [None, None, None, None]
         if student_grads:
             out[0] = torch.empty((p.B, p.H, p.Nq, p.d_s), dtype=torch.float32, device=dev)
-            out[1] = torch.empty((p.B, p.H, p.Nk, p.d_s), dtype=torch.float32, device=dev)
+            out[1] = torch.empty((p.B, p.Hk_s, p.Nk, p.d_s), dtype=torch.float32, device=dev)
         if teacher_grads:
             out[2] = torch.empty((p.B, p.H, p.Nq, p.d_t), dtype=torch.float32, device=dev)
-            out[3] = torch.empty((p.B, p.H, p.Nk, p.d_t), dtype=torch.float32, device=dev)
+            out[3] = torch.empty((p.B, p.Hk_t, p.Nk, p.d_t), dtype=torch.float32, device=dev)
     out = list(out) + [None] * (4 - len(out))
     dq_s, dk_s = (out[0], out[1]) if student_grads else (None, None)
     dq_t, dk_t = (out[2], out[3]) if teacher_grads else (None, None)
@@ -175,7 +184,7 @@ def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
     if out is None:
-        out = torch.empty((p.B, p.H, p.Nk, p.d_s), dtype=torch.float32, device=qt.device)
+        out = torch.empty((p.B, p.Hk_s, p.Nk, p.d_s), dtype=torch.float32, device=qt.device)
     _check(lib().streamkl_bwd_dk(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
                                  _ptr(g), _ptr(out), _stream(stream)), "streamkl_bwd_dk")
     return out

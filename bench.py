@@ -206,6 +206,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=12288)
     ap.add_argument("--no-autograd", action="store_true",
                     help="skip timing the same step through the torch autograd wrapper (attention_kl_amd.loss)")
+    ap.add_argument("--student-key-heads", type=int, default=None,
+                    help="grouped student keys: K key heads shared by the H query heads (K divides H); key head j "
+                         "is the workload's head j*H/K.  Default: one key head per query head")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -232,11 +235,16 @@ def main():
         qt, kt, qs, ks = (torch.from_numpy(a).to(dev) for a in wl.full_f32(w))
     g = torch.from_numpy(wl.full_g(w)).to(dev)
     B, H = w.B, w.H
+    hk_s = H if args.student_key_heads is None else args.student_key_heads
+    if hk_s < 1 or H % hk_s != 0:
+        print(f"bench.py: --student-key-heads must divide H = {H}", file=sys.stderr)
+        sys.exit(2)
+    ks = ks[:, ::H // hk_s]
     kl = torch.empty((B, H, w.Nq), dtype=torch.float32, device=dev)
     lt = torch.empty_like(kl)
     ls = torch.empty_like(kl)
     dq = torch.empty((B, H, w.Nq, w.d_s), dtype=torch.float32, device=dev)
-    dk = torch.empty((B, H, w.Nk, w.d_s), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, hk_s, w.Nk, w.d_s), dtype=torch.float32, device=dev)
     kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
 
     def step(ev=None):
@@ -290,15 +298,16 @@ def main():
     achieved = dom_fl / kern[dominant]["ms"] / 1e9
     roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": MI355X_PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(dominant, w.name)}
+            "traffic": load_traffic(dominant, w.name) if hk_s == H else None}
     value = (fwd_fl + bwd_fl) / step_ms / 1e9
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded N(0,1) bf16 inputs of the workload's shape)",
-        "config": {"workload": w.name, "B": B, "H": H, "N_Q": w.Nq, "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s,
-                   "causal": w.causal, "teacher_grads": False},
+        "config": {"workload": w.name if hk_s == H else f"{w.name}-hks{hk_s}", "B": B, "H": H, "N_Q": w.Nq,
+                   "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s, "causal": w.causal, "teacher_grads": False,
+                   "student_key_heads": hk_s},
         "fwd_ms": fwd_ms, "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_fl / fwd_ms / 1e9, 2), "bwd_tflops": round(bwd_fl / bwd_ms / 1e9, 2),
         "fwd_frac_of_bf16_peak": round(fwd_fl / fwd_ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4),

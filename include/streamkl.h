@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10000 /* 1.0.0 */
+#define STREAMKL_VERSION 10100 /* 1.1.0: key heads per side (grouped-query attention) */
 
 typedef enum {
   STREAMKL_FP32 = 0, /* inputs float32; products on fp32 MFMA                */
@@ -57,8 +57,8 @@ typedef enum {
   STREAMKL_OK = 0,
   STREAMKL_ERR_INVALID = 1,     /* bad argument: NULL pointer, negative size, Nk == 0 with rows to
                                    compute, causal with Nq > Nk, non-positive or non-finite scale,
-                                   d stride != 1, only one pointer of a gradient pair given, or no
-                                   gradient asked for                                               */
+                                   d stride != 1, a key-head count that does not divide H, only one
+                                   pointer of a gradient pair given, or no gradient asked for      */
   STREAMKL_ERR_UNSUPPORTED = 2, /* valid but not built: d_t or d_s not in {64, 128}, misaligned base
                                    pointer or stride (16-byte alignment needed), dtype unknown, or
                                    one (b, h) slice spanning 2 GiB or more ((N + 512) * n-stride
@@ -66,12 +66,16 @@ typedef enum {
   STREAMKL_ERR_LAUNCH = 3       /* the HIP launch itself failed (hipGetLastError after launch)     */
 } streamkl_status_t;
 
-/* Problem description.  Q/K tensors are [B, H, N, d] with the d axis contiguous;
- * stride_*[0..2] are the element strides of the b, h and n axes (any order of
- * axes in memory is allowed as long as d is unit-stride).  All four inputs share
- * `dtype`.  Row statistics and gradients are dense and contiguous:
- * kl, lse_t, lse_s, g are float32 [B, H, Nq]; dq_s [B, H, Nq, d_s], dk_s
- * [B, H, Nk, d_s], dq_t [B, H, Nq, d_t], dk_t [B, H, Nk, d_t], all float32.   */
+/* Problem description.  Q tensors are [B, H, Nq, d], K tensors [B, Hk, Nk, d] with
+ * Hk = Hk_t or Hk_s key heads for that side, each dividing H: query head h reads
+ * key head h / (H / Hk) (grouped-query attention; Hk = H is one key head per query
+ * head, Hk = 1 one shared head).  The d axis is contiguous; stride_*[0..2] are the
+ * element strides of the b, head and n axes (any order of axes in memory is
+ * allowed as long as d is unit-stride).  All four inputs share `dtype`.  Row
+ * statistics and gradients are dense and contiguous: kl, lse_t, lse_s, g are
+ * float32 [B, H, Nq]; dq_s [B, H, Nq, d_s], dk_s [B, Hk_s, Nk, d_s], dq_t
+ * [B, H, Nq, d_t], dk_t [B, Hk_t, Nk, d_t], all float32; a key head's gradient
+ * sums over the query heads that read it.                                        */
 typedef struct {
   int64_t B, H, Nq, Nk;   /* B, H, Nq >= 0 (any zero = nothing to do, returns OK); Nk >= 1 when
                              there are rows; causal needs Nq <= Nk                              */
@@ -80,6 +84,7 @@ typedef struct {
   int32_t causal;         /* 0: every key; 1: key j allowed for row i iff j <= i + Nk - Nq      */
   int32_t dtype;          /* streamkl_dtype_t                                                    */
   int64_t stride_qt[3], stride_kt[3], stride_qs[3], stride_ks[3]; /* (b, h, n) strides, elements */
+  int64_t Hk_t, Hk_s;     /* key heads of teacher and student: each divides H; 0 means H          */
 } streamkl_problem_t;
 
 /* Forward (S4): KL_i, LSE_t,i, LSE_s,i for every row, float32 [B, H, Nq] each.

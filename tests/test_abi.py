@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared) <= exported
-    assert S.version() == 10000
+    assert S.version() == 10100
 
 
 def test_status_strings():
@@ -67,6 +67,10 @@ def fwd_status(p, ptrs=PTRS, outs=OUTS):
     (dict(scale_t=float("inf")), S.ERR_INVALID),
     (dict(stride_qt=[1, 1, 3]), S.ERR_UNSUPPORTED),  # 6-byte row stride breaks 16-byte alignment
     (dict(stride_ks=[-128, 128, 128]), S.ERR_INVALID),
+    (dict(H=4, Hk_t=3), S.ERR_INVALID),  # key heads must divide the query heads
+    (dict(H=4, Hk_s=8), S.ERR_INVALID),
+    (dict(H=4, Hk_s=-1), S.ERR_INVALID),
+    (dict(H=4, Hk_t=2, Hk_s=1, stride_qt=[1, 1, 3]), S.ERR_UNSUPPORTED),  # valid grouping: later checks run
 ])
 def test_fwd_rejects_bad_problems(kw, expected):
     assert fwd_status(_problem(**kw)) == expected
@@ -110,6 +114,37 @@ def test_bwd_argument_rules():
     assert L.streamkl_bwd_dk(ctypes.byref(_problem(d_s=48)), *PTRS, st[0], st[1], st[3], A, None) == \
         S.ERR_UNSUPPORTED
     assert L.streamkl_bwd(ctypes.byref(_problem(B=0)), *([0] * 12), None) == S.OK
+
+
+def test_problem_struct_layout_matches_the_header(tmp_path):
+    """The ctypes mirror has the C struct's size and field offsets (compiled from include/streamkl.h)."""
+    fields = [f[0] for f in S.Problem._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "streamkl.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(streamkl_problem_t));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(streamkl_problem_t, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(S.Problem)
+    assert got[1:] == [getattr(S.Problem, f).offset for f in fields]
+
+
+def test_grouped_key_heads_are_accepted_and_described():
+    # every divisor of H (0 meaning H) passes the problem checks: the misaligned pointer checked after
+    # them is what the call reports; a non-divisor stops at the problem checks
+    for hk_t, hk_s in ((0, 0), (1, 4), (2, 1), (4, 2)):
+        assert fwd_status(_problem(H=4, Hk_t=hk_t, Hk_s=hk_s), ptrs=[A + 2, A, A, A]) == S.ERR_UNSUPPORTED
+    assert fwd_status(_problem(H=4, Hk_t=3), ptrs=[A + 2, A, A, A]) == S.ERR_INVALID
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(2, 8, 4, 64)
+    p = S.make_problem(q, torch.zeros(2, 2, 6, 64), torch.zeros(2, 8, 4, 128), torch.zeros(2, 1, 6, 128), True)
+    assert (p.H, p.Hk_t, p.Hk_s, p.Nk, p.d_s) == (8, 2, 1, 6, 128)
+    with pytest.raises(ValueError):  # 3 key heads cannot serve 8 query heads
+        S.make_problem(q, torch.zeros(2, 3, 6, 64), q, torch.zeros(2, 8, 6, 64), False)
+    with pytest.raises(ValueError):  # key heads of the student's own dimension
+        S.make_problem(q, torch.zeros(2, 2, 6, 64), q, torch.zeros(2, 2, 6, 128), False)
 
 
 def test_python_binding_validates_shapes():
