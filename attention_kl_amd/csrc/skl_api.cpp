@@ -27,10 +27,19 @@ int check_problem(const streamkl_problem_t* p, bool* empty) {
     return STREAMKL_ERR_INVALID;
   if (elt_size(p->dtype) == 0) return STREAMKL_ERR_UNSUPPORTED;
   if ((p->d_t != 64 && p->d_t != 128) || (p->d_s != 64 && p->d_s != 128)) return STREAMKL_ERR_UNSUPPORTED;
-  *empty = (p->B == 0 || p->H == 0 || p->Nq == 0);
+  // packed variable-length batch: the segment bounds live in device memory; what the host can check
+  // is the pair of pointers and that the longest segment fits the packed axes
+  const bool packed = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
+  if (packed) {
+    if (!p->cu_seqlens_q || !p->cu_seqlens_k) return STREAMKL_ERR_INVALID;
+    if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0 || p->max_seqlen_q > p->Nq || p->max_seqlen_k > p->Nk)
+      return STREAMKL_ERR_INVALID;
+    if (!aligned(p->cu_seqlens_q, 4) || !aligned(p->cu_seqlens_k, 4)) return STREAMKL_ERR_UNSUPPORTED;
+  }
+  *empty = (p->B == 0 || p->H == 0 || p->Nq == 0 || (packed && p->max_seqlen_q == 0));
   if (*empty) return STREAMKL_OK;
   if (p->Nk == 0) return STREAMKL_ERR_INVALID;  // softmax over no keys
-  if (p->causal && p->Nq > p->Nk) return STREAMKL_ERR_INVALID;
+  if (!packed && p->causal && p->Nq > p->Nk) return STREAMKL_ERR_INVALID;
   if (p->Nq > kMaxDim || p->Nk > kMaxDim || p->B > kMaxDim || p->H > kMaxDim || p->B * p->H > kMaxDim)
     return STREAMKL_ERR_UNSUPPORTED;
   for (const int64_t hk : {p->Hk_t, p->Hk_s})  // key heads per side: 0 (= H) or a divisor of H
@@ -80,6 +89,11 @@ void fill_common(A& a, const streamkl_problem_t* p, const void* qt, const void* 
   a.gs = (int32_t)(p->Hk_s > 0 ? p->H / p->Hk_s : 1);
   a.Nq = (int32_t)p->Nq;
   a.Nk = (int32_t)p->Nk;
+  const bool packed = p->cu_seqlens_q != nullptr;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.mq = (int32_t)(packed ? p->max_seqlen_q : p->Nq);
+  a.mk = (int32_t)(packed ? p->max_seqlen_k : p->Nk);
   a.c_t = p->scale_t * 1.4426950408889634f;
   a.c_s = p->scale_s * 1.4426950408889634f;
 }

@@ -210,14 +210,16 @@ bwd_kernel(const BwdArgs a) {
   const int GX = GRP ? (TEACHER ? a.gt : a.gs) : 1;
   const int HX = GRP ? a.H / GX : a.H;  // heads of the owned rows
   const int nbh = a.B * HX;
-  const int n_own = OWN_Q ? a.Nq : a.Nk, n_str = OWN_Q ? a.Nk : a.Nq;
-  const int nob = (n_own + BW - 1) / BW;
+  const int nob = ((OWN_Q ? a.mq : a.mk) + BW - 1) / BW;
   const int bh = blockIdx.x % nbh;  // (batch, owned head)
   const int oi = blockIdx.x / nbh;
   // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
   const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
   const int b = bh / HX, ho = bh % HX;
-  const int off = a.Nk - a.Nq;
+  const Segment sg = segment_of(a, b);
+  const int n_own = OWN_Q ? sg.nq : sg.nk, n_str = OWN_Q ? sg.nk : sg.nq;
+  if (ob * BW >= n_own) return;  // past the end of a shorter segment of a packed batch (whole workgroup)
+  const int off = sg.nk - sg.nq;
 
   const int64_t own_pt = OWN_Q ? a.sqt[2] : a.skt[2], own_ps = OWN_Q ? a.sqs[2] : a.sks[2];
   const int64_t str_pt = (OWN_Q ? a.skt[2] : a.sqt[2]) * (int64_t)sizeof(T);
@@ -234,10 +236,10 @@ bwd_kernel(const BwdArgs a) {
   const T *str_t, *str_s;
   const float *lse_t_bh, *lse_s_bh, *g_bh, *kl_bh;
   auto set_head = [&](const BwdArgs& A, int hq) {
-    const T* qt = reinterpret_cast<const T*>(A.qt) + b * A.sqt[0] + hq * A.sqt[1];
-    const T* kt = reinterpret_cast<const T*>(A.kt) + b * A.skt[0] + (hq / A.gt) * A.skt[1];
-    const T* qs = reinterpret_cast<const T*>(A.qs) + b * A.sqs[0] + hq * A.sqs[1];
-    const T* ks = reinterpret_cast<const T*>(A.ks) + b * A.sks[0] + (hq / A.gs) * A.sks[1];
+    const T* qt = reinterpret_cast<const T*>(A.qt) + sg.bs * A.sqt[0] + hq * A.sqt[1] + sg.q0 * A.sqt[2];
+    const T* kt = reinterpret_cast<const T*>(A.kt) + sg.bs * A.skt[0] + (hq / A.gt) * A.skt[1] + sg.k0 * A.skt[2];
+    const T* qs = reinterpret_cast<const T*>(A.qs) + sg.bs * A.sqs[0] + hq * A.sqs[1] + sg.q0 * A.sqs[2];
+    const T* ks = reinterpret_cast<const T*>(A.ks) + sg.bs * A.sks[0] + (hq / A.gs) * A.sks[1] + sg.k0 * A.sks[2];
     str_t = OWN_Q ? kt : qt;
     str_s = OWN_Q ? ks : qs;
     // the row offsets are formed from an opaque copy of orow in every pass: computed once before the
@@ -247,7 +249,7 @@ bwd_kernel(const BwdArgs a) {
     const bool valid = row < n_own;
     load_row_regs<T, DT>(ot_r, (OWN_Q ? qt : kt) + (int64_t)row * own_pt, valid, hf);
     load_row_regs<T, DS>(os_r, (OWN_Q ? qs : ks) + (int64_t)row * own_ps, valid, hf);
-    const int64_t r0 = ((int64_t)b * A.H + hq) * A.Nq;
+    const int64_t r0 = ((int64_t)sg.bs * A.H + hq) * A.Nq + sg.q0;
     lse_t_bh = A.lse_t + r0;
     lse_s_bh = A.lse_s + r0;
     g_bh = A.g + r0;
@@ -260,27 +262,29 @@ bwd_kernel(const BwdArgs a) {
   // streamed range of the workgroup: tiles t_begin .. t_begin + ntile - 1 (ntile >= 1)
   int t_begin, t_end;
   if constexpr (OWN_Q) {
-    const int q_last = min(a.Nq, o0 + BW) - 1;
-    const int kend = CAUSAL ? min(a.Nk, q_last + off + 1) : a.Nk;
+    const int q_last = min(n_own, o0 + BW) - 1;
+    const int kend = CAUSAL ? min(n_str, q_last + off + 1) : n_str;
     t_begin = 0;
     t_end = (kend + BS - 1) / BS;
   } else {
     const int qmin = CAUSAL ? max(0, o0 - off) : 0;  // first query that may see this block's first key
     t_begin = qmin / BS;
-    t_end = (a.Nq + BS - 1) / BS;
+    t_end = (n_str + BS - 1) / BS;
   }
-  const int ntile = t_end - t_begin;
+  // never negative: the two groups' barrier counts (2 ntile + 3 each) stay equal even for rows
+  // with no allowed key (an invalid segment of a packed batch)
+  const int ntile = max(t_end - t_begin, 0);
 
   // ---- streamed tiles: buffer->LDS DMA into the ring, two tiles ahead
   u32x4 rs_t, rs_s, rst[4];
   auto set_rsrc = [&]() {  // buffer descriptors of the current head's streamed rows and statistics
-    rs_t = rsrc_words(str_t, (uint32_t)((n_str - 1) * str_pt + RBT));
-    rs_s = rsrc_words(str_s, (uint32_t)((n_str - 1) * str_ps + RBS));
+    rs_t = rsrc_words(str_t, n_str > 0 ? (uint32_t)((n_str - 1) * str_pt + RBT) : 0u);
+    rs_s = rsrc_words(str_s, n_str > 0 ? (uint32_t)((n_str - 1) * str_ps + RBS) : 0u);
     if constexpr (!OWN_Q) {
-      rst[0] = rsrc_words(lse_t_bh, (uint32_t)a.Nq * 4u);
-      rst[1] = rsrc_words(lse_s_bh, (uint32_t)a.Nq * 4u);
-      rst[2] = rsrc_words(g_bh, (uint32_t)a.Nq * 4u);
-      rst[3] = TEACHER ? rsrc_words(kl_bh, (uint32_t)a.Nq * 4u) : rst[2];
+      rst[0] = rsrc_words(lse_t_bh, (uint32_t)n_str * 4u);
+      rst[1] = rsrc_words(lse_s_bh, (uint32_t)n_str * 4u);
+      rst[2] = rsrc_words(g_bh, (uint32_t)n_str * 4u);
+      rst[3] = TEACHER ? rsrc_words(kl_bh, (uint32_t)n_str * 4u) : rst[2];
     }
   };
   DmaT dma_t;
@@ -538,7 +542,8 @@ bwd_kernel(const BwdArgs a) {
   }
 
   const float scale = TEACHER ? a.scale_t : a.scale_s;
-  float* out = (OWN_Q ? a.dq : a.dk) + (int64_t)bh * n_own * DX;
+  float* out = (OWN_Q ? a.dq : a.dk) +
+               (((int64_t)sg.bs * HX + ho) * (OWN_Q ? a.Nq : a.Nk) + (OWN_Q ? sg.q0 : sg.k0)) * DX;
   // query owner: dS was formed without the row weight (it is one factor per output row)
   float rscale[16];
 #pragma unroll
@@ -559,7 +564,7 @@ bwd_kernel(const BwdArgs a) {
 // ----------------------------------------------------------------------------------------------
 template <typename T, int DT, int DS, bool C, bool TE, bool OWN_Q>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  const int n_own = OWN_Q ? a.Nq : a.Nk;
+  const int n_own = OWN_Q ? a.mq : a.mk;  // longest segment (dense batch: all rows)
   // owned heads: query heads, or the key heads of the gradient's side
   const int gx = OWN_Q ? 1 : (TE ? a.gt : a.gs);
   const int64_t nblk = (int64_t)((n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * (a.H / gx);

@@ -104,45 +104,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: per-wave tests branch on SCC
   const int nbh = a.B * a.H;
-  const int nqb = (a.Nq + BQ - 1) / BQ;
+  const int nqb = (a.mq + BQ - 1) / BQ;
   const int bh = blockIdx.x % nbh;
   const int qi = blockIdx.x / nbh;
   const int qb = CAUSAL ? (nqb - 1 - qi) : qi;  // causal: longest rows first
   const int b = bh / a.H, h = bh % a.H;
-  const int off = a.Nk - a.Nq;
+  const Segment sg = segment_of(a, b);
+  const int nq = sg.nq, nk = sg.nk;
+  const int q0 = qb * BQ;
+  if (q0 >= nq) return;  // past the end of a shorter segment of a packed batch (whole workgroup)
+  const int off = nk - nq;
 
-  const T* qt = reinterpret_cast<const T*>(a.qt) + b * a.sqt[0] + h * a.sqt[1];
+  const T* qt = reinterpret_cast<const T*>(a.qt) + sg.bs * a.sqt[0] + h * a.sqt[1] + sg.q0 * a.sqt[2];
   // grouped-query attention: query head h reads key head h / g of each side
-  const char* kt =
-      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.kt) + b * a.skt[0] + (h / a.gt) * a.skt[1]);
-  const T* qs = reinterpret_cast<const T*>(a.qs) + b * a.sqs[0] + h * a.sqs[1];
-  const char* ks =
-      reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.ks) + b * a.sks[0] + (h / a.gs) * a.sks[1]);
+  const char* kt = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.kt) + sg.bs * a.skt[0] +
+                                                 (h / a.gt) * a.skt[1] + sg.k0 * a.skt[2]);
+  const T* qs = reinterpret_cast<const T*>(a.qs) + sg.bs * a.sqs[0] + h * a.sqs[1] + sg.q0 * a.sqs[2];
+  const char* ks = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.ks) + sg.bs * a.sks[0] +
+                                                 (h / a.gs) * a.sks[1] + sg.k0 * a.sks[2]);
   const int64_t kt_pitch = a.skt[2] * (int64_t)sizeof(T), ks_pitch = a.sks[2] * (int64_t)sizeof(T);
 
-  const int q0 = qb * BQ;
   const int q0w = q0 + wave * 32;
   const int qrow = q0w + r32;
   u32x4 qt_r[NCT / 2], qs_r[NCS / 2];
-  load_row_regs<T, DT>(qt_r, qt + (int64_t)qrow * a.sqt[2], qrow < a.Nq, hf);
-  load_row_regs<T, DS>(qs_r, qs + (int64_t)qrow * a.sqs[2], qrow < a.Nq, hf);
+  load_row_regs<T, DT>(qt_r, qt + (int64_t)qrow * a.sqt[2], qrow < nq, hf);
+  load_row_regs<T, DS>(qs_r, qs + (int64_t)qrow * a.sqs[2], qrow < nq, hf);
 
   RowState rs{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
 
-  const int q_last = min(a.Nq, q0 + BQ) - 1;
-  const int kend = CAUSAL ? min(a.Nk, q_last + off + 1) : a.Nk;
-  const int ntiles = (kend + BK - 1) / BK;
+  const int q_last = min(nq, q0 + BQ) - 1;
+  const int kend = CAUSAL ? min(nk, q_last + off + 1) : nk;
+  const int ntiles = max(kend + BK - 1, 0) / BK;  // 0 only for rows with no key (an invalid segment)
 
   // K tiles: buffer->LDS DMA (zero past the last key) into a NBUF-deep ring, two tiles ahead
-  const u32x4 rk_t = rsrc_words(kt, (uint32_t)((a.Nk - 1) * kt_pitch + RBT));
-  const u32x4 rk_s = rsrc_words(ks, (uint32_t)((a.Nk - 1) * ks_pitch + RBS));
+  const u32x4 rk_t = rsrc_words(kt, nk > 0 ? (uint32_t)((nk - 1) * kt_pitch + RBT) : 0u);
+  const u32x4 rk_s = rsrc_words(ks, nk > 0 ? (uint32_t)((nk - 1) * ks_pitch + RBS) : 0u);
   DmaT dma_t;
   DmaS dma_s;
   dma_t.init(kt_pitch, wave, lane);
   dma_s.init(ks_pitch, wave, lane);
   auto slot_ptr = [&](int slot) -> char* { return slot == 0 ? slot0 : (slot == 1 ? slot1 : slot2); };
   auto issue = [&](int tile, int slot) {
-    const bool whole = (tile + 1) * BK <= a.Nk;
+    const bool whole = (tile + 1) * BK <= nk;
     dma_t.issue(rk_t, tile * BK * (int)kt_pitch, whole, slot_ptr(slot), wave);
     dma_s.issue(rk_s, tile * BK * (int)ks_pitch, whole, slot_ptr(slot) + BK * RBT, wave);
   };
@@ -186,13 +189,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
         // with every key at -inf the update leaves the state bit for bit unchanged, and the loop
         // keeps one definition of the state (no copies at a join).  Such tiles are under 1% of
         // a causal problem's.
-        const bool full = t < ntiles && kb + 31 < a.Nk && (!CAUSAL || kb + 31 <= q0w + off);
+        const bool full = t < ntiles && kb + 31 < nk && (!CAUSAL || kb + 31 <= q0w + off);
         if (!full) {  // in place, so the update below has one copy of its state
           asm volatile("");  // keep this a branch: the compiler would otherwise select on every tile
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb + acc_row(i, hf);
-            const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + off);
+            const bool ok = key < nk && (!CAUSAL || key <= qrow + off);
             st[i] = ok ? st[i] : -INFINITY;
             ss[i] = ok ? ss[i] : -INFINITY;
           }
@@ -215,9 +218,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   const float Ls = rs.l_s * g1 + o_ls * g2;
   const float A = rs.acc * f1 + o_acc * f2;
 
-  if (hf == 0 && qrow < a.Nq) {
+  if (hf == 0 && qrow < nq) {
     // true divisions: Ls / Lt is exactly 1 when the two states are bitwise equal
-    const int64_t o = ((int64_t)bh) * a.Nq + qrow;
+    const int64_t o = ((int64_t)sg.bs * a.H + h) * a.Nq + sg.q0 + qrow;
     a.kl[o] = a.scale_t * (A / Lt) + kLn2 * ((Ms - Mt) + fast_log2(Ls / Lt));
     a.lse_t[o] = kLn2 * (Mt + fast_log2(Lt));
     a.lse_s[o] = kLn2 * (Ms + fast_log2(Ls));
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 
 template <typename T, int DT, int DS, bool C>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-  const int64_t nqb = (a.Nq + FwdTile<T>::BQ - 1) / FwdTile<T>::BQ;
+  const int64_t nqb = (a.mq + FwdTile<T>::BQ - 1) / FwdTile<T>::BQ;
   const int64_t nblk = nqb * a.B * a.H;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;

@@ -17,6 +17,12 @@ struct FwdArgs {
   int64_t sqt[3], skt[3], sqs[3], sks[3];  // (b, h, n) element strides; K strides per key head
   int32_t B, H, Nq, Nk;
   int32_t gt, gs;   // query heads per key head (teacher, student): query head h reads key head h / g
+  // Packed variable-length batch (cu_q non-NULL): batch entry b is the segment of query rows
+  // cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1 of one packed axis of Nq / Nk rows;
+  // mq, mk bound the segment lengths (the grid).  Dense batch: cu_q = cu_k = NULL, mq = Nq, mk = Nk.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t mq, mk;
   float c_t, c_s;   // scale * log2(e): logits enter exp2 in these units
   float ratio;      // scale_s / scale_t
   float scale_t;
@@ -36,9 +42,28 @@ struct BwdArgs {
   int64_t sqt[3], skt[3], sqs[3], sks[3];
   int32_t B, H, Nq, Nk;
   int32_t gt, gs;  // query heads per key head (teacher, student)
+  const int32_t* cu_q;  // packed variable-length batch, as in FwdArgs
+  const int32_t* cu_k;
+  int32_t mq, mk;
   float c_t, c_s;            // scale * log2(e)
   float scale_t, scale_s;
 };
+
+// Rows of batch entry b.  Dense: all Nq query and Nk key rows, at batch index b of the strides.
+// Packed: the segment's rows, which start at row q0 / k0 of the packed axis (batch index 0).  The
+// row statistics and gradients of entry b start at ((bs * H + h) * Nq + q0) (keys: with Nk, k0).
+struct Segment {
+  int q0, k0, nq, nk, bs;
+};
+template <class A>
+__device__ __forceinline__ Segment segment_of(const A& a, int b) {
+  if (a.cu_q != nullptr) {
+    const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]), q1 = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]);
+    const int k0 = __builtin_amdgcn_readfirstlane(a.cu_k[b]), k1 = __builtin_amdgcn_readfirstlane(a.cu_k[b + 1]);
+    return Segment{q0, k0, q1 - q0, k1 - k0, 0};
+  }
+  return Segment{0, 0, a.Nq, a.Nk, b};
+}
 
 // dtype: 0 fp32, 1 bf16.  d_t, d_s in {64, 128}.  Return hipErrorInvalidValue for
 // combinations that are not built (the C ABI rejects them before calling).

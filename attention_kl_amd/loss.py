@@ -19,6 +19,10 @@ Directions (the pages fix none, S1):
                teacher-gradient path
   "symmetric"  KL(P_t || P_s) + KL(P_s || P_t)
 
+Packed variable-length batches (inputs [N, heads, d], segments given by cu_seqlens_q /
+cu_seqlens_k) give the per-row KL as [H, N_Q]; "batchmean" then divides by the number of
+sequences.
+
 Gradients with respect to the teacher inputs are computed only when one of them
 requires grad.  The library returns float32 gradients; autograd needs them in
 the dtype of the input, so bf16 inputs receive bf16-rounded gradients (a relative
@@ -37,13 +41,17 @@ REDUCTIONS = ("none", "sum", "mean", "batchmean")
 
 
 class StreamKLFunction(torch.autograd.Function):
-    """Per-row KL(P_t || P_s) with its backward on the library.  Inputs [B, H, N, d]."""
+    """Per-row KL(P_t || P_s) with its backward on the library.  Inputs [B, H, N, d], or [N, H, d]
+    with packed = (cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k) for a packed batch."""
 
     @staticmethod
-    def forward(ctx, qt, kt, qs, ks, causal: bool, scale_t: Optional[float], scale_s: Optional[float]):
-        kl, lse_t, lse_s = S.fwd(qt, kt, qs, ks, causal=causal, scale_t=scale_t, scale_s=scale_s)
+    def forward(ctx, qt, kt, qs, ks, causal: bool, scale_t: Optional[float], scale_s: Optional[float],
+                packed: Optional[tuple] = None):
+        seg = _seg_kwargs(packed)
+        kl, lse_t, lse_s = S.fwd(qt, kt, qs, ks, causal=causal, scale_t=scale_t, scale_s=scale_s, **seg)
         ctx.save_for_backward(qt, kt, qs, ks, kl, lse_t, lse_s)
         ctx.cfg = (bool(causal), scale_t, scale_s)
+        ctx.packed = packed
         return kl
 
     @staticmethod
@@ -53,46 +61,73 @@ class StreamKLFunction(torch.autograd.Function):
         need_t = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
         need_s = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
         if not (need_t or need_s):
-            return (None,) * 7
+            return (None,) * 8
         g = g.to(torch.float32).contiguous()  # the upstream gradient may be a broadcast view
-        dq_s, dk_s, dq_t, dk_t = S.bwd(qt, kt, qs, ks, lse_t, lse_s, g, causal=causal,
-                                       kl=kl if need_t else None, teacher_grads=need_t, student_grads=need_s,
-                                       scale_t=scale_t, scale_s=scale_s)
+        grads = S.bwd(qt, kt, qs, ks, lse_t, lse_s, g, causal=causal, kl=kl if need_t else None,
+                      teacher_grads=need_t, student_grads=need_s, scale_t=scale_t, scale_s=scale_s,
+                      **_seg_kwargs(ctx.packed))
+        if ctx.packed is not None:  # the library's packed layout [heads, N, d] -> the inputs' [N, heads, d]
+            grads = tuple(None if x is None else x.transpose(0, 1) for x in grads)
+        dq_s, dk_s, dq_t, dk_t = grads
 
         def cast(grad, like, needed):
             return grad.to(like.dtype) if (needed and grad is not None) else None
 
         return (cast(dq_t, qt, ctx.needs_input_grad[0]), cast(dk_t, kt, ctx.needs_input_grad[1]),
                 cast(dq_s, qs, ctx.needs_input_grad[2]), cast(dk_s, ks, ctx.needs_input_grad[3]),
-                None, None, None)
+                None, None, None, None)
+
+
+def _seg_kwargs(packed):
+    if packed is None:
+        return {}
+    cu_q, cu_k, mq, mk = packed
+    return dict(cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, max_seqlen_q=mq, max_seqlen_k=mk)
 
 
 def attention_kl(qt, kt, qs, ks, *, causal: bool = False, scale_t: Optional[float] = None,
-                 scale_s: Optional[float] = None, direction: str = "forward", reduction: str = "none"):
+                 scale_s: Optional[float] = None, direction: str = "forward", reduction: str = "none",
+                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[int] = None,
+                 max_seqlen_k: Optional[int] = None):
     """Attention-KL divergence between teacher (qt, kt) and student (qs, ks) attention rows.
 
-    Shapes [B, H, N_Q, d_t], [B, H, N_K, d_t], [B, H, N_Q, d_s], [B, H, N_K, d_s], bf16 or float32,
-    d unit-stride.  Softmax scales default to 1/sqrt(d) per side.
+    Shapes [B, H, N_Q, d_t], [B, Hk_t, N_K, d_t], [B, H, N_Q, d_s], [B, Hk_s, N_K, d_s] (Hk dividing
+    H: grouped key heads), bf16 or float32, d unit-stride.  Softmax scales default to 1/sqrt(d) per
+    side.  Packed variable-length batch: [N_Q, H, d] / [N_K, Hk, d] inputs and int32 device
+    cu_seqlens_q, cu_seqlens_k of B + 1 segment offsets (max_seqlen_* default to the longest
+    segment, read back from the device once).
 
-    reduction: "none" -> per-row float32 [B, H, N_Q]; "sum" -> sum over rows; "mean" -> mean over
-    all B*H*N_Q rows; "batchmean" -> sum divided by B (per-sample divergence summed over heads
-    and rows).
+    reduction: "none" -> per-row float32 [B, H, N_Q] ([H, N_Q] packed); "sum" -> sum over rows;
+    "mean" -> mean over all rows; "batchmean" -> sum divided by B (per-sample divergence summed
+    over heads and rows).
     """
     if direction not in DIRECTIONS:
         raise ValueError(f"direction must be one of {DIRECTIONS}, got {direction!r}")
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {REDUCTIONS}, got {reduction!r}")
+    packed = None
+    n_batch = qt.shape[0]
+    if cu_seqlens_q is not None or cu_seqlens_k is not None:
+        if cu_seqlens_q is None or cu_seqlens_k is None:
+            raise ValueError("a packed batch needs both cu_seqlens_q and cu_seqlens_k")
+
+        def longest(c):
+            return int((c[1:] - c[:-1]).max().item()) if c.numel() > 1 else 0
+        mq = longest(cu_seqlens_q) if max_seqlen_q is None else int(max_seqlen_q)
+        mk = longest(cu_seqlens_k) if max_seqlen_k is None else int(max_seqlen_k)
+        packed = (cu_seqlens_q, cu_seqlens_k, mq, mk)
+        n_batch = cu_seqlens_q.numel() - 1
     if direction == "forward":
-        kl = StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s)
+        kl = StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s, packed)
     elif direction == "reverse":
-        kl = StreamKLFunction.apply(qs, ks, qt, kt, causal, scale_s, scale_t)
+        kl = StreamKLFunction.apply(qs, ks, qt, kt, causal, scale_s, scale_t, packed)
     else:
-        kl = (StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s)
-              + StreamKLFunction.apply(qs, ks, qt, kt, causal, scale_s, scale_t))
+        kl = (StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s, packed)
+              + StreamKLFunction.apply(qs, ks, qt, kt, causal, scale_s, scale_t, packed))
     if reduction == "none":
         return kl
     if reduction == "sum":
         return kl.sum()
     if reduction == "mean":
         return kl.mean()
-    return kl.sum() / kl.shape[0]
+    return kl.sum() / n_batch

@@ -37,7 +37,23 @@ class Problem(ctypes.Structure):
                 ("scale_t", ctypes.c_float), ("scale_s", ctypes.c_float),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("stride_qt", _I64x3), ("stride_kt", _I64x3), ("stride_qs", _I64x3), ("stride_ks", _I64x3),
-                ("Hk_t", ctypes.c_int64), ("Hk_s", ctypes.c_int64)]
+                ("Hk_t", ctypes.c_int64), ("Hk_s", ctypes.c_int64),
+                ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("max_seqlen_q", ctypes.c_int64), ("max_seqlen_k", ctypes.c_int64)]
+
+    @property
+    def packed(self) -> bool:
+        return bool(self.cu_seqlens_q)
+
+    def stat_shape(self):
+        """Shape of kl, lse_t, lse_s and g: [B, H, Nq], or [H, Nq] for a packed batch."""
+        return (self.H, self.Nq) if self.packed else (self.B, self.H, self.Nq)
+
+    def dq_shape(self, d: int):
+        return (self.H, self.Nq, d) if self.packed else (self.B, self.H, self.Nq, d)
+
+    def dk_shape(self, hk: int, d: int):
+        return (hk, self.Nk, d) if self.packed else (self.B, hk, self.Nk, d)
 
 
 _lib = None
@@ -94,12 +110,32 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
-                 scale_s: Optional[float] = None) -> Problem:
+                 scale_s: Optional[float] = None, cu_seqlens_q=None, cu_seqlens_k=None,
+                 max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None) -> Problem:
     """Describe q [B, H, Nq, d] and k [B, Hk, Nk, d] tensors (d unit-stride) as a streamkl_problem_t.
 
     Each side's key-head count Hk (k.shape[1]) must divide H: query head h reads key head
-    h // (H // Hk) of that side (grouped-query attention; Hk == H is one key head per query head)."""
+    h // (H // Hk) of that side (grouped-query attention; Hk == H is one key head per query head).
+
+    Packed variable-length batch: pass cu_seqlens_q and cu_seqlens_k (int32 device tensors of
+    length B + 1, the segments' row offsets) and q [Nq, H, d], k [Nk, Hk, d] holding every
+    segment's rows one after another.  max_seqlen_q / max_seqlen_k default to the longest segment
+    (read back from the device: a synchronisation)."""
     import torch
+    packed = cu_seqlens_q is not None or cu_seqlens_k is not None
+    if packed:
+        if cu_seqlens_q is None or cu_seqlens_k is None:
+            raise ValueError("a packed batch needs both cu_seqlens_q and cu_seqlens_k")
+        for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+            if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous() or c.device != qt.device:
+                raise ValueError(f"{name} must be a contiguous int32 vector on the inputs' device")
+        if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 >= 1 entries")
+        for name, t in (("q_t", qt), ("k_t", kt), ("q_s", qs), ("k_s", ks)):
+            if t.dim() != 3:
+                raise ValueError(f"{name} of a packed batch must be [N, heads, d], got {tuple(t.shape)}")
+        # the packed axis is the n axis of a one-entry batch
+        qt, kt, qs, ks = (t.permute(1, 0, 2).unsqueeze(0) for t in (qt, kt, qs, ks))
     for name, t in (("q_t", qt), ("k_t", kt), ("q_s", qs), ("k_s", ks)):
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, d], got {tuple(t.shape)}")
@@ -128,16 +164,31 @@ def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
     p.dtype = dt
     for f, t in (("stride_qt", qt), ("stride_kt", kt), ("stride_qs", qs), ("stride_ks", ks)):
         getattr(p, f)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    if packed:
+        p.B = cu_seqlens_q.numel() - 1
+        p.cu_seqlens_q, p.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+
+        def longest(c):
+            return int((c[1:] - c[:-1]).max().item()) if c.numel() > 1 else 0
+        p.max_seqlen_q = longest(cu_seqlens_q) if max_seqlen_q is None else int(max_seqlen_q)
+        p.max_seqlen_k = longest(cu_seqlens_k) if max_seqlen_k is None else int(max_seqlen_k)
     return p
 
 
-def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None
+_PACKED_DOC = """Packed variable-length batch: cu_seqlens_q, cu_seqlens_k (and optionally max_seqlen_q,
+    max_seqlen_k) as in make_problem; outputs then take the C ABI's packed layout: statistics
+    [H, Nq], dQ [H, Nq, d], dK [Hk, Nk, d]."""
+
+
+def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
+        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None
         ) -> Tuple["torch.Tensor", "torch.Tensor", "torch.Tensor"]:
     """Per-row KL(P_t || P_s), LSE_t, LSE_s as float32 [B, H, Nq] (streamkl_fwd)."""
     import torch
-    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k)
     if out is None:
-        out = tuple(torch.empty((p.B, p.H, p.Nq), dtype=torch.float32, device=qt.device) for _ in range(3))
+        out = tuple(torch.empty(p.stat_shape(), dtype=torch.float32, device=qt.device) for _ in range(3))
     kl, lse_t, lse_s = out
     _check(lib().streamkl_fwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(kl), _ptr(lse_t),
                               _ptr(lse_s), _stream(stream)), "streamkl_fwd")
@@ -145,20 +196,22 @@ def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, s
 
 
 def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads: bool = False,
-        student_grads: bool = True, scale_t=None, scale_s=None, out=None, stream=None):
+        student_grads: bool = True, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
+        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
     """Gradients of sum_i g_i KL_i (streamkl_bwd): (dq_s, dk_s, dq_t, dk_t), the pairs not asked for
     returned as None (student pair by default, teacher pair with teacher_grads=True)."""
     import torch
-    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k)
     dev = qt.device
     if out is None:
         out = [None, None, None, None]
         if student_grads:
-            out[0] = torch.empty((p.B, p.H, p.Nq, p.d_s), dtype=torch.float32, device=dev)
-            out[1] = torch.empty((p.B, p.Hk_s, p.Nk, p.d_s), dtype=torch.float32, device=dev)
+            out[0] = torch.empty(p.dq_shape(p.d_s), dtype=torch.float32, device=dev)
+            out[1] = torch.empty(p.dk_shape(p.Hk_s, p.d_s), dtype=torch.float32, device=dev)
         if teacher_grads:
-            out[2] = torch.empty((p.B, p.H, p.Nq, p.d_t), dtype=torch.float32, device=dev)
-            out[3] = torch.empty((p.B, p.Hk_t, p.Nk, p.d_t), dtype=torch.float32, device=dev)
+            out[2] = torch.empty(p.dq_shape(p.d_t), dtype=torch.float32, device=dev)
+            out[3] = torch.empty(p.dk_shape(p.Hk_t, p.d_t), dtype=torch.float32, device=dev)
     out = list(out) + [None] * (4 - len(out))
     dq_s, dk_s = (out[0], out[1]) if student_grads else (None, None)
     dq_t, dk_t = (out[2], out[3]) if teacher_grads else (None, None)
@@ -168,23 +221,31 @@ def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads
     return dq_s, dk_s, dq_t, dk_t
 
 
-def bwd_dq(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None):
+def bwd_dq(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None,
+           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
     """Student dQ only: the query-owner half of the backward (streamkl_bwd_dq)."""
     import torch
-    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k)
     if out is None:
-        out = torch.empty((p.B, p.H, p.Nq, p.d_s), dtype=torch.float32, device=qt.device)
+        out = torch.empty(p.dq_shape(p.d_s), dtype=torch.float32, device=qt.device)
     _check(lib().streamkl_bwd_dq(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
                                  _ptr(g), _ptr(out), _stream(stream)), "streamkl_bwd_dq")
     return out
 
 
-def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None):
+def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None,
+           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
     """Student dK only: the key-owner half of the backward (streamkl_bwd_dk)."""
     import torch
-    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s)
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k)
     if out is None:
-        out = torch.empty((p.B, p.Hk_s, p.Nk, p.d_s), dtype=torch.float32, device=qt.device)
+        out = torch.empty(p.dk_shape(p.Hk_s, p.d_s), dtype=torch.float32, device=qt.device)
     _check(lib().streamkl_bwd_dk(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
                                  _ptr(g), _ptr(out), _stream(stream)), "streamkl_bwd_dk")
     return out
+
+
+for _f in (fwd, bwd, bwd_dq, bwd_dk):
+    _f.__doc__ += "\n\n    " + _PACKED_DOC

@@ -97,6 +97,18 @@ def custom(B, H, Nq, Nk, d_t, d_s, causal, dtype="bf16", recipe="noise", sigma=0
                     B, H, Nq, Nk, d_t, d_s, causal, dtype, recipe, sigma, peak_frac, peak_scale, seed)
 
 
+def length_mix(total: int, seed: int, lo: int = 256, hi: int = 8192) -> list:
+    """Segment lengths of a packed batch: log-uniform in [lo, hi], drawn until they fill `total` rows
+    (the last one cut to fit).  Seeded: PCG64(SeedSequence([seed, 6]))."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 6])))
+    out, left = [], total
+    while left > 0:
+        n = int(round(math.exp(g.uniform(math.log(lo), math.log(hi)))))
+        out.append(min(n, left))
+        left -= out[-1]
+    return out
+
+
 def _rng(seed: int, tid: int, b: int, h: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, b, h])))
 

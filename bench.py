@@ -36,7 +36,7 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_flops(w, kernel: str) -> float:
+def kernel_flops(w, kernel: str, pairs=None) -> float:
     """Algorithmic MFMA flops of one launch.
 
     fwd:    both logit products, 2 (d_t + d_s) per allowed pair.
@@ -44,7 +44,7 @@ def kernel_flops(w, kernel: str) -> float:
             2 (d_t + 2 d_s) per pair.   bwd_dk: the same with dK_s.
     The hi/lo split of dS and masked-tile work are not counted.
     """
-    pairs = w.pairs_per_head() * w.B * w.H
+    pairs = w.pairs_per_head() * w.B * w.H if pairs is None else pairs
     if kernel == "fwd":
         return 2.0 * pairs * (w.d_t + w.d_s)
     return 2.0 * pairs * (w.d_t + 2 * w.d_s)
@@ -161,7 +161,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int = 
     return ent
 
 
-def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3):
+def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3, seg=None):
     """The same step (forward, student dQ and dK) through torch autograd: sum_i g_i KL_i .backward().
 
     Beyond the raw kernels it pays for autograd bookkeeping, output allocation and the cast of
@@ -174,7 +174,7 @@ def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3):
 
     def run():
         qs_.grad = ks_.grad = None
-        kl = attention_kl(qt, kt, qs_, ks_, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+        kl = attention_kl(qt, kt, qs_, ks_, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s, **(seg or {}))
         (kl * g).sum().backward()
 
     run()
@@ -209,6 +209,9 @@ def main():
     ap.add_argument("--student-key-heads", type=int, default=None,
                     help="grouped student keys: K key heads shared by the H query heads (K divides H); key head j "
                          "is the workload's head j*H/K.  Default: one key head per query head")
+    ap.add_argument("--packed-mix", type=int, default=None, metavar="SEED",
+                    help="packed variable-length batch: the workload's rows cut into segments of a seeded "
+                         "log-uniform length mix (256..8192 rows), each its own (causal) problem")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -240,12 +243,26 @@ def main():
         print(f"bench.py: --student-key-heads must divide H = {H}", file=sys.stderr)
         sys.exit(2)
     ks = ks[:, ::H // hk_s]
-    kl = torch.empty((B, H, w.Nq), dtype=torch.float32, device=dev)
+    seg = {}
+    pairs = None  # allowed pairs of the whole step (None: the workload's own)
+    if args.packed_mix is not None:
+        if B != 1 or hk_s != H:
+            print("bench.py: --packed-mix needs a one-entry workload and no key grouping", file=sys.stderr)
+            sys.exit(2)
+        lens = wl.length_mix(w.Nq, args.packed_mix)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        seg = dict(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=max(lens), max_seqlen_k=max(lens))
+        qt, kt, qs, ks = (x[0].permute(1, 0, 2) for x in (qt, kt, qs, ks))  # [N, H, d] views, same memory
+        g = g[0]
+        per_seg = [(n * (n + 1) // 2) if w.causal else n * n for n in lens]
+        pairs = sum(per_seg) * H
+    lead = () if seg else (B,)  # a packed batch takes the one-entry layout [H, N...]
+    kl = torch.empty(lead + (H, w.Nq), dtype=torch.float32, device=dev)
     lt = torch.empty_like(kl)
     ls = torch.empty_like(kl)
-    dq = torch.empty((B, H, w.Nq, w.d_s), dtype=torch.float32, device=dev)
-    dk = torch.empty((B, hk_s, w.Nk, w.d_s), dtype=torch.float32, device=dev)
-    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    dq = torch.empty(lead + (H, w.Nq, w.d_s), dtype=torch.float32, device=dev)
+    dk = torch.empty(lead + (hk_s, w.Nk, w.d_s), dtype=torch.float32, device=dev)
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s, **seg)
 
     def step(ev=None):
         if ev is not None:
@@ -287,38 +304,41 @@ def main():
     kern = {}
     for k, v in per.items():
         ms = float(np.mean(v))
-        fl = kernel_flops(w, k)
+        fl = kernel_flops(w, k, pairs)
         kern[k] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
                    "frac_of_bf16_peak": round(fl / ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4)}
-    fwd_fl, bwd_fl = w.fwd_flops(), w.bwd_flops()
+    P = pairs if pairs is not None else w.pairs_per_head() * B * H
+    # algorithmic work of the step: the two logit products once, then dQ_s and dK_s
+    fwd_fl, bwd_fl = 2.0 * P * (w.d_t + w.d_s), 2.0 * P * (w.d_t + 3 * w.d_s)
     fwd_ms = kern["fwd"]["ms"]
     bwd_ms = kern["bwd_dk"]["ms"] + kern["bwd_dq"]["ms"]
     dominant = max(kern, key=lambda k: kern[k]["ms"])
-    dom_fl = kernel_flops(w, dominant)
+    dom_fl = kernel_flops(w, dominant, pairs)
     achieved = dom_fl / kern[dominant]["ms"] / 1e9
     roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": MI355X_PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(dominant, w.name) if hk_s == H else None}
+            "traffic": load_traffic(dominant, w.name) if (hk_s == H and not seg) else None}
     value = (fwd_fl + bwd_fl) / step_ms / 1e9
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded N(0,1) bf16 inputs of the workload's shape)",
-        "config": {"workload": w.name if hk_s == H else f"{w.name}-hks{hk_s}", "B": B, "H": H, "N_Q": w.Nq,
+        "config": {"workload": w.name + (f"-hks{hk_s}" if hk_s != H else "") + (
+                       f"-packed{len(seg and lens)}seg" if seg else ""), "B": B, "H": H, "N_Q": w.Nq,
                    "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s, "causal": w.causal, "teacher_grads": False,
                    "student_key_heads": hk_s},
         "fwd_ms": fwd_ms, "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_fl / fwd_ms / 1e9, 2), "bwd_tflops": round(bwd_fl / bwd_ms / 1e9, 2),
         "fwd_frac_of_bf16_peak": round(fwd_fl / fwd_ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4),
         "extra_hbm_bytes": 12 * B * H * w.Nq, "library_alloc_bytes": int(extra_alloc),
-        "materialised_bytes_avoided": 2 * 4 * w.pairs_per_head() * B * H,
+        "materialised_bytes_avoided": 2 * 4 * P,
         "kernels": kern, "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
     if not args.no_autograd:
-        out["autograd"] = autograd_step(w, qt, kt, qs, ks, g, step_ms)
-    if not args.no_cpu_baseline:
+        out["autograd"] = autograd_step(w, qt, kt, qs, ks, g, step_ms, seg=seg)
+    if not args.no_cpu_baseline and not seg:  # the CPU sample is of the dense workload's rows
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)
 

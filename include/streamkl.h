@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10100 /* 1.1.0: key heads per side (grouped-query attention) */
+#define STREAMKL_VERSION 10200 /* 1.2.0: packed variable-length batches (1.1.0: key heads per side) */
 
 typedef enum {
   STREAMKL_FP32 = 0, /* inputs float32; products on fp32 MFMA                */
@@ -58,9 +58,12 @@ typedef enum {
   STREAMKL_ERR_INVALID = 1,     /* bad argument: NULL pointer, negative size, Nk == 0 with rows to
                                    compute, causal with Nq > Nk, non-positive or non-finite scale,
                                    d stride != 1, a key-head count that does not divide H, only one
-                                   pointer of a gradient pair given, or no gradient asked for      */
+                                   pointer of a gradient pair given, or no gradient asked for; packed
+                                   batch: one cu_seqlens pointer NULL, or a max_seqlen below 0 or
+                                   above the packed row count                                      */
   STREAMKL_ERR_UNSUPPORTED = 2, /* valid but not built: d_t or d_s not in {64, 128}, misaligned base
-                                   pointer or stride (16-byte alignment needed), dtype unknown, or
+                                   pointer or stride (16-byte alignment needed; 4 bytes for the
+                                   cu_seqlens arrays), dtype unknown, or
                                    one (b, h) slice spanning 2 GiB or more ((N + 512) * n-stride
                                    * element size must stay below 2^31 bytes)                     */
   STREAMKL_ERR_LAUNCH = 3       /* the HIP launch itself failed (hipGetLastError after launch)     */
@@ -75,7 +78,20 @@ typedef enum {
  * statistics and gradients are dense and contiguous: kl, lse_t, lse_s, g are
  * float32 [B, H, Nq]; dq_s [B, H, Nq, d_s], dk_s [B, Hk_s, Nk, d_s], dq_t
  * [B, H, Nq, d_t], dk_t [B, Hk_t, Nk, d_t], all float32; a key head's gradient
- * sums over the query heads that read it.                                        */
+ * sums over the query heads that read it.
+ *
+ * Packed variable-length batch (cu_seqlens_q, cu_seqlens_k non-NULL).  The inputs
+ * hold Nq query rows and Nk key rows along their n axis (the b stride is unused),
+ * cut into B segments: segment b is query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1, and is its own problem (its
+ * keys only, causal alignment within it).  Both arrays are DEVICE int32 [B + 1],
+ * non-decreasing, from >= 0 up to <= Nq (resp. Nk); max_seqlen_q / max_seqlen_k must
+ * be >= every segment's length (they size the grid).  The kernels read the arrays as
+ * given and do not check them: values outside these rules are undefined behaviour.
+ * A segment with queries needs keys (and, causal, at least as many keys as
+ * queries); otherwise its rows' outputs are unspecified (no other row is
+ * affected).  Statistics and gradients take the layout of a one-entry batch:
+ * kl, lse_t, lse_s, g float32 [H, Nq]; dq [H, Nq, d]; dk [Hk, Nk, d].              */
 typedef struct {
   int64_t B, H, Nq, Nk;   /* B, H, Nq >= 0 (any zero = nothing to do, returns OK); Nk >= 1 when
                              there are rows; causal needs Nq <= Nk                              */
@@ -85,6 +101,9 @@ typedef struct {
   int32_t dtype;          /* streamkl_dtype_t                                                    */
   int64_t stride_qt[3], stride_kt[3], stride_qs[3], stride_ks[3]; /* (b, h, n) strides, elements */
   int64_t Hk_t, Hk_s;     /* key heads of teacher and student: each divides H; 0 means H          */
+  const int32_t* cu_seqlens_q; /* packed batch: segment row offsets, DEVICE int32 [B + 1]; NULL =  */
+  const int32_t* cu_seqlens_k; /* dense batch.  Both NULL or both non-NULL.                        */
+  int64_t max_seqlen_q, max_seqlen_k; /* packed batch: longest segment (ignored when dense)         */
 } streamkl_problem_t;
 
 /* Forward (S4): KL_i, LSE_t,i, LSE_s,i for every row, float32 [B, H, Nq] each.

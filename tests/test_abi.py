@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared) <= exported
-    assert S.version() == 10100
+    assert S.version() == 10200
 
 
 def test_status_strings():
@@ -164,3 +164,37 @@ def test_product_path_has_no_fallback():
     src = open(os.path.join(ROOT, "attention_kl_amd", "streamkl.py")).read()
     assert "oracle" not in src.replace("no fallback", "")
     assert "numpy" not in src
+
+
+def test_packed_batch_argument_rules():
+    # packed problem: 3 segments over 300 packed rows; fake device addresses for the offsets
+    cu_q, cu_k = A + 0x8000, A + 0x9000
+    ok = dict(B=3, Nq=300, Nk=300, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, max_seqlen_q=128, max_seqlen_k=128)
+    bad_ptr = [A + 2, A, A, A]  # checked after the problem: UNSUPPORTED means the problem passed
+    assert fwd_status(_problem(**ok), ptrs=bad_ptr) == S.ERR_UNSUPPORTED
+    # causal with more packed query rows than key rows is a per-segment matter, not rejected here
+    assert fwd_status(_problem(**{**ok, "Nq": 400, "max_seqlen_q": 200}), ptrs=bad_ptr) == S.ERR_UNSUPPORTED
+    for kw in (dict(cu_seqlens_k=None), dict(cu_seqlens_q=None), dict(max_seqlen_q=301), dict(max_seqlen_k=-1)):
+        assert fwd_status(_problem(**{**ok, **kw}), ptrs=bad_ptr) == S.ERR_INVALID, kw
+    assert fwd_status(_problem(**{**ok, "cu_seqlens_q": cu_q + 2}), ptrs=bad_ptr) == S.ERR_UNSUPPORTED
+    # nothing to do: no rows in any segment
+    assert fwd_status(_problem(**{**ok, "max_seqlen_q": 0}), ptrs=[0] * 4, outs=[0] * 3) == S.OK
+
+
+def test_python_binding_describes_a_packed_batch():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(300, 4, 64)    # [N, H, d]
+    k = torch.zeros(350, 2, 64)    # [N, Hk, d]
+    cu_q = torch.tensor([0, 100, 100, 300], dtype=torch.int32)
+    cu_k = torch.tensor([0, 150, 170, 350], dtype=torch.int32)
+    p = S.make_problem(q, k, q, k, True, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+    assert (p.B, p.H, p.Nq, p.Nk, p.Hk_t) == (3, 4, 300, 350, 2)
+    assert (p.max_seqlen_q, p.max_seqlen_k) == (200, 180)
+    assert list(p.stride_qt)[1:] == [64, 4 * 64]  # head and row strides of [N, H, d] (the b stride is unused)
+    assert p.packed and p.stat_shape() == (4, 300) and p.dk_shape(2, 64) == (2, 350, 64)
+    with pytest.raises(ValueError):  # both offset vectors or neither
+        S.make_problem(q, k, q, k, True, cu_seqlens_q=cu_q)
+    with pytest.raises(ValueError):  # int32 offsets only
+        S.make_problem(q, k, q, k, True, cu_seqlens_q=cu_q.long(), cu_seqlens_k=cu_k)
+    with pytest.raises(ValueError):  # packed inputs are [N, heads, d]
+        S.make_problem(q[None], k[None], q[None], k[None], True, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
