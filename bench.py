@@ -14,6 +14,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -107,10 +108,13 @@ def _kernel_class(name: str):
     if "fwd_kernel" in name:
         return "fwd"
     if "bwd_kernel" in name:
-        # last template argument: owner is the query side (dQ) or the key side (dK)
-        if name.rstrip().endswith("true>(skl::BwdArgs)") or "Lb1EEEvNS_7BwdArgsE" in name:
-            return "bwd_dq"
-        return "bwd_dk"
+        # template arguments <T, DT, DS, CAUSAL, TEACHER, OWN_Q, GRP>: OWN_Q picks the query owner (dQ)
+        m = re.search(r"bwd_kernel<([^>]*)>", name)
+        if m:
+            own_q = m.group(1).split(",")[5].strip() in ("true", "1")
+        else:  # mangled: the four bool arguments are Lb0E / Lb1E
+            own_q = re.findall(r"Lb([01])E", name)[2] == "1"
+        return "bwd_dq" if own_q else "bwd_dk"
     if "copy" in name.lower():
         return "copy"
     return None

@@ -48,3 +48,21 @@ def test_config_flops():
     assert wl.CONFIGS[4].pairs_per_head() == 8192 * 8192
     g = wl.head_g(c3, 0, 5)
     assert g.shape == (32768,) and g.min() >= 0.5 and g.max() <= 1.5
+
+
+def test_bench_kernel_classes_follow_the_owner_argument():
+    """Profiler rows are attributed by the OWN_Q template argument, in demangled and mangled names."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    k = bench._kernel_class
+    assert k("void skl::fwd_kernel<__bf16, 128, 128, true>(skl::FwdArgs)") == "fwd"
+    assert k("void skl::bwd_kernel<__bf16, 128, 128, true, false, true, false>(skl::BwdArgs)") == "bwd_dq"
+    assert k("void skl::bwd_kernel<__bf16, 128, 128, true, false, false, false>(skl::BwdArgs)") == "bwd_dk"
+    assert k("void skl::bwd_kernel<__bf16, 128, 128, true, true, false, true>(skl::BwdArgs)") == "bwd_dk"
+    assert k("_ZN3skl10bwd_kernelIDF16bLi128ELi128ELb1ELb0ELb1ELb0EEEvNS_7BwdArgsE") == "bwd_dq"
+    assert k("_ZN3skl10bwd_kernelIDF16bLi128ELi128ELb1ELb0ELb0ELb1EEEvNS_7BwdArgsE") == "bwd_dk"
+    assert k("void at::native::copy_kernel") == "copy" and k("other") is None
