@@ -195,6 +195,7 @@ bwd_kernel(const BwdArgs a) {
   // wave of group 1 per statistic converts them a phase before use), per wave otherwise
   constexpr bool CSLOT = !OWN_Q && NG == 2;
   __shared__ __attribute__((aligned(16))) float cst[CSLOT ? NBUF : 1][4][32];
+  __shared__ int cst_neg[CSLOT ? NBUF : 1];  // per slot: some streamed query of the tile has g < 0
   __shared__ __attribute__((aligned(16))) float wst[(!OWN_Q && NG == 1) ? NW : 1][4][32];
 
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
@@ -340,31 +341,41 @@ bwd_kernel(const BwdArgs a) {
   f32x16 st = {}, ss = {};
   DsTile<T> dsr;  // dS of the last tile through the vector phase, for the gradient product
 
-  // Ping-pong, key owner: wave 4 + k of group 1 converts statistic k of the tile in slot u, in two
-  // halves around its vector phase: the LDS reads go out first and the converted value is stored
-  // at the end, so their latency hides behind the dS work instead of delaying this wave's barrier.
+  // Key owner: statistics of the streamed query rows, converted per tile to the units the vector
+  // phase uses.  The row weight g enters the exponents: g P = sgn(g) exp2(x - (LSE log2 e - log2|g|)),
+  // so dS needs no per-element product with g; only a tile holding a negative weight multiplies by
+  // the sign afterwards (g = 0 gives an exponent of -inf and a zero term).
+  //   0: LSE_t log2 e - log2|g|   1: LSE_s log2 e - log2|g|   2: sgn(g)   3: KL + LSE_t - LSE_s
+  constexpr int NSTAT = TEACHER ? 4 : 3;
+  auto convert_one = [&](int k, const float* raw) -> float {
+    const float g = raw[128 + r32];
+    if (k == 0) return raw[r32] * kLog2e - fast_log2(fabsf(g));
+    if (k == 1) return raw[64 + r32] * kLog2e - fast_log2(fabsf(g));
+    if (k == 2) return g;  // its sign is taken when stored
+    return raw[192 + r32] + raw[r32] - raw[64 + r32];
+  };
+  // Ping-pong: wave 4 + k of group 1 converts statistic k of the tile in slot u, in two halves around
+  // its vector phase: the LDS reads go out first and the converted value is stored at the end, so
+  // their latency hides behind the dS work instead of delaying this wave's barrier.  Both halves of
+  // the wave hold the same 32 rows and store the same values.
   auto stats_load = [&](const char* sl) -> float {
     float v = 0.f;
     if constexpr (CSLOT) {
       const int k = wave - 4;
-      if (k < (TEACHER ? 4 : 3) && hf == 0) {
-        const float* raw = reinterpret_cast<const float*>(sl + TILE);
-        if (k == 0)
-          v = raw[r32] * kLog2e;
-        else if (k == 1)
-          v = raw[64 + r32] * kLog2e;
-        else if (k == 2)
-          v = raw[128 + r32];
-        else
-          v = raw[192 + r32] + raw[r32] - raw[64 + r32];
-      }
+      if (k < NSTAT) v = convert_one(k, reinterpret_cast<const float*>(sl + TILE));
     }
     return v;
   };
   auto stats_store = [&](int u, float v) {
     if constexpr (CSLOT) {
       const int k = wave - 4;
-      if (k < (TEACHER ? 4 : 3) && hf == 0) cst[u][k][r32] = v;
+      if (k < NSTAT) {
+        cst[u][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
+        if (k == 2) {
+          const bool neg = __builtin_amdgcn_ballot_w64(v < 0.f) != 0;
+          if (lane == 0) cst_neg[u] = neg;
+        }
+      }
     }
   };
   auto convert_stats = [&](int u, const char* sl) { stats_store(u, stats_load(sl)); };
@@ -374,32 +385,33 @@ bwd_kernel(const BwdArgs a) {
     bool skip, full;
     tile_state(s, skip, full);
     if (NG == 1 && skip) return;  // ping-pong: a skipped tile goes through the masked path (all zero)
-    if constexpr (!OWN_Q && !CSLOT) {  // statistics of the 32 streamed queries, converted once per wave
-      if (hf == 0) {
-        const float* raw = reinterpret_cast<const float*>(sl + TILE);
-        const float lt = raw[r32], ls = raw[64 + r32];
-        wst[wave][0][r32] = lt * kLog2e;
-        wst[wave][1][r32] = ls * kLog2e;
-        wst[wave][2][r32] = raw[128 + r32];
-        if constexpr (TEACHER) wst[wave][3][r32] = raw[192 + r32] + lt - ls;
+    bool neg = false;  // some row weight of the tile is negative
+    if constexpr (!OWN_Q && !CSLOT) {  // statistics of the 32 streamed queries, converted by each wave
+      const float* raw = reinterpret_cast<const float*>(sl + TILE);
+#pragma unroll
+      for (int k = 0; k < NSTAT; ++k) {
+        const float v = convert_one(k, raw);
+        wst[wave][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
       }
+      neg = __builtin_amdgcn_ballot_w64(raw[128 + r32] < 0.f) != 0;
     }
+    if constexpr (CSLOT) neg = __builtin_amdgcn_readfirstlane(cst_neg[u]) != 0;
     const int sb = (t_begin + s) * BS;
     float ds[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      f32x4 lt4, ls4, gg4, cc4;
+      // The row weight is not applied here: the query owner scales each output row by it at the
+      // store, the key owner has it folded into the statistics (sign below).
+      f32x4 lt4, ls4, cc4;
       if constexpr (OWN_Q) {
         lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
         ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
-        gg4 = f32x4{1.f, 1.f, 1.f, 1.f};  // the row weight g is constant along the stream: applied at the store
         cc4 = f32x4{own_c, own_c, own_c, own_c};
       } else {
         const int ql = 8 * g4 + 4 * hf;
         const float(*cs)[32] = CSLOT ? cst[u] : wst[CSLOT ? 0 : wave];
         lt4 = *reinterpret_cast<const f32x4*>(&cs[0][ql]);
         ls4 = *reinterpret_cast<const f32x4*>(&cs[1][ql]);
-        gg4 = *reinterpret_cast<const f32x4*>(&cs[2][ql]);
         cc4 = TEACHER ? *reinterpret_cast<const f32x4*>(&cs[3][ql]) : f32x4{};
       }
 #pragma unroll
@@ -408,12 +420,22 @@ bwd_kernel(const BwdArgs a) {
         const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
         float v;
         if constexpr (TEACHER) {
-          v = gg4[e] * pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
+          v = pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
         } else {
           const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
-          v = gg4[e] * (ps - pt);
+          v = ps - pt;
         }
         ds[i] = v;
+      }
+    }
+    if (neg) {  // key owner, a tile with a negative row weight: dS takes the sign of g
+      asm volatile("");  // keep this a branch: taken only for such tiles
+      const float(*cs)[32] = CSLOT ? cst[u] : wst[CSLOT ? 0 : wave];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 sg4 = *reinterpret_cast<const f32x4*>(&cs[2][8 * g4 + 4 * hf]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[4 * g4 + e] *= sg4[e];
       }
     }
     if (!full) {

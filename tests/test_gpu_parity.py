@@ -214,3 +214,35 @@ def test_config5_full_size_sampled():
     w = wl.CONFIGS[5]
     n = w.Nq
     _sampled(w, [(0, 0), (0, 5)], _rows(n, 5), [n - 1, n - 2, n - 33, n - 100])
+
+
+@pytest.mark.parametrize("w", [wl.custom(1, 2, 300, 300, 128, 128, True, recipe="independent", seed=41),
+                               wl.custom(2, 1, 129, 200, 128, 64, False, recipe="independent", seed=42),
+                               wl.custom(1, 2, 100, 100, 64, 64, True, dtype="fp32", recipe="independent", seed=43)],
+                         ids=lambda w: w.name)
+def test_signed_and_zero_row_weights(w):
+    """g of either sign, with exact zeros: the key owner folds |g| into its statistics and applies the
+    sign per tile, so tiles with and without negative weights both occur here (every 4th row is zero,
+    and a whole 32-row tile of each head has only positive weights)."""
+    print(f"case {w.name} signed g", flush=True)
+    dev_in, host = device_inputs(w)
+    qt, kt, qs, ks = dev_in
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 7])))
+    g = rng.standard_normal((w.B, w.H, w.Nq)).astype(np.float32)
+    g[..., ::4] = 0.0
+    g[..., 32:64] = np.abs(g[..., 32:64]) + 0.1
+    kl, lt, ls = S.fwd(qt, kt, qs, ks, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    grads = S.bwd(qt, kt, qs, ks, lt, ls, torch.from_numpy(g).cuda(), causal=w.causal, kl=kl, teacher_grads=True,
+                  scale_t=w.scale_t, scale_s=w.scale_s)
+    torch.cuda.synchronize()
+    h64 = [a.astype(np.float64) for a in host]
+    rg = oracle.backward(*h64, w.scale_t, w.scale_s, w.causal, g.astype(np.float64), teacher=True)
+    rt = rtol_of(w)
+    ag = np.abs(g)
+    r = {}
+    for name, x, other, sc in (("dq_s", grads[0], h64[3], w.scale_s), ("dk_s", grads[1], h64[2], w.scale_s),
+                               ("dq_t", grads[2], h64[1], w.scale_t), ("dk_t", grads[3], h64[0], w.scale_t)):
+        r[name] = ratio_rows(x.cpu().numpy(), rg[name], rt, grad_floor(sc, ag, other))
+    msg = report(w.name + " signed g", **r)
+    print(msg, flush=True)
+    assert max(r.values()) <= 1.0, msg
