@@ -4,4 +4,4 @@ Imported by the tests, the smoke check and the bench's CPU-baseline leg; never b
 product path, and it shares no code with it.
 """
 from .streamkl_oracle import (allowed_mask, backward, backward_head, forward,  # noqa: F401
-                              forward_head)
+                              forward_head, js_backward, js_backward_head, js_forward, js_forward_head)

@@ -182,3 +182,90 @@ def backward(qt, kt, qs, ks, scale_t, scale_s, causal, g, teacher: bool = False,
             for k, v in o.items():
                 res[k][b, h] = v
     return res
+
+
+# ------------------------------------------------------------------------------------------------
+# Jensen-Shannon divergence between the same two attention rows.  The pages name only KL (S1); the
+# JS variant is the symmetric, bounded relative commonly used in distillation, defined here as
+#
+#   M = (P_t + P_s) / 2,   JS_i = 1/2 KL(P_t || M)_i + 1/2 KL(P_s || M)_i      (natural log, <= ln 2)
+#
+# and, with per-row weights g_i, the gradient of sum_i g_i JS_i with respect to the logits (the
+# softmax chain rule applied to d JS / d P = 1/2 log(P / M) on each side):
+#
+#   dS_t = g_i 1/2 P_t (log(P_t / M) - KL(P_t || M)_i)     dQ_t = s_t dS_t K_t,  dK_t = s_t dS_t^T Q_t
+#   dS_s = g_i 1/2 P_s (log(P_s / M) - KL(P_s || M)_i)     dQ_s = s_s dS_s K_s,  dK_s = s_s dS_s^T Q_s
+
+def _js_terms(la, lb, mask):
+    """log(P_t/M), log(P_s/M) over the allowed entries (0 where masked) and P_t, P_s."""
+    lm = np.logaddexp(np.where(mask, la, 0.0), np.where(mask, lb, 0.0)) - np.log(2.0)
+    pt = np.where(mask, np.exp(la), 0.0)
+    ps = np.where(mask, np.exp(lb), 0.0)
+    return np.where(mask, la - lm, 0.0), np.where(mask, lb - lm, 0.0), pt, ps
+
+
+def js_forward_head(qt, kt, qs, ks, scale_t, scale_s, causal, block: int = ROW_BLOCK):
+    """Per-row JS, KL(P_t || M), KL(P_s || M), LSE_t, LSE_s (float64) of one head."""
+    qt, kt, qs, ks = (np.asarray(x, np.float64) for x in (qt, kt, qs, ks))
+    nq, _ = _check(qt, kt, qs, ks, causal)
+    out = [np.empty(nq) for _ in range(5)]
+    for r in _row_blocks(np.arange(nq), block):
+        _, _, mask, la, lb, lse_t, lse_s, _ = _block_terms(qt, kt, qs, ks, float(scale_t), float(scale_s), causal, r)
+        lrt, lrs, pt, ps = _js_terms(la, lb, mask)
+        kt_m = (pt * lrt).sum(axis=1)
+        ks_m = (ps * lrs).sum(axis=1)
+        for o, v in zip(out, (0.5 * (kt_m + ks_m), kt_m, ks_m, lse_t, lse_s)):
+            o[r] = v
+    return tuple(out)
+
+
+def js_backward_head(qt, kt, qs, ks, scale_t, scale_s, causal, g, teacher: bool = False,
+                     block: int = ROW_BLOCK) -> Dict[str, np.ndarray]:
+    """Gradients of sum_i g_i JS_i for one head: dq_s, dk_s (and dq_t, dk_t when `teacher`)."""
+    qt, kt, qs, ks = (np.asarray(x, np.float64) for x in (qt, kt, qs, ks))
+    g = np.asarray(g, np.float64)
+    nq, nk = _check(qt, kt, qs, ks, causal)
+    s_t, s_s = float(scale_t), float(scale_s)
+    out = {"dq_s": np.zeros((nq, qs.shape[1])), "dk_s": np.zeros((nk, ks.shape[1]))}
+    if teacher:
+        out["dq_t"] = np.zeros((nq, qt.shape[1]))
+        out["dk_t"] = np.zeros((nk, kt.shape[1]))
+    for r in _row_blocks(np.arange(nq), block):
+        _, _, mask, la, lb, _, _, kmax = _block_terms(qt, kt, qs, ks, s_t, s_s, causal, r)
+        lrt, lrs, pt, ps = _js_terms(la, lb, mask)
+        gr = g[r][:, None]
+        ds_s = gr * 0.5 * ps * (lrs - (ps * lrs).sum(axis=1, keepdims=True))
+        out["dq_s"][r] = s_s * (ds_s @ ks[:kmax])
+        out["dk_s"][:kmax] += s_s * (ds_s.T @ qs[r])
+        if teacher:
+            ds_t = gr * 0.5 * pt * (lrt - (pt * lrt).sum(axis=1, keepdims=True))
+            out["dq_t"][r] = s_t * (ds_t @ kt[:kmax])
+            out["dk_t"][:kmax] += s_t * (ds_t.T @ qt[r])
+    return out
+
+
+def js_forward(qt, kt, qs, ks, scale_t, scale_s, causal, block: int = ROW_BLOCK):
+    """All heads: inputs [B, H, N, d]; returns JS, KL(P_t||M), KL(P_s||M), LSE_t, LSE_s, float64 [B, H, N_Q]."""
+    B, H, nq = qt.shape[:3]
+    res = [np.empty((B, H, nq)) for _ in range(5)]
+    for b in range(B):
+        for h in range(H):
+            for o, v in zip(res, js_forward_head(qt[b, h], kt[b, h], qs[b, h], ks[b, h], scale_t, scale_s, causal,
+                                                 block=block)):
+                o[b, h] = v
+    return tuple(res)
+
+
+def js_backward(qt, kt, qs, ks, scale_t, scale_s, causal, g, teacher: bool = False, block: int = ROW_BLOCK):
+    """All heads: gradients of sum g*JS; returns a dict of float64 [B, H, N, d] arrays."""
+    B, H = qt.shape[:2]
+    res = None
+    for b in range(B):
+        for h in range(H):
+            o = js_backward_head(qt[b, h], kt[b, h], qs[b, h], ks[b, h], scale_t, scale_s, causal, g[b, h],
+                                 teacher=teacher, block=block)
+            if res is None:
+                res = {k: np.empty((B, H) + v.shape) for k, v in o.items()}
+            for k, v in o.items():
+                res[k][b, h] = v
+    return res
