@@ -23,7 +23,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 # MFMA accumulators in VGPRs: the softmax/KL VALU reads them with no v_accvgpr_read copies
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-result"]
-DEVICE_SOURCES = ["skl_fwd.hip", "skl_bwd.hip"]
+DEVICE_SOURCES = ["skl_fwd.hip", "skl_bwd.hip", "skl_js.hip"]
 HOST_SOURCES = ["skl_api.cpp"]
 
 

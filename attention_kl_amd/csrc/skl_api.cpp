@@ -203,6 +203,60 @@ int streamkl_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, 
   return STREAMKL_OK;
 }
 
+int streamkl_js_fwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                    float* js, float* lse_t, float* lse_s, float* js_t, void* hip_stream) {
+  bool empty = false;
+  int st = check_problem(p, &empty);
+  if (st != STREAMKL_OK || empty) return st;
+  if ((st = check_inputs(q_t, k_t, q_s, k_s)) != STREAMKL_OK) return st;
+  if ((st = check_f32(js)) != STREAMKL_OK || (st = check_f32(lse_t)) != STREAMKL_OK ||
+      (st = check_f32(lse_s)) != STREAMKL_OK || (st = check_f32(js_t)) != STREAMKL_OK)
+    return st;
+  skl::FwdArgs a{};
+  fill_common(a, p, q_t, k_t, q_s, k_s);
+  a.kl = js;  // the KL forward's per-row KL lands here first, then the JS pass overwrites it
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  a.js_t = js_t;
+  a.ratio = p->scale_s / p->scale_t;
+  a.scale_t = p->scale_t;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  if ((st = to_status(skl::launch_fwd(a, p->dtype, p->d_t, p->d_s, p->causal != 0, s))) != STREAMKL_OK) return st;
+  return to_status(skl::launch_js_fwd(a, p->dtype, p->d_t, p->d_s, p->causal != 0, s));
+}
+
+int streamkl_js_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                    const float* lse_t, const float* lse_s, const float* js, const float* js_t, const float* g,
+                    float* dq_s, float* dk_s, float* dq_t, float* dk_t, void* hip_stream) {
+  bool empty = false;
+  int st = check_bwd(p, q_t, k_t, q_s, k_s, lse_t, lse_s, g, &empty);
+  if (st != STREAMKL_OK) return st;
+  if ((dq_t == nullptr) != (dk_t == nullptr) || (dq_s == nullptr) != (dk_s == nullptr)) return STREAMKL_ERR_INVALID;
+  if (empty) return STREAMKL_OK;
+  const bool teacher = dq_t != nullptr, student = dq_s != nullptr;
+  if (!teacher && !student) return STREAMKL_ERR_INVALID;  // no gradient asked for
+  if ((st = check_f32(js)) != STREAMKL_OK || (st = check_f32(js_t)) != STREAMKL_OK) return st;
+  if (student && ((st = check_f32(dq_s)) != STREAMKL_OK || (st = check_f32(dk_s)) != STREAMKL_OK)) return st;
+  if (teacher && ((st = check_f32(dq_t)) != STREAMKL_OK || (st = check_f32(dk_t)) != STREAMKL_OK)) return st;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  const bool causal = p->causal != 0;
+  skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, js_t, g);
+  a.js = js;
+  if (student) {
+    a.dq = dq_s;
+    a.dk = dk_s;
+    if ((st = to_status(skl::launch_js_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
+    if ((st = to_status(skl::launch_js_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
+  }
+  if (teacher) {
+    a.dq = dq_t;
+    a.dk = dk_t;
+    if ((st = to_status(skl::launch_js_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, true, s))) != STREAMKL_OK) return st;
+    if ((st = to_status(skl::launch_js_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, true, s))) != STREAMKL_OK) return st;
+  }
+  return STREAMKL_OK;
+}
+
 const char* streamkl_status_string(int status) {
   switch (status) {
     case STREAMKL_OK:

@@ -1,635 +1,14 @@
-// Recompute backward of the attention KL divergence on gfx950.
-//
-// StreamKL abstract (arXiv 2026), S5: the backward recomputes the attention
-// probabilities tile by tile instead of storing any N_Q x N_K intermediate.
-// From the forward's per-row log-sum-exps, each logit tile gives
-//   P_t = exp(a - LSE_t),  P_s = exp(b - LSE_s)
-// and the gradients of L = sum_i g_i KL_i (calculus of the KL definition):
-//   student  dS = g_i (P_s - P_t)
-//   teacher  dS = g_i P_t ((a - b) - (KL_i + LSE_t,i - LSE_s,i))
-//   dQ = scale dS K,   dK = scale dS^T Q     (K, Q of the same side)
-//
-// One kernel template serves both halves.  Each wave owns 32 rows of the output
-// (query rows for dQ, key rows for dK) and keeps their Q or K slices in registers
-// as MFMA B operands; the other side streams through a 4-slot LDS ring filled by
-// buffer->LDS DMA.  Owning the output rows means no atomics and no workspace.
-// Both halves recompute both logit tiles.
-//
-// The logit tile is formed with the owned rows as columns, so each lane holds 16
-// streamed rows of one owned row; that register block is directly the A operand
-// of the gradient product (contraction over the streamed rows).  The B operand,
-// the streamed tile read with the streamed rows as the contraction index, comes
-// from the row-major LDS tile through transpose reads, so no transposed copy is
-// stored.  bf16: dS enters the MFMA as hi + lo bf16 parts (two products), so its
-// rounding contributes about 2^-16 relative instead of bf16's 2^-9.
-//
-// Per streamed tile s a wave runs a matrix phase, M(s) = gradient product of
-// tile s-1 then the two logit products of tile s, and a vector phase, V(s) = the
-// probabilities and dS of tile s.  bf16 workgroups have eight waves in two
-// groups, one wave of each group per SIMD; group 1 starts one phase late and
-// every phase ends at a workgroup barrier, so on every SIMD one wave is in its
-// matrix phase while the other is in its vector phase (ping-pong) and the matrix
-// cores and the vector ALUs work at the same time.
-#include "skl_device.hpp"
-#include "skl_kernels.hpp"
+// Launchers of the KL backward kernels (the kernel template and its dispatch are in skl_bwd_impl.hpp).
+#include "skl_bwd_impl.hpp"
 
 namespace skl {
 
-// a * sa - b * sb with both products rounded before the subtraction (no FMA contraction), so the
-// result is exactly 0 when (a, sa) == (b, sb): identical teacher and student give zero gradients.
-__device__ __forceinline__ float scaled_diff(float a, float sa, float b, float sb) {
-#pragma clang fp contract(off)
-  return a * sa - b * sb;
-}
-
-template <typename T>
-struct BwdTile {
-  static constexpr int NG = sizeof(T) == 2 ? 2 : 1;  // wave groups (two: ping-pong)
-  static constexpr int NW = 4 * NG;                  // waves per workgroup
-  static constexpr int NT = 64 * NW;
-  static constexpr int BW = 32 * NW;  // owned rows per workgroup (32 per wave)
-  static constexpr int BS = 32;       // streamed rows per LDS tile
-  // LDS ring: tile s is read in phases 2s..2s+3 (ping-pong) or in step s (one group), while the
-  // next PD = NBUF - 2 tiles are in flight
-  static constexpr int NBUF = 4;
-  static constexpr int PD = NBUF - 2;
-};
-
-// dS of one 32 x 32 tile in the accumulator layout, kept from a vector phase to the next matrix
-// phase as the gradient product's A operand: bf16 hi + lo chunks, or fp32 values.
-template <typename T>
-struct DsTile;
-template <>
-struct DsTile<__bf16> {
-  u32x4 hi[2], lo[2];
-  __device__ __forceinline__ void set(const float* v) {
-    split_bf16x8(v, hi[0], lo[0]);
-    split_bf16x8(v + 8, hi[1], lo[1]);
-  }
-};
-template <>
-struct DsTile<float> {
-  float v[16];
-  __device__ __forceinline__ void set(const float* x) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = x[i];
-  }
-};
-
-// Per-lane byte offsets, inside a swizzled streamed tile of RB-byte rows, of the transpose-read
-// sources of the gradient product: pass s in {0, 1} covers rows 8s + 4 hf + (lane%16)/4 (plus 16c
-// for chunk c, an immediate), column 32 db + 16 ((lane/16)%2) + 4 (lane%4).
-template <int RB, int DX>
-__device__ __forceinline__ void tr_offsets(int (*off)[DX / 32], int lane) {
-  const int trow = 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // element column inside a 32-wide block
-#pragma unroll
-  for (int sp = 0; sp < 2; ++sp) {
-    const int row = trow + 8 * sp;
-#pragma unroll
-    for (int db = 0; db < DX / 32; ++db) {
-      const int chunk = 4 * db + (tcol >> 3);
-      off[sp][db] = row * RB + ((chunk ^ swz<RB>(row)) << 4) + (tcol & 7) * 2;
-    }
-  }
-}
-
-// Gradient-product B operands of chunk c (streamed rows 16c .. 16c + 15) of the streamed tile X
-// at `xt` (row-major, swizzled): columns 32 db .. 32 db + 31 for each db, through transpose reads.
-template <int DX, int RB>
-__device__ __forceinline__ void grad_operands(u32x4* bop, const char* xt, const int (*toff)[DX / 32], int c) {
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) {
-    const u32x2 p0 = lds_read_tr16(xt + toff[0][db] + 16 * c * RB);
-    const u32x2 p1 = lds_read_tr16(xt + toff[1][db] + 16 * c * RB);
-    bop[db] = u32x4{p0[0], p0[1], p1[0], p1[1]};
-  }
-}
-// out[db] += dS[:, chunk c] . B[db]: hi parts into every accumulator, then lo parts, so no MFMA
-// waits on the one just before it.
-template <int DX>
-__device__ __forceinline__ void grad_mma(f32x16* out, const DsTile<__bf16>& ds, int c, const u32x4* bop) {
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) mma_chunk<__bf16>(out[db], ds.hi[c], bop[db]);
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) mma_chunk<__bf16>(out[db], ds.lo[c], bop[db]);
-}
-
-// out[db] += dS . X[:, 32 db .. 32 db + 31] for one 32-row streamed tile.  dS is in the logit
-// accumulator layout (lane = owned row, element i = streamed row acc_row(i, hf)); X is the
-// streamed tile of the side being differentiated, row-major and swizzled in LDS at `xt`.
-template <typename T, int DX, int RB>
-__device__ __forceinline__ void grad_product(f32x16* out, const DsTile<T>& ds, const char* xt,
-                                             const int (*toff)[DX / 32], int lane) {
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      u32x4 bop[DX / 32];
-      grad_operands<DX, RB>(bop, xt, toff, c);
-      grad_mma<DX>(out, ds, c, bop);
-    }
-  } else {
-    const int hf = lane >> 5, r32 = lane & 31;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = acc_row(i, hf);
-#pragma unroll
-      for (int db = 0; db < DX / 32; ++db) {
-        const int col = 32 * db + r32;  // fp32 element column; 4 per 16-byte chunk
-        const float x = *reinterpret_cast<const float*>(xt + row * RB + ((((col >> 2) ^ swz<RB>(row))) << 4) +
-                                                        (col & 3) * 4);
-        out[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(ds.v[i], x, out[db], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// Wait until at most N of this wave's vector-memory operations are outstanding, N wave-uniform
-// and below 16.
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<15>(); break;
-  }
-}
-
-// OWN_Q: the workgroup owns query rows and writes dQ; otherwise it owns key rows and writes dK.
-// TEACHER: gradients of the teacher side (dQ_t / dK_t) instead of the student side.
-// GRP (key owner only): several query heads read each key head of the gradient's side.  It is a
-// template flag, not just the run-time count, so that the one-head kernel has no pass loop around
-// its tile loop: with one, the compiler schedules the tile loop's LDS reads less far ahead.
-template <typename T, int DT, int DS, bool CAUSAL, bool TEACHER, bool OWN_Q, bool GRP>
-__global__ __launch_bounds__(BwdTile<T>::NT) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2))) void
-bwd_kernel(const BwdArgs a) {
-  using C = BwdTile<T>;
-  constexpr int NG = C::NG, NW = C::NW, NT = C::NT, BW = C::BW, BS = C::BS, NBUF = C::NBUF, PD = C::PD;
-  constexpr int DX = TEACHER ? DT : DS;
-  constexpr int RBT = DT * (int)sizeof(T), RBS = DS * (int)sizeof(T), RBX = TEACHER ? RBT : RBS;
-  constexpr int NCT = RBT / 16, NCS = RBS / 16;
-  constexpr int TILE = BS * (RBT + RBS);
-  constexpr int STAT = OWN_Q ? 0 : 4 * 256;  // raw lse_t, lse_s, g, kl of the streamed queries (64 slots each)
-  constexpr int SLOT = TILE + STAT;
-  using DmaT = DmaTile<BS, RBT, NT>;
-  using DmaS = DmaTile<BS, RBS, NT>;
-  constexpr int NI = DmaT::NI + DmaS::NI;             // tile DMA instructions per wave per tile
-  constexpr int NIS = OWN_Q ? 0 : (TEACHER ? 4 : 3);  // statistics DMA instructions (wave 0 only)
-  constexpr int NRG = 4 * (DX / 32);                       // bf16 gradient product: LDS reads = MFMAs
-  constexpr int NRL = (RBT + RBS) / 32;                    // bf16 logit products: LDS reads = MFMAs
-  static_assert(SLOT % 256 == 0, "ring slots start on a 256-byte bank window");
-  __shared__ __attribute__((aligned(1024))) char ring[NBUF][SLOT];
-  // converted statistics (log2 units) of the streamed queries: per ring slot in the ping-pong (one
-  // wave of group 1 per statistic converts them a phase before use), per wave otherwise
-  constexpr bool CSLOT = !OWN_Q && NG == 2;
-  __shared__ __attribute__((aligned(16))) float cst[CSLOT ? NBUF : 1][4][32];
-  __shared__ int cst_neg[CSLOT ? NBUF : 1];  // per slot: some streamed query of the tile has g < 0
-  __shared__ __attribute__((aligned(16))) float wst[(!OWN_Q && NG == 1) ? NW : 1][4][32];
-
-  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
-  // wave index in a scalar register: every branch on it (and on the group) is a scalar branch, so a
-  // barrier inside one is executed only by the waves that take it
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = NG == 2 ? (wave >> 2) : 0;
-  // Heads: query head h reads teacher key head h / gt and student key head h / gs.  A query-owner
-  // workgroup serves one query head.  A key-owner workgroup owns key rows of one key head of the
-  // gradient's side and makes one pass over the stream of each of the GX query heads that read it,
-  // accumulating its dK rows over the passes.
-  static_assert(!(OWN_Q && GRP), "a query-owner workgroup serves one query head");
-  const int GX = GRP ? (TEACHER ? a.gt : a.gs) : 1;
-  const int HX = GRP ? a.H / GX : a.H;  // heads of the owned rows
-  const int nbh = a.B * HX;
-  const int nob = ((OWN_Q ? a.mq : a.mk) + BW - 1) / BW;
-  const int bh = blockIdx.x % nbh;  // (batch, owned head)
-  const int oi = blockIdx.x / nbh;
-  // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
-  const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
-  const int b = bh / HX, ho = bh % HX;
-  const Segment sg = segment_of(a, b);
-  const int n_own = OWN_Q ? sg.nq : sg.nk, n_str = OWN_Q ? sg.nk : sg.nq;
-  if (ob * BW >= n_own) return;  // past the end of a shorter segment of a packed batch (whole workgroup)
-  const int off = sg.nk - sg.nq;
-
-  const int64_t own_pt = OWN_Q ? a.sqt[2] : a.skt[2], own_ps = OWN_Q ? a.sqs[2] : a.sks[2];
-  const int64_t str_pt = (OWN_Q ? a.skt[2] : a.sqt[2]) * (int64_t)sizeof(T);
-  const int64_t str_ps = (OWN_Q ? a.sks[2] : a.sqs[2]) * (int64_t)sizeof(T);
-
-  const int o0 = ob * BW;
-  const int o0w = o0 + wave * 32;
-  const int orow = o0w + r32;
-  const bool ovalid = orow < n_own;
-  u32x4 ot_r[NCT / 2], os_r[NCS / 2];
-
-  // Per query head hq (one pass): the streamed operands, this wave's owned rows of both sides (the
-  // other side's key head can change from pass to pass), and the row statistics of head hq.
-  const T *str_t, *str_s;
-  const float *lse_t_bh, *lse_s_bh, *g_bh, *kl_bh;
-  auto set_head = [&](const BwdArgs& A, int hq) {
-    const T* qt = reinterpret_cast<const T*>(A.qt) + sg.bs * A.sqt[0] + hq * A.sqt[1] + sg.q0 * A.sqt[2];
-    const T* kt = reinterpret_cast<const T*>(A.kt) + sg.bs * A.skt[0] + (hq / A.gt) * A.skt[1] + sg.k0 * A.skt[2];
-    const T* qs = reinterpret_cast<const T*>(A.qs) + sg.bs * A.sqs[0] + hq * A.sqs[1] + sg.q0 * A.sqs[2];
-    const T* ks = reinterpret_cast<const T*>(A.ks) + sg.bs * A.sks[0] + (hq / A.gs) * A.sks[1] + sg.k0 * A.sks[2];
-    str_t = OWN_Q ? kt : qt;
-    str_s = OWN_Q ? ks : qs;
-    // the row offsets are formed from an opaque copy of orow in every pass: computed once before the
-    // pass loop instead, they would hold registers through the tile loop that its LDS reads need
-    int row = orow;
-    asm volatile("" : "+v"(row));
-    const bool valid = row < n_own;
-    load_row_regs<T, DT>(ot_r, (OWN_Q ? qt : kt) + (int64_t)row * own_pt, valid, hf);
-    load_row_regs<T, DS>(os_r, (OWN_Q ? qs : ks) + (int64_t)row * own_ps, valid, hf);
-    const int64_t r0 = ((int64_t)sg.bs * A.H + hq) * A.Nq + sg.q0;
-    lse_t_bh = A.lse_t + r0;
-    lse_s_bh = A.lse_s + r0;
-    g_bh = A.g + r0;
-    kl_bh = TEACHER ? A.kl + r0 : nullptr;
-  };
-
-  // query-owner: this lane's row statistics (log2 units), constant over the key stream
-  float own_lt = 0.f, own_ls = 0.f, own_c = 0.f;
-
-  // streamed range of the workgroup: tiles t_begin .. t_begin + ntile - 1 (ntile >= 1)
-  int t_begin, t_end;
-  if constexpr (OWN_Q) {
-    const int q_last = min(n_own, o0 + BW) - 1;
-    const int kend = CAUSAL ? min(n_str, q_last + off + 1) : n_str;
-    t_begin = 0;
-    t_end = (kend + BS - 1) / BS;
-  } else {
-    const int qmin = CAUSAL ? max(0, o0 - off) : 0;  // first query that may see this block's first key
-    t_begin = qmin / BS;
-    t_end = (n_str + BS - 1) / BS;
-  }
-  // never negative: the two groups' barrier counts (2 ntile + 3 each) stay equal even for rows
-  // with no allowed key (an invalid segment of a packed batch)
-  const int ntile = max(t_end - t_begin, 0);
-
-  // ---- streamed tiles: buffer->LDS DMA into the ring, two tiles ahead
-  u32x4 rs_t, rs_s, rst[4];
-  auto set_rsrc = [&]() {  // buffer descriptors of the current head's streamed rows and statistics
-    rs_t = rsrc_words(str_t, n_str > 0 ? (uint32_t)((n_str - 1) * str_pt + RBT) : 0u);
-    rs_s = rsrc_words(str_s, n_str > 0 ? (uint32_t)((n_str - 1) * str_ps + RBS) : 0u);
-    if constexpr (!OWN_Q) {
-      rst[0] = rsrc_words(lse_t_bh, (uint32_t)n_str * 4u);
-      rst[1] = rsrc_words(lse_s_bh, (uint32_t)n_str * 4u);
-      rst[2] = rsrc_words(g_bh, (uint32_t)n_str * 4u);
-      rst[3] = TEACHER ? rsrc_words(kl_bh, (uint32_t)n_str * 4u) : rst[2];
-    }
-  };
-  DmaT dma_t;
-  DmaS dma_s;
-  dma_t.init(str_pt, wave, lane);
-  dma_s.init(str_ps, wave, lane);
-  auto slot_ptr = [&](int u) -> char* { return ring[u]; };
-  auto issue = [&](int s, int u) {  // tile s of the workgroup's stream into ring slot u
-    const int t = t_begin + s;
-    char* sl = slot_ptr(u);
-    const bool whole = (t + 1) * BS <= n_str;
-    dma_t.issue(rs_t, t * BS * (int)str_pt, whole, sl, wave);
-    dma_s.issue(rs_s, t * BS * (int)str_ps, whole, sl + BS * RBT, wave);
-    if constexpr (!OWN_Q) {
-      if (wave == 0) {
-        const int vo = (t * BS + lane) * 4;  // lanes 32..63 fetch the next tile's rows: unused
-#pragma unroll
-        for (int k = 0; k < NIS; ++k) dma_dword(rst[k], vo, sl + TILE + k * 256);
-      }
-    }
-  };
-  // this wave's DMA of the older of its two newest tiles has landed (the newest may be in flight)
-  auto wait_tile = [&]() {
-    if constexpr (NIS > 0) {
-      if (wave == 0)
-        wait_vmcnt<(PD - 1) * (NI + NIS)>();
-      else
-        wait_vmcnt<(PD - 1) * NI>();
-    } else {
-      wait_vmcnt<(PD - 1) * NI>();
-    }
-  };
-  auto tile_state = [&](int s, bool& skip, bool& full) {
-    const int sb = (t_begin + s) * BS;  // first streamed row of the tile
-    if constexpr (OWN_Q) {
-      skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
-      full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
-    } else {
-      skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
-      full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
-    }
-  };
-
-  int off_t[NCT / 2], off_s[NCS / 2];  // logit-product operand offsets (row r32 of a tile)
-  swz_operand_offsets<RBT, NCT / 2>(off_t, r32, hf);
-  swz_operand_offsets<RBS, NCS / 2>(off_s, r32, hf);
-  int toff[2][DX / 32];  // transpose-read offsets of the gradient product
-  tr_offsets<RBX, DX>(toff, lane);
-
-  f32x16 dacc[DX / 32];
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
-  f32x16 st = {}, ss = {};
-  DsTile<T> dsr;  // dS of the last tile through the vector phase, for the gradient product
-
-  // Key owner: statistics of the streamed query rows, converted per tile to the units the vector
-  // phase uses.  The row weight g enters the exponents: g P = sgn(g) exp2(x - (LSE log2 e - log2|g|)),
-  // so dS needs no per-element product with g; only a tile holding a negative weight multiplies by
-  // the sign afterwards (g = 0 gives an exponent of -inf and a zero term).
-  //   0: LSE_t log2 e - log2|g|   1: LSE_s log2 e - log2|g|   2: sgn(g)   3: KL + LSE_t - LSE_s
-  constexpr int NSTAT = TEACHER ? 4 : 3;
-  auto convert_one = [&](int k, const float* raw) -> float {
-    const float g = raw[128 + r32];
-    if (k == 0) return raw[r32] * kLog2e - fast_log2(fabsf(g));
-    if (k == 1) return raw[64 + r32] * kLog2e - fast_log2(fabsf(g));
-    if (k == 2) return g;  // its sign is taken when stored
-    return raw[192 + r32] + raw[r32] - raw[64 + r32];
-  };
-  // Ping-pong: wave 4 + k of group 1 converts statistic k of the tile in slot u, in two halves around
-  // its vector phase: the LDS reads go out first and the converted value is stored at the end, so
-  // their latency hides behind the dS work instead of delaying this wave's barrier.  Both halves of
-  // the wave hold the same 32 rows and store the same values.
-  auto stats_load = [&](const char* sl) -> float {
-    float v = 0.f;
-    if constexpr (CSLOT) {
-      const int k = wave - 4;
-      if (k < NSTAT) v = convert_one(k, reinterpret_cast<const float*>(sl + TILE));
-    }
-    return v;
-  };
-  auto stats_store = [&](int u, float v) {
-    if constexpr (CSLOT) {
-      const int k = wave - 4;
-      if (k < NSTAT) {
-        cst[u][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
-        if (k == 2) {
-          const bool neg = __builtin_amdgcn_ballot_w64(v < 0.f) != 0;
-          if (lane == 0) cst_neg[u] = neg;
-        }
-      }
-    }
-  };
-  auto convert_stats = [&](int u, const char* sl) { stats_store(u, stats_load(sl)); };
-
-  // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
-  auto vector_phase = [&](int s, int u, const char* sl) {
-    bool skip, full;
-    tile_state(s, skip, full);
-    if (NG == 1 && skip) return;  // ping-pong: a skipped tile goes through the masked path (all zero)
-    bool neg = false;  // some row weight of the tile is negative
-    if constexpr (!OWN_Q && !CSLOT) {  // statistics of the 32 streamed queries, converted by each wave
-      const float* raw = reinterpret_cast<const float*>(sl + TILE);
-#pragma unroll
-      for (int k = 0; k < NSTAT; ++k) {
-        const float v = convert_one(k, raw);
-        wst[wave][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
-      }
-      neg = __builtin_amdgcn_ballot_w64(raw[128 + r32] < 0.f) != 0;
-    }
-    if constexpr (CSLOT) neg = __builtin_amdgcn_readfirstlane(cst_neg[u]) != 0;
-    const int sb = (t_begin + s) * BS;
-    float ds[16];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      // The row weight is not applied here: the query owner scales each output row by it at the
-      // store, the key owner has it folded into the statistics (sign below).
-      f32x4 lt4, ls4, cc4;
-      if constexpr (OWN_Q) {
-        lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
-        ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
-        cc4 = f32x4{own_c, own_c, own_c, own_c};
-      } else {
-        const int ql = 8 * g4 + 4 * hf;
-        const float(*cs)[32] = CSLOT ? cst[u] : wst[CSLOT ? 0 : wave];
-        lt4 = *reinterpret_cast<const f32x4*>(&cs[0][ql]);
-        ls4 = *reinterpret_cast<const f32x4*>(&cs[1][ql]);
-        cc4 = TEACHER ? *reinterpret_cast<const f32x4*>(&cs[3][ql]) : f32x4{};
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * g4 + e;
-        const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
-        float v;
-        if constexpr (TEACHER) {
-          v = pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
-        } else {
-          const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
-          v = ps - pt;
-        }
-        ds[i] = v;
-      }
-    }
-    if (neg) {  // key owner, a tile with a negative row weight: dS takes the sign of g
-      asm volatile("");  // keep this a branch: taken only for such tiles
-      const float(*cs)[32] = CSLOT ? cst[u] : wst[CSLOT ? 0 : wave];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 sg4 = *reinterpret_cast<const f32x4*>(&cs[2][8 * g4 + 4 * hf]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ds[4 * g4 + e] *= sg4[e];
-      }
-    }
-    if (!full) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int sr = sb + acc_row(i, hf);
-        const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
-        ds[i] = ok ? ds[i] : 0.f;
-      }
-    }
-    dsr.set(ds);
-  };
-  // Matrix-core work of tile s (ring slot at sl): the gradient product, and the two logit products.
-  auto grad_phase = [&](int s, const char* sl) {
-    bool skip, full;
-    tile_state(s, skip, full);
-    if (!skip) grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sl : sl + BS * RBT, toff, lane);
-  };
-  auto logit_phase = [&](int s, const char* sl) {
-    bool skip, full;
-    tile_state(s, skip, full);
-    if (!skip) {
-      st = f32x16{};
-      ss = f32x16{};
-      tile_dot2_swz<T, DT, DS>(st, ss, sl, sl + BS * RBT, off_t, off_s, ot_r, os_r);
-      if constexpr (sizeof(T) == 2) sched_read_ahead<NRL, 4>();
-    }
-  };
-  // Matrix phase of the ping-pong: gradient product of tile s-1 (slot sp), logit products of
-  // tile s (slot sc), as one straight run of LDS reads and MFMAs so that the reads for the logit
-  // products go out while the gradient MFMAs still run.  It has no branches: a tile that a wave
-  // skips has an all-zero dS (its vector phase masks every element), at s = 0 the gradient
-  // product adds a zero dS times ring slot 3 (zero-filled before the first barrier; tile 3 only
-  // arrives in phase 2), and at s = ntile the logit products (of a tile that has landed, so
-  // finite) are not used.  Those cost under one percent of the MFMA work of a causal problem and
-  // keep a single register assignment for the accumulators.
-  auto matrix_phase = [&](const char* sp, const char* sc) {
-    grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sp : sp + BS * RBT, toff, lane);
-    st = f32x16{};
-    ss = f32x16{};
-    tile_dot2_swz<T, DT, DS>(st, ss, sc, sc + BS * RBT, off_t, off_s, ot_r, os_r);
-    if constexpr (sizeof(T) == 2) sched_read_ahead<NRG + NRL, 6>();
-  };
-
-  for (int pass = 0; pass < GX; ++pass) {
-    set_head(a, ho * GX + pass);
-    set_rsrc();
-    if constexpr (OWN_Q) {
-      if (ovalid) {
-        own_lt = lse_t_bh[orow] * kLog2e;
-        own_ls = lse_s_bh[orow] * kLog2e;
-        if constexpr (TEACHER) own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
-      }
-    }
-    {
-      float z[16] = {};
-      dsr.set(z);
-    }
-    if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
-      static_assert(TILE % 16 == 0, "slot fill");
-#pragma unroll
-      for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
-    }
-    wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
-#pragma unroll
-    for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
-    wait_tile();
-    __syncthreads();
-    if constexpr (NG == 2) {
-      // Ring protocol (phases p = 0, 1, ...; tile s is read from phase 2s to 2s+3): tile s+PD is
-      // issued at the start of phase 2s into the slot of tile s-2, and each wave waits for its share
-      // of tile s+1 at the end of phase 2s+1, before that phase's barrier.  The last slot, read by
-      // the s = 0 gradient product, first receives a tile in phase 2.
-      if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
-        issue(PD, PD);
-        convert_stats(0, ring[0]);
-        __syncthreads();
-      }
-      for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
-#pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-          const int s = s0 + u;
-          if (s <= ntile) {
-            // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
-            if (grp == 0) issue(s + PD, (u + PD) % NBUF);
-            matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
-            if (grp == 1) wait_tile();
-            __syncthreads();
-            // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
-            if (s < ntile) {
-              float cv = 0.f;
-              if (grp == 1) {
-                issue(s + PD + 1, (u + PD + 1) % NBUF);
-                cv = stats_load(slot_ptr((u + 1) % NBUF));  // tile s+1 landed in the last phase
-              }
-              vector_phase(s, u, slot_ptr(u));
-              if (grp == 1) stats_store((u + 1) % NBUF, cv);
-              if (grp == 0) wait_tile();
-              __syncthreads();
-            } else if (grp == 0) {
-              __syncthreads();  // group 0's last phase, matching group 1's late start
-            }
-          }
-        }
-      }
-    } else {
-      // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
-      // and tile s+1 waited for at its end.
-      for (int s0 = 0; s0 < ntile; s0 += NBUF) {
-#pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-          const int s = s0 + u;
-          if (s < ntile) {
-            issue(s + PD, (u + PD) % NBUF);
-            logit_phase(s, slot_ptr(u));
-            vector_phase(s, u, slot_ptr(u));
-            grad_phase(s, slot_ptr(u));
-            wait_tile();
-            __syncthreads();
-          }
-        }
-      }
-    }
-    wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
-    if (pass + 1 < GX) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
-  }
-
-  const float scale = TEACHER ? a.scale_t : a.scale_s;
-  float* out = (OWN_Q ? a.dq : a.dk) +
-               (((int64_t)sg.bs * HX + ho) * (OWN_Q ? a.Nq : a.Nk) + (OWN_Q ? sg.q0 : sg.k0)) * DX;
-  // query owner: dS was formed without the row weight (it is one factor per output row)
-  float rscale[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = o0w + acc_row(i, hf);
-    rscale[i] = OWN_Q ? (r < n_own ? scale * g_bh[r] : 0.f) : scale;
-  }
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = o0w + acc_row(i, hf);
-      if (r < n_own) out[(int64_t)r * DX + db * 32 + r32] = rscale[i] * dacc[db][i];
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------------------------
-template <typename T, int DT, int DS, bool C, bool TE, bool OWN_Q>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  const int n_own = OWN_Q ? a.mq : a.mk;  // longest segment (dense batch: all rows)
-  // owned heads: query heads, or the key heads of the gradient's side
-  const int gx = OWN_Q ? 1 : (TE ? a.gt : a.gs);
-  const int64_t nblk = (int64_t)((n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * (a.H / gx);
-  if (nblk <= 0) return hipSuccess;
-  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  if constexpr (!OWN_Q) {
-    if (gx > 1) {
-      hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, false, true>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s,
-                         a);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, OWN_Q, false>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s,
-                     a);
-  return hipGetLastError();
-}
-
-template <bool OWN_Q, typename T, int DT, int DS>
-static hipError_t bwd_ct(const BwdArgs& a, bool causal, bool teacher, hipStream_t s) {
-  if (causal)
-    return teacher ? launch_bwd_t<T, DT, DS, true, true, OWN_Q>(a, s) : launch_bwd_t<T, DT, DS, true, false, OWN_Q>(a, s);
-  return teacher ? launch_bwd_t<T, DT, DS, false, true, OWN_Q>(a, s) : launch_bwd_t<T, DT, DS, false, false, OWN_Q>(a, s);
-}
-
-template <bool OWN_Q, typename T>
-static hipError_t bwd_d(const BwdArgs& a, int dt, int ds, bool causal, bool teacher, hipStream_t s) {
-  if (dt == 128 && ds == 128) return bwd_ct<OWN_Q, T, 128, 128>(a, causal, teacher, s);
-  if (dt == 128 && ds == 64) return bwd_ct<OWN_Q, T, 128, 64>(a, causal, teacher, s);
-  if (dt == 64 && ds == 128) return bwd_ct<OWN_Q, T, 64, 128>(a, causal, teacher, s);
-  if (dt == 64 && ds == 64) return bwd_ct<OWN_Q, T, 64, 64>(a, causal, teacher, s);
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int dt, int ds, bool causal, bool teacher, hipStream_t s) {
-  if (dtype == 1) return bwd_d<true, __bf16>(a, dt, ds, causal, teacher, s);
-  if (dtype == 0) return bwd_d<true, float>(a, dt, ds, causal, teacher, s);
-  return hipErrorInvalidValue;
+  return bwd_dispatch<false, true>(a, dtype, dt, ds, causal, teacher, s);
 }
 
 hipError_t launch_bwd_dk(const BwdArgs& a, int dtype, int dt, int ds, bool causal, bool teacher, hipStream_t s) {
-  if (dtype == 1) return bwd_d<false, __bf16>(a, dt, ds, causal, teacher, s);
-  if (dtype == 0) return bwd_d<false, float>(a, dt, ds, causal, teacher, s);
-  return hipErrorInvalidValue;
+  return bwd_dispatch<false, false>(a, dtype, dt, ds, causal, teacher, s);
 }
 
 }  // namespace skl

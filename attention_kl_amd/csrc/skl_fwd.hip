@@ -1,260 +1,10 @@
-// One-pass forward of the attention KL divergence on gfx950.
-//
-// StreamKL abstract (arXiv 2026), S4: the coupled two-distribution KL is reduced
-// online, in one pass that streams query/key tiles through on-chip memory.  The
-// online form used here follows from the definition: with per-row running
-// maxima m_t, m_s of the teacher and student logits, running sums
-// l_t = sum exp(a_j - m_t), l_s = sum exp(b_j - m_s) and the teacher-weighted
-// accumulator acc = sum exp(a_j - m_t) (a_j - b_j), all rescaled when a maximum
-// grows,
-//     sum_j P_t,j (a_j - b_j) = acc / l_t,   KL = acc/l_t - (m_t + ln l_t) + (m_s + ln l_s).
-// The row is closed as acc/l_t + (m_s - m_t) + ln(l_s/l_t), the same value
-// with one log of a ratio instead of two large log-sum-exps that cancel.
-//
-// Work split: one workgroup = 4 wavefronts = 128 query rows of one (b, h); each
-// wavefront keeps its 32 rows' Q_t, Q_s in registers as MFMA B operands and
-// streams key tiles through LDS.  The logit tile is formed transposed
-// (keys x queries) so each lane owns one query row and 16 of its keys: the two
-// lane halves of a row keep separate running states over disjoint key subsets
-// and are merged once at the end, so the key loop needs no cross-lane traffic.
-//
-// Schedule: 32-key tiles reach LDS by buffer->LDS DMA into a 3-slot ring, two
-// tiles ahead, one barrier per tile; three workgroups share a CU, so while one
-// wavefront waits on its MFMAs the others run their exp/VALU work.  Keys a row
-// may not see (causal diagonal, ragged end) are set to -inf in the logit tile
-// under a wave-uniform branch, then every tile takes the same update.
-#include "skl_device.hpp"
-#include "skl_kernels.hpp"
+// Launcher of the KL forward kernel (the kernel template and its dispatch are in skl_fwd_impl.hpp).
+#include "skl_fwd_impl.hpp"
 
 namespace skl {
 
-template <typename T>
-struct FwdTile {
-  static constexpr int BQ = 128;  // query rows per workgroup (4 wavefronts x 32)
-  static constexpr int BK = 32;   // keys per LDS tile (one 32 x 32 logit block per wavefront)
-  static constexpr int NBUF = 3;  // LDS ring depth: tiles t+1 and t+2 are in flight while t is used
-  static constexpr int NT = 256;
-};
-
-// Per-lane running state of one query row over the keys this lane half sees.
-struct RowState {
-  float m_t, m_s;  // running maxima in log2 units (logit * scale * log2 e)
-  float l_t, l_s, acc;
-};
-
-// max(a, b, c) as one v_max3_f32.  Logits here are finite or -inf, never NaN, so the NaN
-// quieting the compiler puts in front of fmaxf (one extra VALU op per operand that is not
-// known to be quiet, such as an MFMA result) is not needed.
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// Online update with one 32-key subtile: st/ss are the raw (unscaled) logits of this
-// lane's 16 keys; masked keys are -inf in st/ss, dif = (a - b) / scale_t is finite.
-__device__ __forceinline__ void online_update(RowState& s, const f32x16& st, const f32x16& ss, const float* dif,
-                                              float c_t, float c_s) {
-  float mx = max3(st[0], st[1], st[2]), my = max3(ss[0], ss[1], ss[2]);
-#pragma unroll
-  for (int i = 3; i < 15; i += 2) {
-    mx = max3(mx, st[i], st[i + 1]);
-    my = max3(my, ss[i], ss[i + 1]);
-  }
-  mx = max3(mx, st[15], mx);
-  my = max3(my, ss[15], my);
-  const float mt_new = max3(s.m_t, mx * c_t, s.m_t);
-  const float ms_new = max3(s.m_s, my * c_s, s.m_s);
-  const float al_t = fast_exp2(s.m_t - mt_new);
-  const float al_s = fast_exp2(s.m_s - ms_new);
-  s.m_t = mt_new;
-  s.m_s = ms_new;
-  // partial sums of this subtile, started from its first key
-  float pt = fast_exp2(fmaf(st[0], c_t, -mt_new));
-  float ps = fast_exp2(fmaf(ss[0], c_s, -ms_new));
-  float pa = pt * dif[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) {
-    const float e = fast_exp2(fmaf(st[i], c_t, -mt_new));
-    const float f = fast_exp2(fmaf(ss[i], c_s, -ms_new));
-    pt += e;
-    ps += f;
-    pa = fmaf(e, dif[i], pa);
-  }
-  s.l_t = fmaf(s.l_t, al_t, pt);
-  s.l_s = fmaf(s.l_s, al_s, ps);
-  s.acc = fmaf(s.acc, al_t, pa);
-}
-
-template <typename T, int DT, int DS, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1, 3))) void fwd_kernel(
-    const FwdArgs a) {
-  constexpr int BQ = FwdTile<T>::BQ, BK = FwdTile<T>::BK, NBUF = FwdTile<T>::NBUF, NT = FwdTile<T>::NT;
-  constexpr int RBT = DT * (int)sizeof(T), RBS = DS * (int)sizeof(T);  // row bytes
-  constexpr int TILE = BK * (RBT + RBS);                                  // one K_t + K_s tile
-  constexpr int NCT = RBT / 16, NCS = RBS / 16;                           // 16-byte chunks per row
-  using DmaT = DmaTile<BK, RBT, NT>;
-  using DmaS = DmaTile<BK, RBS, NT>;
-  constexpr int NI = DmaT::NI + DmaS::NI;  // DMA instructions per thread per tile
-  // one array per ring slot: distinct objects let the compiler see that a DMA into one slot never
-  // aliases reads of another, so it adds no wait beyond the explicit ones below
-  __shared__ __attribute__((aligned(1024))) char slot0[TILE], slot1[TILE], slot2[TILE];
-  static_assert(NBUF == 3, "one named array per ring slot");
-
-  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: per-wave tests branch on SCC
-  const int nbh = a.B * a.H;
-  const int nqb = (a.mq + BQ - 1) / BQ;
-  const int bh = blockIdx.x % nbh;
-  const int qi = blockIdx.x / nbh;
-  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;  // causal: longest rows first
-  const int b = bh / a.H, h = bh % a.H;
-  const Segment sg = segment_of(a, b);
-  const int nq = sg.nq, nk = sg.nk;
-  const int q0 = qb * BQ;
-  if (q0 >= nq) return;  // past the end of a shorter segment of a packed batch (whole workgroup)
-  const int off = nk - nq;
-
-  const T* qt = reinterpret_cast<const T*>(a.qt) + sg.bs * a.sqt[0] + h * a.sqt[1] + sg.q0 * a.sqt[2];
-  // grouped-query attention: query head h reads key head h / g of each side
-  const char* kt = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.kt) + sg.bs * a.skt[0] +
-                                                 (h / a.gt) * a.skt[1] + sg.k0 * a.skt[2]);
-  const T* qs = reinterpret_cast<const T*>(a.qs) + sg.bs * a.sqs[0] + h * a.sqs[1] + sg.q0 * a.sqs[2];
-  const char* ks = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.ks) + sg.bs * a.sks[0] +
-                                                 (h / a.gs) * a.sks[1] + sg.k0 * a.sks[2]);
-  const int64_t kt_pitch = a.skt[2] * (int64_t)sizeof(T), ks_pitch = a.sks[2] * (int64_t)sizeof(T);
-
-  const int q0w = q0 + wave * 32;
-  const int qrow = q0w + r32;
-  u32x4 qt_r[NCT / 2], qs_r[NCS / 2];
-  load_row_regs<T, DT>(qt_r, qt + (int64_t)qrow * a.sqt[2], qrow < nq, hf);
-  load_row_regs<T, DS>(qs_r, qs + (int64_t)qrow * a.sqs[2], qrow < nq, hf);
-
-  RowState rs{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
-
-  const int q_last = min(nq, q0 + BQ) - 1;
-  const int kend = CAUSAL ? min(nk, q_last + off + 1) : nk;
-  const int ntiles = max(kend + BK - 1, 0) / BK;  // 0 only for rows with no key (an invalid segment)
-
-  // K tiles: buffer->LDS DMA (zero past the last key) into a NBUF-deep ring, two tiles ahead
-  const u32x4 rk_t = rsrc_words(kt, nk > 0 ? (uint32_t)((nk - 1) * kt_pitch + RBT) : 0u);
-  const u32x4 rk_s = rsrc_words(ks, nk > 0 ? (uint32_t)((nk - 1) * ks_pitch + RBS) : 0u);
-  DmaT dma_t;
-  DmaS dma_s;
-  dma_t.init(kt_pitch, wave, lane);
-  dma_s.init(ks_pitch, wave, lane);
-  auto slot_ptr = [&](int slot) -> char* { return slot == 0 ? slot0 : (slot == 1 ? slot1 : slot2); };
-  auto issue = [&](int tile, int slot) {
-    const bool whole = (tile + 1) * BK <= nk;
-    dma_t.issue(rk_t, tile * BK * (int)kt_pitch, whole, slot_ptr(slot), wave);
-    dma_s.issue(rk_s, tile * BK * (int)ks_pitch, whole, slot_ptr(slot) + BK * RBT, wave);
-  };
-  // this lane's operand chunk offsets (row r32 of a tile), loop-invariant
-  int off_t[NCT / 2], off_s[NCS / 2];
-  swz_operand_offsets<RBT, NCT / 2>(off_t, r32, hf);
-  swz_operand_offsets<RBS, NCS / 2>(off_s, r32, hf);
-
-  // The compiler cannot see the DMAs in the hardware's vmcnt; retire every load of its own now,
-  // so that none of its waits lands inside the loop, where it would also drain the DMA ring.
-  wait_vmcnt<0>();
-  issue(0, 0);
-  issue(1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
-  // One step per tile; the loop is unrolled by the ring depth so every LDS address is a
-  // per-lane base plus an immediate.  The tile count is rounded up to a multiple of the ring
-  // depth: the extra tiles lie past every row's last key, so they are fully masked and leave the
-  // state unchanged, and the unrolled body needs no guard (whose join would copy the state).
-  const int ntiles_pad = (ntiles + NBUF - 1) / NBUF * NBUF;
-  for (int t0 = 0; t0 < ntiles_pad; t0 += NBUF) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int t = t0 + u;
-      {
-        wait_vmcnt<NI>();  // tile t has landed (tile t+1 may still be in flight)
-        __syncthreads();   // ... for every wave; and every wave is done with tile t-1
-        issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
-        const char* tile = slot_ptr(u);
-        const int kb = t * BK;
-        f32x16 st = {}, ss = {};
-        tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
-        tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
-        float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          dif[i] = fmaf(ss[i], -a.ratio, st[i]);
-          // pin dif here, ahead of the masking branch: then no unmasked logit outlives the branch
-          // and the masking below rewrites st/ss in place instead of copying them on every tile
-          asm volatile("" : "+v"(dif[i]));
-        }
-        // A tile that no row of this wavefront reaches (causal) goes through the masked path too:
-        // with every key at -inf the update leaves the state bit for bit unchanged, and the loop
-        // keeps one definition of the state (no copies at a join).  Such tiles are under 1% of
-        // a causal problem's.
-        const bool full = t < ntiles && kb + 31 < nk && (!CAUSAL || kb + 31 <= q0w + off);
-        if (!full) {  // in place, so the update below has one copy of its state
-          asm volatile("");  // keep this a branch: the compiler would otherwise select on every tile
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + acc_row(i, hf);
-            const bool ok = key < nk && (!CAUSAL || key <= qrow + off);
-            st[i] = ok ? st[i] : -INFINITY;
-            ss[i] = ok ? ss[i] : -INFINITY;
-          }
-        }
-        online_update(rs, st, ss, dif, a.c_t, a.c_s);
-        // the new state exists before the next barrier: keeps each tile's update in its own step
-        asm volatile("" ::"v"(rs.m_t), "v"(rs.m_s), "v"(rs.l_t), "v"(rs.l_s), "v"(rs.acc));
-      }
-    }
-  }
-  wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS when it exits
-
-  // Merge the two half-row states (disjoint key subsets) of each query row.
-  const float o_mt = __shfl_xor(rs.m_t, 32), o_lt = __shfl_xor(rs.l_t, 32), o_acc = __shfl_xor(rs.acc, 32);
-  const float o_ms = __shfl_xor(rs.m_s, 32), o_ls = __shfl_xor(rs.l_s, 32);
-  const float Mt = fmaxf(rs.m_t, o_mt), Ms = fmaxf(rs.m_s, o_ms);
-  const float f1 = fast_exp2(rs.m_t - Mt), f2 = fast_exp2(o_mt - Mt);
-  const float g1 = fast_exp2(rs.m_s - Ms), g2 = fast_exp2(o_ms - Ms);
-  const float Lt = rs.l_t * f1 + o_lt * f2;
-  const float Ls = rs.l_s * g1 + o_ls * g2;
-  const float A = rs.acc * f1 + o_acc * f2;
-
-  if (hf == 0 && qrow < nq) {
-    // true divisions: Ls / Lt is exactly 1 when the two states are bitwise equal
-    const int64_t o = ((int64_t)sg.bs * a.H + h) * a.Nq + sg.q0 + qrow;
-    a.kl[o] = a.scale_t * (A / Lt) + kLn2 * ((Ms - Mt) + fast_log2(Ls / Lt));
-    a.lse_t[o] = kLn2 * (Mt + fast_log2(Lt));
-    a.lse_s[o] = kLn2 * (Ms + fast_log2(Ls));
-  }
-}
-
-template <typename T, int DT, int DS, bool C>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-  const int64_t nqb = (a.mq + FwdTile<T>::BQ - 1) / FwdTile<T>::BQ;
-  const int64_t nblk = nqb * a.B * a.H;
-  if (nblk <= 0) return hipSuccess;
-  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename T, int DT, int DS>
-static hipError_t fwd_c(const FwdArgs& a, bool causal, hipStream_t s) {
-  return causal ? launch_fwd_t<T, DT, DS, true>(a, s) : launch_fwd_t<T, DT, DS, false>(a, s);
-}
-
-template <typename T>
-static hipError_t fwd_d(const FwdArgs& a, int dt, int ds, bool causal, hipStream_t s) {
-  if (dt == 128 && ds == 128) return fwd_c<T, 128, 128>(a, causal, s);
-  if (dt == 128 && ds == 64) return fwd_c<T, 128, 64>(a, causal, s);
-  if (dt == 64 && ds == 128) return fwd_c<T, 64, 128>(a, causal, s);
-  if (dt == 64 && ds == 64) return fwd_c<T, 64, 64>(a, causal, s);
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int dt, int ds, bool causal, hipStream_t s) {
-  if (dtype == 1) return fwd_d<__bf16>(a, dt, ds, causal, s);
-  if (dtype == 0) return fwd_d<float>(a, dt, ds, causal, s);
-  return hipErrorInvalidValue;
+  return fwd_dispatch<false>(a, dtype, dt, ds, causal, s);
 }
 
 }  // namespace skl

@@ -11,9 +11,10 @@ struct FwdArgs {
   const void* kt;
   const void* qs;
   const void* ks;
-  float* kl;
-  float* lse_t;
+  float* kl;     // KL forward: KL_i.  JS pass: JS_i
+  float* lse_t;  // KL forward: written.  JS pass: read
   float* lse_s;
+  float* js_t;   // JS pass: KL(P_t || M)_i
   int64_t sqt[3], skt[3], sqs[3], sks[3];  // (b, h, n) element strides; K strides per key head
   int32_t B, H, Nq, Nk;
   int32_t gt, gs;   // query heads per key head (teacher, student): query head h reads key head h / g
@@ -35,7 +36,8 @@ struct BwdArgs {
   const void* ks;
   const float* lse_t;
   const float* lse_s;
-  const float* kl;  // read only for teacher gradients
+  const float* kl;  // KL: read only for teacher gradients.  JS: js_t, the teacher half KL(P_t || M)
+  const float* js;  // JS: JS_i
   const float* g;
   float* dq;  // query-owner kernel output [B,H,Nq,d_side]
   float* dk;  // key-owner kernel output   [B,Hk_side,Nk,d_side]
@@ -70,5 +72,10 @@ __device__ __forceinline__ Segment segment_of(const A& a, int b) {
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int d_t, int d_s, bool causal, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
 hipError_t launch_bwd_dk(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
+// Jensen-Shannon: the forward's second pass (kl receives JS, js_t the teacher half; lse_t, lse_s are
+// read) and the backward kernels of sum_i g_i JS_i (kl = js_t, js = JS).
+hipError_t launch_js_fwd(const FwdArgs& a, int dtype, int d_t, int d_s, bool causal, hipStream_t s);
+hipError_t launch_js_bwd_dq(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
+hipError_t launch_js_bwd_dk(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
 
 }  // namespace skl

@@ -18,6 +18,8 @@ Directions (the pages fix none, S1):
                gradients of the student then come from the primitive's
                teacher-gradient path
   "symmetric"  KL(P_t || P_s) + KL(P_s || P_t)
+  "js"         Jensen-Shannon: KL(P_t || M)/2 + KL(P_s || M)/2 with M = (P_t + P_s)/2, symmetric and at
+               most ln 2 (streamkl_js_fwd / streamkl_js_bwd)
 
 Packed variable-length batches (inputs [N, heads, d], segments given by cu_seqlens_q /
 cu_seqlens_k) give the per-row KL as [H, N_Q]; "batchmean" then divides by the number of
@@ -36,36 +38,45 @@ import torch
 
 from . import streamkl as S
 
-DIRECTIONS = ("forward", "reverse", "symmetric")
+DIRECTIONS = ("forward", "reverse", "symmetric", "js")
 REDUCTIONS = ("none", "sum", "mean", "batchmean")
 
 
 class StreamKLFunction(torch.autograd.Function):
-    """Per-row KL(P_t || P_s) with its backward on the library.  Inputs [B, H, N, d], or [N, H, d]
-    with packed = (cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k) for a packed batch."""
+    """Per-row KL(P_t || P_s) (js=True: Jensen-Shannon divergence) with its backward on the library.
+    Inputs [B, H, N, d], or [N, H, d] with packed = (cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+    max_seqlen_k) for a packed batch."""
 
     @staticmethod
     def forward(ctx, qt, kt, qs, ks, causal: bool, scale_t: Optional[float], scale_s: Optional[float],
-                packed: Optional[tuple] = None):
+                packed: Optional[tuple] = None, js: bool = False):
         seg = _seg_kwargs(packed)
-        kl, lse_t, lse_s = S.fwd(qt, kt, qs, ks, causal=causal, scale_t=scale_t, scale_s=scale_s, **seg)
-        ctx.save_for_backward(qt, kt, qs, ks, kl, lse_t, lse_s)
-        ctx.cfg = (bool(causal), scale_t, scale_s)
+        kw = dict(causal=causal, scale_t=scale_t, scale_s=scale_s, **seg)
+        if js:
+            div, lse_t, lse_s, half_t = S.js_fwd(qt, kt, qs, ks, **kw)
+            ctx.save_for_backward(qt, kt, qs, ks, div, lse_t, lse_s, half_t)
+        else:
+            div, lse_t, lse_s = S.fwd(qt, kt, qs, ks, **kw)
+            ctx.save_for_backward(qt, kt, qs, ks, div, lse_t, lse_s)
+        ctx.cfg = (bool(causal), scale_t, scale_s, bool(js))
         ctx.packed = packed
-        return kl
+        return div
 
     @staticmethod
     def backward(ctx, g):
-        qt, kt, qs, ks, kl, lse_t, lse_s = ctx.saved_tensors
-        causal, scale_t, scale_s = ctx.cfg
+        qt, kt, qs, ks, div, lse_t, lse_s = ctx.saved_tensors[:7]
+        causal, scale_t, scale_s, js = ctx.cfg
         need_t = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
         need_s = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
         if not (need_t or need_s):
-            return (None,) * 8
+            return (None,) * 9
         g = g.to(torch.float32).contiguous()  # the upstream gradient may be a broadcast view
-        grads = S.bwd(qt, kt, qs, ks, lse_t, lse_s, g, causal=causal, kl=kl if need_t else None,
-                      teacher_grads=need_t, student_grads=need_s, scale_t=scale_t, scale_s=scale_s,
-                      **_seg_kwargs(ctx.packed))
+        kw = dict(causal=causal, teacher_grads=need_t, student_grads=need_s, scale_t=scale_t, scale_s=scale_s,
+                  **_seg_kwargs(ctx.packed))
+        if js:
+            grads = S.js_bwd(qt, kt, qs, ks, lse_t, lse_s, div, ctx.saved_tensors[7], g, **kw)
+        else:
+            grads = S.bwd(qt, kt, qs, ks, lse_t, lse_s, g, kl=div if need_t else None, **kw)
         if ctx.packed is not None:  # the library's packed layout [heads, N, d] -> the inputs' [N, heads, d]
             grads = tuple(None if x is None else x.transpose(0, 1) for x in grads)
         dq_s, dk_s, dq_t, dk_t = grads
@@ -75,7 +86,7 @@ class StreamKLFunction(torch.autograd.Function):
 
         return (cast(dq_t, qt, ctx.needs_input_grad[0]), cast(dk_t, kt, ctx.needs_input_grad[1]),
                 cast(dq_s, qs, ctx.needs_input_grad[2]), cast(dk_s, ks, ctx.needs_input_grad[3]),
-                None, None, None, None)
+                None, None, None, None, None)
 
 
 def _seg_kwargs(packed):
@@ -117,7 +128,9 @@ def attention_kl(qt, kt, qs, ks, *, causal: bool = False, scale_t: Optional[floa
         mk = longest(cu_seqlens_k) if max_seqlen_k is None else int(max_seqlen_k)
         packed = (cu_seqlens_q, cu_seqlens_k, mq, mk)
         n_batch = cu_seqlens_q.numel() - 1
-    if direction == "forward":
+    if direction == "js":
+        kl = StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s, packed, True)
+    elif direction == "forward":
         kl = StreamKLFunction.apply(qt, kt, qs, ks, causal, scale_t, scale_s, packed)
     elif direction == "reverse":
         kl = StreamKLFunction.apply(qs, ks, qt, kt, causal, scale_s, scale_t, packed)

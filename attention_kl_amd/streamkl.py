@@ -72,7 +72,10 @@ def lib() -> ctypes.CDLL:
         L.streamkl_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.streamkl_bwd_dq.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.streamkl_bwd_dk.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-        for f in ("streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_version"):
+        L.streamkl_js_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.streamkl_js_bwd.argtypes = [_P] + [_vp] * 14
+        for f in ("streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_js_fwd",
+                  "streamkl_js_bwd", "streamkl_version"):
             getattr(L, f).restype = ctypes.c_int
         L.streamkl_status_string.argtypes = [ctypes.c_int]
         L.streamkl_status_string.restype = ctypes.c_char_p
@@ -247,5 +250,45 @@ def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale
     return out
 
 
-for _f in (fwd, bwd, bwd_dq, bwd_dk):
+def js_fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
+           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+    """Per-row Jensen-Shannon divergence (streamkl_js_fwd): (js, lse_t, lse_s, js_t), float32 in the
+    layout of fwd's outputs; js_t is the teacher half KL(P_t || M), which js_bwd needs."""
+    import torch
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k)
+    if out is None:
+        out = tuple(torch.empty(p.stat_shape(), dtype=torch.float32, device=qt.device) for _ in range(4))
+    js, lse_t, lse_s, js_t = out
+    _check(lib().streamkl_js_fwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(js), _ptr(lse_t),
+                                 _ptr(lse_s), _ptr(js_t), _stream(stream)), "streamkl_js_fwd")
+    return js, lse_t, lse_s, js_t
+
+
+def js_bwd(qt, kt, qs, ks, lse_t, lse_s, js, js_t, g, *, causal: bool, teacher_grads: bool = False,
+           student_grads: bool = True, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
+           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+    """Gradients of sum_i g_i JS_i (streamkl_js_bwd): (dq_s, dk_s, dq_t, dk_t) as bwd returns them."""
+    import torch
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k)
+    dev = qt.device
+    if out is None:
+        out = [None, None, None, None]
+        if student_grads:
+            out[0] = torch.empty(p.dq_shape(p.d_s), dtype=torch.float32, device=dev)
+            out[1] = torch.empty(p.dk_shape(p.Hk_s, p.d_s), dtype=torch.float32, device=dev)
+        if teacher_grads:
+            out[2] = torch.empty(p.dq_shape(p.d_t), dtype=torch.float32, device=dev)
+            out[3] = torch.empty(p.dk_shape(p.Hk_t, p.d_t), dtype=torch.float32, device=dev)
+    out = list(out) + [None] * (4 - len(out))
+    dq_s, dk_s = (out[0], out[1]) if student_grads else (None, None)
+    dq_t, dk_t = (out[2], out[3]) if teacher_grads else (None, None)
+    _check(lib().streamkl_js_bwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
+                                 _ptr(js), _ptr(js_t), _ptr(g), _ptr(dq_s), _ptr(dk_s), _ptr(dq_t), _ptr(dk_t),
+                                 _stream(stream)), "streamkl_js_bwd")
+    return dq_s, dk_s, dq_t, dk_t
+
+
+for _f in (fwd, bwd, bwd_dq, bwd_dk, js_fwd, js_bwd):
     _f.__doc__ += "\n\n    " + _PACKED_DOC

@@ -25,12 +25,15 @@ MI355X_PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flo
 MI355X_PEAK_FP32_MFMA_TFLOPS = 157.3
 MI355X_HBM_GBS = 8000.0
 METRIC = "attention-KL fwd/bwd TFLOP/s and ms at N=32K, % of MFMA peak, extra HBM bytes"
-KERNEL_SOURCES = {"fwd": "attention_kl_amd/csrc/skl_fwd.hip", "bwd_dq": "attention_kl_amd/csrc/skl_bwd.hip",
-                  "bwd_dk": "attention_kl_amd/csrc/skl_bwd.hip"}
+_C = "attention_kl_amd/csrc/"
+KERNEL_SOURCES = {"fwd": [_C + "skl_fwd.hip", _C + "skl_fwd_impl.hpp"],
+                  "bwd_dq": [_C + "skl_bwd.hip", _C + "skl_bwd_impl.hpp"],
+                  "bwd_dk": [_C + "skl_bwd.hip", _C + "skl_bwd_impl.hpp"]}
 
 
 def source_sha(kernel: str) -> str:
-    paths = [KERNEL_SOURCES[kernel], "attention_kl_amd/csrc/skl_device.hpp"]
+    """Hash of the sources a kernel is built from (its template, launchers and the shared headers)."""
+    paths = KERNEL_SOURCES[kernel] + [_C + "skl_device.hpp", _C + "skl_kernels.hpp"]
     h = hashlib.sha256()
     for p in paths:
         h.update(open(os.path.join(ROOT, p), "rb").read())
@@ -48,6 +51,10 @@ def kernel_flops(w, kernel: str, pairs=None) -> float:
     pairs = w.pairs_per_head() * w.B * w.H if pairs is None else pairs
     if kernel == "fwd":
         return 2.0 * pairs * (w.d_t + w.d_s)
+    if kernel == "js_fwd":  # Jensen-Shannon: the KL pass for the log-sum-exps, then the JS pass
+        return 4.0 * pairs * (w.d_t + w.d_s)
+    if kernel == "js_bwd":  # both backward kernels of the student side
+        return 4.0 * pairs * (w.d_t + 2 * w.d_s)
     return 2.0 * pairs * (w.d_t + 2 * w.d_s)
 
 
@@ -165,7 +172,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int = 
     return ent
 
 
-def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3, seg=None):
+def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3, seg=None, direction="kl"):
     """The same step (forward, student dQ and dK) through torch autograd: sum_i g_i KL_i .backward().
 
     Beyond the raw kernels it pays for autograd bookkeeping, output allocation and the cast of
@@ -178,7 +185,8 @@ def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3, seg=None)
 
     def run():
         qs_.grad = ks_.grad = None
-        kl = attention_kl(qt, kt, qs_, ks_, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s, **(seg or {}))
+        kl = attention_kl(qt, kt, qs_, ks_, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s,
+                          direction="js" if direction == "js" else "forward", **(seg or {}))
         (kl * g).sum().backward()
 
     run()
@@ -213,6 +221,8 @@ def main():
     ap.add_argument("--student-key-heads", type=int, default=None,
                     help="grouped student keys: K key heads shared by the H query heads (K divides H); key head j "
                          "is the workload's head j*H/K.  Default: one key head per query head")
+    ap.add_argument("--divergence", choices=("kl", "js"), default="kl",
+                    help="kl (default): KL(P_t || P_s); js: the Jensen-Shannon step (streamkl_js_fwd + streamkl_js_bwd)")
     ap.add_argument("--packed-mix", type=int, default=None, metavar="SEED",
                     help="packed variable-length batch: the workload's rows cut into segments of a seeded "
                          "log-uniform length mix (256..8192 rows), each its own (causal) problem")
@@ -267,8 +277,21 @@ def main():
     dq = torch.empty(lead + (H, w.Nq, w.d_s), dtype=torch.float32, device=dev)
     dk = torch.empty(lead + (hk_s, w.Nk, w.d_s), dtype=torch.float32, device=dev)
     kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s, **seg)
+    js = args.divergence == "js"
+    ht = torch.empty_like(kl)  # JS: the teacher half KL(P_t || M)
 
     def step(ev=None):
+        if js:  # forward (two launches), then both student backward kernels
+            if ev is not None:
+                ev[0].record()
+            S.js_fwd(qt, kt, qs, ks, out=(kl, lt, ls, ht), **kw)
+            if ev is not None:
+                ev[1].record()
+            S.js_bwd(qt, kt, qs, ks, lt, ls, kl, ht, g, out=[dq, dk], **kw)
+            if ev is not None:
+                ev[2].record()
+                ev[3].record()
+            return
         if ev is not None:
             ev[0].record()
         S.fwd(qt, kt, qs, ks, out=(kl, lt, ls), **kw)
@@ -299,8 +322,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     extra_alloc = free0 - torch.cuda.mem_get_info()[0]
-    per = {"fwd": [], "bwd_dk": [], "bwd_dq": []}
+    per = {"js_fwd": [], "js_bwd": []} if js else {"fwd": [], "bwd_dk": [], "bwd_dq": []}
     for e in evs:
+        if js:
+            per["js_fwd"].append(e[0].elapsed_time(e[1]))
+            per["js_bwd"].append(e[1].elapsed_time(e[2]))
+            continue
         per["fwd"].append(e[0].elapsed_time(e[1]))
         per["bwd_dk"].append(e[1].elapsed_time(e[2]))
         per["bwd_dq"].append(e[2].elapsed_time(e[3]))
@@ -312,16 +339,17 @@ def main():
         kern[k] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
                    "frac_of_bf16_peak": round(fl / ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4)}
     P = pairs if pairs is not None else w.pairs_per_head() * B * H
-    # algorithmic work of the step: the two logit products once, then dQ_s and dK_s
-    fwd_fl, bwd_fl = 2.0 * P * (w.d_t + w.d_s), 2.0 * P * (w.d_t + 3 * w.d_s)
-    fwd_ms = kern["fwd"]["ms"]
-    bwd_ms = kern["bwd_dk"]["ms"] + kern["bwd_dq"]["ms"]
+    # algorithmic work of the step: the two logit products once (JS: twice, a streaming JS needs both
+    # log-sum-exps before its pass), then dQ_s and dK_s
+    fwd_fl, bwd_fl = (4.0 if js else 2.0) * P * (w.d_t + w.d_s), 2.0 * P * (w.d_t + 3 * w.d_s)
+    fwd_ms = kern["js_fwd" if js else "fwd"]["ms"]
+    bwd_ms = kern["js_bwd"]["ms"] if js else kern["bwd_dk"]["ms"] + kern["bwd_dq"]["ms"]
     dominant = max(kern, key=lambda k: kern[k]["ms"])
     dom_fl = kernel_flops(w, dominant, pairs)
     achieved = dom_fl / kern[dominant]["ms"] / 1e9
     roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": MI355X_PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(dominant, w.name) if (hk_s == H and not seg) else None}
+            "traffic": load_traffic(dominant, w.name) if (hk_s == H and not seg and not js) else None}
     value = (fwd_fl + bwd_fl) / step_ms / 1e9
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -329,9 +357,9 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded N(0,1) bf16 inputs of the workload's shape)",
         "config": {"workload": w.name + (f"-hks{hk_s}" if hk_s != H else "") + (
-                       f"-packed{len(seg and lens)}seg" if seg else ""), "B": B, "H": H, "N_Q": w.Nq,
-                   "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s, "causal": w.causal, "teacher_grads": False,
-                   "student_key_heads": hk_s},
+                       f"-packed{len(seg and lens)}seg" if seg else "") + ("-js" if js else ""), "B": B, "H": H,
+                   "N_Q": w.Nq, "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s, "causal": w.causal, "teacher_grads": False,
+                   "student_key_heads": hk_s, "divergence": args.divergence},
         "fwd_ms": fwd_ms, "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_fl / fwd_ms / 1e9, 2), "bwd_tflops": round(bwd_fl / bwd_ms / 1e9, 2),
         "fwd_frac_of_bf16_peak": round(fwd_fl / fwd_ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4),
@@ -341,8 +369,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_autograd:
-        out["autograd"] = autograd_step(w, qt, kt, qs, ks, g, step_ms, seg=seg)
-    if not args.no_cpu_baseline and not seg:  # the CPU sample is of the dense workload's rows
+        out["autograd"] = autograd_step(w, qt, kt, qs, ks, g, step_ms, seg=seg, direction=args.divergence)
+    if not args.no_cpu_baseline and not seg and not js:  # the CPU sample is of the dense KL workload's rows
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)
 

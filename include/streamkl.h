@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10200 /* 1.2.0: packed variable-length batches (1.1.0: key heads per side) */
+#define STREAMKL_VERSION 10300 /* 1.3.0: Jensen-Shannon; 1.2.0: packed batches; 1.1.0: key heads */
 
 typedef enum {
   STREAMKL_FP32 = 0, /* inputs float32; products on fp32 MFMA                */
@@ -138,6 +138,27 @@ int streamkl_bwd_dk(const streamkl_problem_t* p,
                     const void* q_t, const void* k_t, const void* q_s, const void* k_s,
                     const float* lse_t, const float* lse_s, const float* g,
                     float* dk_s, void* hip_stream);
+
+/* Jensen-Shannon divergence of the same two rows (the pages name only KL, S1; this
+ * is its symmetric, bounded relative):
+ *   M = (P_t + P_s) / 2,   JS_i = KL(P_t || M)_i / 2 + KL(P_s || M)_i / 2   (natural log, 0 <= JS <= ln 2)
+ * streamkl_js_fwd: writes js = JS_i, lse_t, lse_s (as streamkl_fwd) and js_t =
+ * KL(P_t || M)_i, all float32 in the layout of kl.  Two launches on hip_stream: the
+ * KL forward (its KL goes to js first), then a second pass over the keys.        */
+int streamkl_js_fwd(const streamkl_problem_t* p,
+                    const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                    float* js, float* lse_t, float* lse_s, float* js_t,
+                    void* hip_stream);
+
+/* Gradients of sum_i g_i JS_i.  Needs streamkl_js_fwd's lse_t, lse_s, js and js_t;
+ * the gradient pairs follow the rules of streamkl_bwd:
+ *   dS_t = g_i P_t (log(P_t/M) - KL(P_t || M)_i) / 2,   dS_s = g_i P_s (log(P_s/M) - KL(P_s || M)_i) / 2,
+ * then dQ, dK as for the KL backward.                                            */
+int streamkl_js_bwd(const streamkl_problem_t* p,
+                    const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                    const float* lse_t, const float* lse_s, const float* js, const float* js_t,
+                    const float* g, float* dq_s, float* dk_s, float* dq_t, float* dk_t,
+                    void* hip_stream);
 
 /* Human-readable name of a status code (static storage; never NULL).            */
 const char* streamkl_status_string(int status);

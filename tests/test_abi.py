@@ -13,7 +13,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     declared = S.declared_symbols()
-    assert {"streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_status_string",
+    assert {"streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_js_fwd", "streamkl_js_bwd",
+            "streamkl_status_string",
             "streamkl_version"} <= set(declared)
     L = S.lib()
     for name in declared:
@@ -21,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared) <= exported
-    assert S.version() == 10200
+    assert S.version() == 10300
 
 
 def test_status_strings():
@@ -198,3 +199,23 @@ def test_python_binding_describes_a_packed_batch():
         S.make_problem(q, k, q, k, True, cu_seqlens_q=cu_q.long(), cu_seqlens_k=cu_k)
     with pytest.raises(ValueError):  # packed inputs are [N, heads, d]
         S.make_problem(q[None], k[None], q[None], k[None], True, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+
+
+def test_js_argument_rules():
+    L = S.lib()
+    p = _problem()
+    outs = [A + 0x4000, A + 0x5000, A + 0x6000, A + 0x7000]  # js, lse_t, lse_s, js_t
+    assert L.streamkl_js_fwd(ctypes.byref(p), *PTRS, *outs[:3], None, None) == S.ERR_INVALID  # js_t missing
+    assert L.streamkl_js_fwd(ctypes.byref(p), *PTRS, outs[0] + 2, *outs[1:], None) == S.ERR_UNSUPPORTED
+    assert L.streamkl_js_fwd(ctypes.byref(_problem(B=0)), *([0] * 8), None) == S.OK
+    st = [A + 0x8000, A + 0x9000, A + 0xA000, A + 0xB000, A + 0xC000]  # lse_t, lse_s, js, js_t, g
+    pair_s, pair_t = [A + 0xD000, A + 0xE000], [A + 0xF000, A + 0x10000]
+    assert L.streamkl_js_bwd(ctypes.byref(p), *PTRS, *st, None, None, None, None, None) == S.ERR_INVALID  # nothing asked
+    assert L.streamkl_js_bwd(ctypes.byref(p), *PTRS, *st, pair_s[0], None, None, None, None) == S.ERR_INVALID  # half pair
+    assert L.streamkl_js_bwd(ctypes.byref(p), *PTRS, st[0], st[1], None, st[3], st[4], *pair_s, None, None,
+                             None) == S.ERR_INVALID  # js missing
+    assert L.streamkl_js_bwd(ctypes.byref(p), *PTRS, st[0], st[1], st[2], None, st[4], None, None, *pair_t,
+                             None) == S.ERR_INVALID  # js_t missing
+    assert L.streamkl_js_bwd(ctypes.byref(p), *PTRS, *st[:4], None, *pair_s, None, None, None) == S.ERR_INVALID  # g
+    assert L.streamkl_js_bwd(ctypes.byref(_problem(d_t=96)), *PTRS, *st, *pair_s, None, None, None) == \
+        S.ERR_UNSUPPORTED

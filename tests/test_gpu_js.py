@@ -1,0 +1,143 @@
+"""GPU parity of the Jensen-Shannon kernels (streamkl_js_fwd / streamkl_js_bwd) against the float64
+oracle's js_forward / js_backward, with the tolerances and criteria of the KL parity tests.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_kl_amd import loss as L
+from attention_kl_amd import streamkl as S
+from attention_kl_amd import workloads as wl
+
+from parity import device_inputs, grad_floor, ratio_kl, ratio_lse, ratio_rows, report, rtol_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, teacher, g=None):
+    print(f"case {w.name} js teacher={teacher}", flush=True)
+    dev_in, host = device_inputs(w)
+    qt, kt, qs, ks = dev_in
+    g = wl.full_g(w) if g is None else g
+    js, lt, ls, ht = S.js_fwd(qt, kt, qs, ks, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    grads = S.js_bwd(qt, kt, qs, ks, lt, ls, js, ht, torch.from_numpy(g).cuda(), causal=w.causal,
+                     teacher_grads=teacher, scale_t=w.scale_t, scale_s=w.scale_s)
+    torch.cuda.synchronize()
+    h64 = [a.astype(np.float64) for a in host]
+    rjs, rht, _, rlt, rls = oracle.js_forward(*h64, w.scale_t, w.scale_s, w.causal)
+    rg = oracle.js_backward(*h64, w.scale_t, w.scale_s, w.causal, g.astype(np.float64), teacher=teacher)
+    rt = rtol_of(w)
+    ag = np.abs(g)
+    c = lambda x: x.cpu().numpy()
+    r = dict(js=ratio_kl(c(js), rjs, rt), js_t=ratio_kl(c(ht), rht, rt), lse_t=ratio_lse(c(lt), rlt, rt),
+             lse_s=ratio_lse(c(ls), rls, rt),
+             dq_s=ratio_rows(c(grads[0]), rg["dq_s"], rt, grad_floor(0.5 * w.scale_s, ag, h64[3])),
+             dk_s=ratio_rows(c(grads[1]), rg["dk_s"], rt, grad_floor(0.5 * w.scale_s, ag, h64[2])))
+    if teacher:
+        r.update(dq_t=ratio_rows(c(grads[2]), rg["dq_t"], rt, grad_floor(0.5 * w.scale_t, ag, h64[1])),
+                 dk_t=ratio_rows(c(grads[3]), rg["dk_t"], rt, grad_floor(0.5 * w.scale_t, ag, h64[0])))
+    msg = report(w.name + " js", **r)
+    print(msg, flush=True)
+    assert max(r.values()) <= 1.0, msg
+    jsv = c(js)
+    assert np.all(jsv >= -1e-6) and np.all(jsv <= math.log(2.0) + 1e-6)
+
+
+CASES = [
+    wl.custom(1, 2, 129, 129, 128, 128, True, seed=51),
+    wl.custom(1, 1, 3, 3, 64, 64, True, seed=52),
+    wl.custom(2, 1, 200, 257, 128, 64, True, recipe="independent", seed=53),
+    wl.custom(1, 2, 70, 300, 64, 128, False, recipe="independent", seed=54),
+    wl.custom(1, 2, 255, 255, 128, 128, True, sigma=0.1, seed=55),          # nearly equal rows: small JS
+    wl.custom(1, 1, 200, 200, 128, 128, True, recipe="independent", peak_frac=0.02, peak_scale=4.0, seed=56),
+    wl.custom(1, 2, 100, 100, 64, 64, True, dtype="fp32", recipe="independent", seed=57),
+    wl.custom(1, 1, 33, 90, 128, 64, False, dtype="fp32", recipe="independent", seed=58),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_js_matches_the_oracle(w):
+    _check(w, teacher=True)
+
+
+def test_js_signed_row_weights():
+    w = wl.custom(1, 2, 160, 160, 128, 128, True, recipe="independent", seed=59)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 7])))
+    g = rng.standard_normal((w.B, w.H, w.Nq)).astype(np.float32)
+    g[..., ::5] = 0.0
+    _check(w, teacher=True, g=g)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_rows_give_exact_zeros(causal):
+    w = wl.custom(1, 2, 150, 150, 128, 128, causal, recipe="same", seed=60)
+    print(f"case {w.name} js same", flush=True)
+    dev_in, _ = device_inputs(w)
+    js, lt, ls, ht = S.js_fwd(*dev_in, causal=causal)
+    grads = S.js_bwd(*dev_in, lt, ls, js, ht, torch.ones_like(js), causal=causal, teacher_grads=True)
+    torch.cuda.synchronize()
+    assert torch.all(js == 0.0) and torch.all(ht == 0.0)
+    for x in grads:
+        assert torch.all(x == 0.0)
+
+
+def test_js_on_packed_and_grouped_inputs():
+    """One packed batch with grouped student keys, each segment against the oracle on its own."""
+    H, hk_s = 4, 2
+    lens = [90, 1, 257]
+    segs = [wl.custom(1, H, n, n, 128, 128, True, recipe="independent", seed=61 + i) for i, n in enumerate(lens)]
+    print(f"case packed js {lens} hk_s={hk_s}", flush=True)
+    hosts = [[a.astype(np.float64) for a in wl.full_f32(w)] for w in segs]
+    for h in hosts:
+        h[3] = h[3][:, ::H // hk_s]
+
+    def pack(i):
+        cat = np.concatenate([h[i][0] for h in hosts], axis=1)  # [heads, N, d]
+        return torch.from_numpy(np.ascontiguousarray(cat.transpose(1, 0, 2))).float().to(torch.bfloat16).cuda()
+    qt, kt, qs, ks = (pack(i) for i in range(4))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32).cuda()
+    seg = dict(cu_seqlens_q=cu, cu_seqlens_k=cu)
+    js, lt, ls, ht = S.js_fwd(qt, kt, qs, ks, causal=True, **seg)
+    g = torch.from_numpy(np.concatenate([wl.full_g(w)[0] for w in segs], axis=1)).cuda()
+    dq, dk, _, _ = S.js_bwd(qt, kt, qs, ks, lt, ls, js, ht, g, causal=True, **seg)
+    torch.cuda.synchronize()
+    js, dq, dk = js.cpu().numpy(), dq.cpu().numpy(), dk.cpu().numpy()
+    q0 = 0
+    worst = {}
+    for w, h, n in zip(segs, hosts, lens):
+        eks = np.repeat(h[3], H // hk_s, axis=1)
+        rjs = oracle.js_forward(h[0], h[1], h[2], eks, w.scale_t, w.scale_s, True)[0]
+        gw = wl.full_g(w)
+        rg = oracle.js_backward(h[0], h[1], h[2], eks, w.scale_t, w.scale_s, True, gw)
+        rdk = rg["dk_s"].reshape(1, hk_s, H // hk_s, n, -1).sum(axis=2)
+        r = dict(js=ratio_kl(js[None, :, q0:q0 + n], rjs, 2e-3),
+                 dq=ratio_rows(dq[None, :, q0:q0 + n], rg["dq_s"], 2e-3, grad_floor(0.5 * w.scale_s, gw, eks)),
+                 dk=ratio_rows(dk[None, :, q0:q0 + n], rdk, 2e-3, grad_floor(0.5 * w.scale_s, gw, h[2])))
+        for k, v in r.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+        q0 += n
+    msg = report("packed js", **worst)
+    print(msg, flush=True)
+    assert max(worst.values()) <= 1.0, msg
+
+
+def test_autograd_js_direction():
+    w = wl.custom(1, 2, 96, 96, 128, 128, True, recipe="independent", seed=65)
+    print(f"case {w.name} autograd js", flush=True)
+    dev_in, host = device_inputs(w)
+    ins = [x.clone().requires_grad_(True) for x in dev_in]
+    out = L.attention_kl(*ins, causal=True, scale_t=w.scale_t, scale_s=w.scale_s, direction="js", reduction="sum")
+    out.backward()
+    torch.cuda.synchronize()
+    h64 = [a.astype(np.float64) for a in host]
+    rjs = oracle.js_forward(*h64, w.scale_t, w.scale_s, True)[0]
+    ones = np.ones((w.B, w.H, w.Nq))
+    rg = oracle.js_backward(*h64, w.scale_t, w.scale_s, True, ones, teacher=True)
+    assert abs(out.item() - rjs.sum()) <= 2e-3 * abs(rjs.sum())
+    rt = 2e-3 + 2.0 ** -9  # bf16 gradients
+    for x, name, other, sc in ((ins[0], "dq_t", h64[1], w.scale_t), (ins[1], "dk_t", h64[0], w.scale_t),
+                               (ins[2], "dq_s", h64[3], w.scale_s), (ins[3], "dk_s", h64[2], w.scale_s)):
+        assert ratio_rows(x.grad.float().cpu().numpy(), rg[name], rt, grad_floor(0.5 * sc, ones, other)) <= 1.0, name

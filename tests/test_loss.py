@@ -42,10 +42,31 @@ def _fake_bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal, kl=None, teacher_grads
             t.get("dq_t") if teacher_grads else None, t.get("dk_t") if teacher_grads else None)
 
 
+def _fake_js_fwd(qt, kt, qs, ks, *, causal, scale_t=None, scale_s=None, out=None, stream=None):
+    st = 1.0 / math.sqrt(qt.shape[-1]) if scale_t is None else scale_t
+    ss = 1.0 / math.sqrt(qs.shape[-1]) if scale_s is None else scale_s
+    js, ht, _, lt, ls = oracle.js_forward(_np(qt), _np(kt), _np(qs), _np(ks), st, ss, causal)
+    return tuple(torch.from_numpy(x) for x in (js, lt, ls, ht))
+
+
+def _fake_js_bwd(qt, kt, qs, ks, lse_t, lse_s, js, js_t, g, *, causal, teacher_grads=False, student_grads=True,
+                 scale_t=None, scale_s=None, out=None, stream=None):
+    CALLS.append(dict(teacher=teacher_grads, student=student_grads, g_dtype=g.dtype, g_contig=g.is_contiguous(),
+                      kl_given=True))
+    st = 1.0 / math.sqrt(qt.shape[-1]) if scale_t is None else scale_t
+    ss = 1.0 / math.sqrt(qs.shape[-1]) if scale_s is None else scale_s
+    r = oracle.js_backward(_np(qt), _np(kt), _np(qs), _np(ks), st, ss, causal, _np(g), teacher=teacher_grads)
+    t = {k: torch.from_numpy(v) for k, v in r.items()}
+    return (t["dq_s"] if student_grads else None, t["dk_s"] if student_grads else None,
+            t.get("dq_t") if teacher_grads else None, t.get("dk_t") if teacher_grads else None)
+
+
 @pytest.fixture
 def fake_backend(monkeypatch):
     monkeypatch.setattr(S, "fwd", _fake_fwd)
     monkeypatch.setattr(S, "bwd", _fake_bwd)
+    monkeypatch.setattr(S, "js_fwd", _fake_js_fwd)
+    monkeypatch.setattr(S, "js_bwd", _fake_js_bwd)
     CALLS.clear()
     yield
 
@@ -64,8 +85,11 @@ def _ref_kl(qt, kt, qs, ks, causal, direction):
         a = a.masked_fill(~allowed, -1e9)
         b = b.masked_fill(~allowed, -1e9)
         la, lb = torch.log_softmax(a, -1), torch.log_softmax(b, -1)
+        if direction == "js":  # masked entries have P = 0 exactly and finite logs, so they add 0
+            lm = torch.logaddexp(la, lb) - math.log(2.0)
+            return 0.5 * (la.exp() * (la - lm)).sum(-1) + 0.5 * (lb.exp() * (lb - lm)).sum(-1)
         return (la.exp() * (la - lb)).sum(-1)
-    if direction == "forward":
+    if direction in ("forward", "js"):
         return one(qt, kt, qs, ks)
     if direction == "reverse":
         return one(qs, ks, qt, kt)
@@ -133,7 +157,7 @@ def test_gradients_come_back_in_the_input_dtype(fake_backend):
 def test_bad_arguments_are_rejected_before_any_call(fake_backend):
     qt, kt, qs, ks = _inputs(3, False)
     with pytest.raises(ValueError):
-        L.attention_kl(qt, kt, qs, ks, direction="js")
+        L.attention_kl(qt, kt, qs, ks, direction="total_variation")
     with pytest.raises(ValueError):
         L.attention_kl(qt, kt, qs, ks, reduction="max")
     assert CALLS == []
