@@ -27,6 +27,7 @@
 
 #include "skl_device.hpp"
 #include "skl_kernels.hpp"
+#include <type_traits>
 
 namespace skl {
 
@@ -86,6 +87,41 @@ __device__ __forceinline__ void online_update(RowState& s, const f32x16& st, con
   s.l_t = fmaf(s.l_t, al_t, pt);
   s.l_s = fmaf(s.l_s, al_s, ps);
   s.acc = fmaf(s.acc, al_t, pa);
+}
+
+// The same sums against a power-of-two reference instead of the running maximum: m_t, m_s hold
+// integers, every exponent is taken relative to them, and every third tile ref_renorm moves the
+// binary exponent of l into m (exact: a power-of-two scaling of l and acc).  No per-element maximum
+// and no per-tile rescaling exps are needed.  It stays finite as long as no logit (log2 units)
+// exceeds the reference by ~120, and keeps full precision unless a sum falls near the denormals;
+// the kernel checks both at the end and reruns the tile loop with online_update when either fails.
+__device__ __forceinline__ void ref_update(RowState& s, const f32x16& st, const f32x16& ss, const float* dif, float c_t,
+                                           float c_s) {
+  float pt = fast_exp2(fmaf(st[0], c_t, -s.m_t));
+  float ps = fast_exp2(fmaf(ss[0], c_s, -s.m_s));
+  float pa = pt * dif[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    const float e = fast_exp2(fmaf(st[i], c_t, -s.m_t));
+    const float f = fast_exp2(fmaf(ss[i], c_s, -s.m_s));
+    pt += e;
+    ps += f;
+    pa = fmaf(e, dif[i], pa);
+  }
+  s.l_t += pt;
+  s.l_s += ps;
+  s.acc += pa;
+}
+
+// l = l' 2^e with l' in [0.5, 1): m += e (0 sums keep e = 0); emin tracks the smallest e seen.
+__device__ __forceinline__ void ref_renorm(RowState& s, int& emin) {
+  const int et = __builtin_amdgcn_frexp_expf(s.l_t), es = __builtin_amdgcn_frexp_expf(s.l_s);
+  s.l_t = __builtin_amdgcn_ldexpf(s.l_t, -et);
+  s.acc = __builtin_amdgcn_ldexpf(s.acc, -et);
+  s.l_s = __builtin_amdgcn_ldexpf(s.l_s, -es);
+  s.m_t += (float)et;
+  s.m_s += (float)es;
+  emin = min(emin, min(et, es));
 }
 
 // Jensen-Shannon pass (second pass over the keys, with both log-sum-exps known from the KL
@@ -159,6 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   load_row_regs<T, DT>(qt_r, qt + (int64_t)qrow * a.sqt[2], qrow < nq, hf);
   load_row_regs<T, DS>(qs_r, qs + (int64_t)qrow * a.sqs[2], qrow < nq, hf);
 
+  constexpr int KL_FAST = 0, KL_EXACT = 1, JS_PASS = 2;  // modes of the tile loop
   RowState rs{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
   JsState js{0.f, 0.f};
   auto stat_index = [&]() -> int64_t { return ((int64_t)sg.bs * a.H + h) * a.Nq + sg.q0 + qrow; };  // row statistics
@@ -192,70 +229,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   swz_operand_offsets<RBT, NCT / 2>(off_t, r32, hf);
   swz_operand_offsets<RBS, NCS / 2>(off_s, r32, hf);
 
-  // The compiler cannot see the DMAs in the hardware's vmcnt; retire every load of its own now,
-  // so that none of its waits lands inside the loop, where it would also drain the DMA ring.
-  wait_vmcnt<0>();
-  issue(0, 0);
-  issue(1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
-  // One step per tile; the loop is unrolled by the ring depth so every LDS address is a
-  // per-lane base plus an immediate.  The tile count is rounded up to a multiple of the ring
-  // depth: the extra tiles lie past every row's last key, so they are fully masked and leave the
-  // state unchanged, and the unrolled body needs no guard (whose join would copy the state).
-  const int ntiles_pad = (ntiles + NBUF - 1) / NBUF * NBUF;
-  for (int t0 = 0; t0 < ntiles_pad; t0 += NBUF) {
+  // The tile loop, for one mode: KL_FAST (ref_update), KL_EXACT (online_update) or JS_PASS.
+  int emin = 0;
+  auto tile_loop = [&](auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    // The compiler cannot see the DMAs in the hardware's vmcnt; retire every load of its own now,
+    // so that none of its waits lands inside the loop, where it would also drain the DMA ring.
+    wait_vmcnt<0>();
+    issue(0, 0);
+    issue(1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
+    // One step per tile; the loop is unrolled by the ring depth so every LDS address is a
+    // per-lane base plus an immediate.  The tile count is rounded up to a multiple of the ring
+    // depth: the extra tiles lie past every row's last key, so they are fully masked and leave the
+    // state unchanged, and the unrolled body needs no guard (whose join would copy the state).
+    const int ntiles_pad = (ntiles + NBUF - 1) / NBUF * NBUF;
+    for (int t0 = 0; t0 < ntiles_pad; t0 += NBUF) {
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int t = t0 + u;
-      {
-        wait_vmcnt<NI>();  // tile t has landed (tile t+1 may still be in flight)
-        __syncthreads();   // ... for every wave; and every wave is done with tile t-1
-        issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
-        const char* tile = slot_ptr(u);
-        const int kb = t * BK;
-        f32x16 st = {}, ss = {};
-        tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
-        tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
-        float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
-        if constexpr (!JS) {
+      for (int u = 0; u < NBUF; ++u) {
+        const int t = t0 + u;
+        {
+          wait_vmcnt<NI>();  // tile t has landed (tile t+1 may still be in flight)
+          __syncthreads();   // ... for every wave; and every wave is done with tile t-1
+          issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
+          const char* tile = slot_ptr(u);
+          const int kb = t * BK;
+          f32x16 st = {}, ss = {};
+          tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
+          tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
+          float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
+          if constexpr (!JS) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            dif[i] = fmaf(ss[i], -a.ratio, st[i]);
-            // pin dif here, ahead of the masking branch: then no unmasked logit outlives the branch
-            // and the masking below rewrites st/ss in place instead of copying them on every tile
-            asm volatile("" : "+v"(dif[i]));
+            for (int i = 0; i < 16; ++i) {
+              dif[i] = fmaf(ss[i], -a.ratio, st[i]);
+              // pin dif here, ahead of the masking branch: then no unmasked logit outlives the branch
+              // and the masking below rewrites st/ss in place instead of copying them on every tile
+              asm volatile("" : "+v"(dif[i]));
+            }
           }
-        }
-        // A tile that no row of this wavefront reaches (causal) goes through the masked path too:
-        // with every key at -inf the update leaves the state bit for bit unchanged, and the loop
-        // keeps one definition of the state (no copies at a join).  Such tiles are under 1% of
-        // a causal problem's.
-        const bool full = t < ntiles && kb + 31 < nk && (!CAUSAL || kb + 31 <= q0w + off);
-        if (!full) {  // in place, so the update below has one copy of its state
-          asm volatile("");  // keep this a branch: the compiler would otherwise select on every tile
+          // A tile that no row of this wavefront reaches (causal) goes through the masked path too:
+          // with every key at -inf the update leaves the state bit for bit unchanged, and the loop
+          // keeps one definition of the state (no copies at a join).  Such tiles are under 1% of
+          // a causal problem's.
+          const bool full = t < ntiles && kb + 31 < nk && (!CAUSAL || kb + 31 <= q0w + off);
+          if (!full) {  // in place, so the update below has one copy of its state
+            asm volatile("");  // keep this a branch: the compiler would otherwise select on every tile
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + acc_row(i, hf);
-            const bool ok = key < nk && (!CAUSAL || key <= qrow + off);
-            // JS: a large finite logit instead of -inf gives P_t = P_s = 0 with a finite r, so
-            // the term is an exact zero rather than 0 * NaN
-            st[i] = ok ? st[i] : (JS ? -1e30f : -INFINITY);
-            ss[i] = ok ? ss[i] : (JS ? -1e30f : -INFINITY);
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb + acc_row(i, hf);
+              const bool ok = key < nk && (!CAUSAL || key <= qrow + off);
+              // JS: a large finite logit instead of -inf gives P_t = P_s = 0 with a finite r, so
+              // the term is an exact zero rather than 0 * NaN
+              st[i] = ok ? st[i] : (JS ? -1e30f : -INFINITY);
+              ss[i] = ok ? ss[i] : (JS ? -1e30f : -INFINITY);
+            }
           }
-        }
-        if constexpr (JS) {
-          js_update(js, st, ss, js_lt, js_ls, a.c_t, a.c_s);
-          asm volatile("" ::"v"(js.at), "v"(js.as));
-        } else {
-          online_update(rs, st, ss, dif, a.c_t, a.c_s);
-          // the new state exists before the next barrier: keeps each tile's update in its own step
-          asm volatile("" ::"v"(rs.m_t), "v"(rs.m_s), "v"(rs.l_t), "v"(rs.l_s), "v"(rs.acc));
+          if constexpr (MODE == JS_PASS) {
+            js_update(js, st, ss, js_lt, js_ls, a.c_t, a.c_s);
+            asm volatile("" ::"v"(js.at), "v"(js.as));
+          } else {
+            if constexpr (MODE == KL_FAST) {
+              ref_update(rs, st, ss, dif, a.c_t, a.c_s);
+              if (u == NBUF - 1) ref_renorm(rs, emin);
+            } else {
+              online_update(rs, st, ss, dif, a.c_t, a.c_s);
+            }
+            // the new state exists before the next barrier: keeps each tile's update in its own step
+            asm volatile("" ::"v"(rs.m_t), "v"(rs.m_s), "v"(rs.l_t), "v"(rs.l_s), "v"(rs.acc));
+          }
         }
       }
     }
-  }
-  wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS when it exits
+    wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS when it exits (or is refilled)
+  };
 
   if constexpr (JS) {
+    tile_loop(std::integral_constant<int, JS_PASS>{});
     const float at = js.at + __shfl_xor(js.at, 32), as = js.as + __shfl_xor(js.as, 32);
     if (hf == 0 && qrow < nq) {
       a.kl[stat_index()] = 0.5f * kLn2 * (at + as);
@@ -264,15 +312,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     return;
   }
 
-  // Merge the two half-row states (disjoint key subsets) of each query row.
-  const float o_mt = __shfl_xor(rs.m_t, 32), o_lt = __shfl_xor(rs.l_t, 32), o_acc = __shfl_xor(rs.acc, 32);
-  const float o_ms = __shfl_xor(rs.m_s, 32), o_ls = __shfl_xor(rs.l_s, 32);
-  const float Mt = fmaxf(rs.m_t, o_mt), Ms = fmaxf(rs.m_s, o_ms);
-  const float f1 = fast_exp2(rs.m_t - Mt), f2 = fast_exp2(o_mt - Mt);
-  const float g1 = fast_exp2(rs.m_s - Ms), g2 = fast_exp2(o_ms - Ms);
-  const float Lt = rs.l_t * f1 + o_lt * f2;
-  const float Ls = rs.l_s * g1 + o_ls * g2;
-  const float A = rs.acc * f1 + o_acc * f2;
+  // Merge the two half-row states (disjoint key subsets) of each query row; the references m are
+  // running maxima or powers of two, the merge is the same.
+  float Mt, Ms, Lt, Ls, A;
+  auto merge = [&]() {
+    const float o_mt = __shfl_xor(rs.m_t, 32), o_lt = __shfl_xor(rs.l_t, 32), o_acc = __shfl_xor(rs.acc, 32);
+    const float o_ms = __shfl_xor(rs.m_s, 32), o_ls = __shfl_xor(rs.l_s, 32);
+    Mt = fmaxf(rs.m_t, o_mt);
+    Ms = fmaxf(rs.m_s, o_ms);
+    const float f1 = fast_exp2(rs.m_t - Mt), f2 = fast_exp2(o_mt - Mt);
+    const float g1 = fast_exp2(rs.m_s - Ms), g2 = fast_exp2(o_ms - Ms);
+    Lt = rs.l_t * f1 + o_lt * f2;
+    Ls = rs.l_s * g1 + o_ls * g2;
+    A = rs.acc * f1 + o_acc * f2;
+  };
+  rs = RowState{0.f, 0.f, 0.f, 0.f, 0.f};  // power-of-two references start at 2^0
+  tile_loop(std::integral_constant<int, KL_FAST>{});
+  merge();
+  // A row whose sums left the safe range (an overflow, or a sum that came near the denormals) is
+  // redone by the whole workgroup with running maxima; realistic logits never get there.
+  const bool risky = !(__builtin_isfinite(Lt) && __builtin_isfinite(Ls) && __builtin_isfinite(A)) || emin < -100 ||
+                     (qrow < nq && (Lt == 0.f || Ls == 0.f));
+  if (__syncthreads_or(risky)) {
+    rs = RowState{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
+    tile_loop(std::integral_constant<int, KL_EXACT>{});
+    merge();
+  }
 
   if (hf == 0 && qrow < nq) {
     // true divisions: Ls / Lt is exactly 1 when the two states are bitwise equal

@@ -5,6 +5,8 @@ full-size workloads run in the same launch configuration the bench times and are
 compared on sampled rows / keys that the oracle computes one by one, plus
 properties that hold at any size.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -244,5 +246,62 @@ def test_signed_and_zero_row_weights(w):
                                ("dq_t", grads[2], h64[1], w.scale_t), ("dk_t", grads[3], h64[0], w.scale_t)):
         r[name] = ratio_rows(x.cpu().numpy(), rg[name], rt, grad_floor(sc, ag, other))
     msg = report(w.name + " signed g", **r)
+    print(msg, flush=True)
+    assert max(r.values()) <= 1.0, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["overflow", "underflow"])
+def test_extreme_logits_take_the_exact_path(dtype, kind):
+    """Rows whose logits leave the range of the forward's power-of-two references: logits of several
+    hundred nats (unit scale, inputs of scale 4) overflow a sum taken against 2^0, and rows whose every
+    logit is near -1000 (queries opposite to clustered keys) underflow it.  The kernel must notice
+    and redo the workgroup with running maxima; the oracle works in float64 at any magnitude.  The
+    gradients are compared for the overflow rows only: in the underflow construction the keys cluster
+    around one direction u and sum_j dS_ij = 0, so dQ = sum_j dS_ij k_j cancels the u component about
+    twentyfold, which magnifies the float32 rounding of the recomputed logits (of order L sqrt(d) 2^-24
+    at |logit| L ~ 640) past the tolerance; that is a property of float32 at these magnitudes, not of
+    the forward under test."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([71, kind == "overflow", dtype == "fp32"])))
+    B, H, N, d = 1, 2, 160, 64
+    if kind == "overflow":
+        arrs = [4.0 * rng.standard_normal((B, H, N, d)) for _ in range(4)]
+    else:
+        u = rng.standard_normal((B, H, 1, d))
+        k = u + 0.05 * rng.standard_normal((B, H, N, d))
+        q = -10.0 * u + 0.05 * rng.standard_normal((B, H, N, d))
+        q[:, :, ::3] = rng.standard_normal((B, H, (N + 2) // 3, d))  # ordinary rows in the same workgroups
+        arrs = [q, k, q + 0.1 * rng.standard_normal((B, H, N, d)), k]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = [torch.from_numpy(a.astype(np.float32)).cuda().to(tdt) for a in arrs]
+    host = [x.float().cpu().numpy().astype(np.float64) for x in dev]  # the values the kernels see
+    print(f"case extreme logits {kind} {dtype}", flush=True)
+    kl, lt, ls = S.fwd(*dev, causal=True, scale_t=1.0, scale_s=1.0)
+    g = torch.ones_like(kl)
+    dq, dk, _, _ = S.bwd(*dev, lt, ls, g, causal=True, scale_t=1.0, scale_s=1.0)
+    torch.cuda.synchronize()
+    rkl, rlt, rls = oracle.forward(*host, 1.0, 1.0, True)
+    rg = oracle.backward(*host, 1.0, 1.0, True, np.ones((B, H, N)))
+    rt = {"bf16": 2e-3, "fp32": 1e-5}[dtype]
+    # float32 limit at these magnitudes: every logit is a float32 sum of d products whose partial sums
+    # reach L = max |logit|, so it carries an absolute rounding error of order L sqrt(d) 2^-24 (the
+    # fp32 products accumulate in d/2 steps).  KL, a P-weighted difference of two logits, inherits
+    # that absolute error (bounded here by 4 L sqrt(d) 2^-24), and P = exp(a - LSE) with the
+    # gradients the relative one; both are added to the usual criteria.
+    L = max(float(np.abs(host[0] @ host[1].transpose(0, 1, 3, 2)).max()),
+            float(np.abs(host[2] @ host[3].transpose(0, 1, 3, 2)).max()))
+    kl_abs = 4.0 * L * math.sqrt(d) * 2.0 ** -24
+    rt_g = max(rt, L * math.sqrt(d) * 2.0 ** -22)
+    c = lambda x: x.cpu().numpy()
+    assert np.all(np.isfinite(c(kl))) and np.all(np.isfinite(c(lt))) and np.all(np.isfinite(c(ls)))
+    rms = np.maximum(np.sqrt((rkl ** 2).mean(axis=-1, keepdims=True)), 1e-3)
+    kl_ratio = float((np.abs(c(kl) - rkl) / (rt * np.abs(rkl) + rt * rms + kl_abs)).max())
+    r = dict(kl=kl_ratio, lse_t=ratio_lse(c(lt), rlt, max(rt, rt_g)), lse_s=ratio_lse(c(ls), rls, max(rt, rt_g)))
+    if kind == "overflow":
+        r.update(dq=ratio_rows(c(dq), rg["dq_s"], rt_g, grad_floor(1.0, np.ones((B, H, N)), host[3])),
+                 dk=ratio_rows(c(dk), rg["dk_s"], rt_g, grad_floor(1.0, np.ones((B, H, N)), host[2])))
+    else:
+        assert np.all(np.isfinite(c(dq))) and np.all(np.isfinite(c(dk)))
+    msg = report(f"extreme {kind} {dtype}", **r)
     print(msg, flush=True)
     assert max(r.values()) <= 1.0, msg
