@@ -197,7 +197,7 @@ bwd_kernel(const BwdArgs a) {
   static_assert(SLOT % 256 == 0, "ring slots start on a 256-byte bank window");
   __shared__ __attribute__((aligned(1024))) char ring[NBUF][SLOT];
   // converted statistics (log2 units) of the streamed queries: per ring slot in the ping-pong (one
-  // wave of group 1 per statistic converts them a phase before use), per wave otherwise
+  // wave of group 0 per statistic converts them a phase before use), per wave otherwise
   constexpr bool CSLOT = !OWN_Q && NG == 2;
   __shared__ __attribute__((aligned(16))) float cst[CSLOT ? NBUF : 1][4][32];
   __shared__ int cst_neg[CSLOT ? NBUF : 1];  // per slot: some streamed query of the tile has g < 0
@@ -364,21 +364,21 @@ bwd_kernel(const BwdArgs a) {
     if constexpr (JS) return (TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32])) * kLog2e;
     return raw[192 + r32] + raw[r32] - raw[64 + r32];
   };
-  // Ping-pong: wave 4 + k of group 1 converts statistic k of the tile in slot u, in two halves around
-  // its vector phase: the LDS reads go out first and the converted value is stored at the end, so
-  // their latency hides behind the dS work instead of delaying this wave's barrier.  Both halves of
-  // the wave hold the same 32 rows and store the same values.
+  // Ping-pong: wave k of group 0 converts statistic k of tile s during its matrix phase of that tile
+  // (phase 2s: the tile landed before it, and the wave's VALU is idle while its MFMAs run); group 0
+  // reads the values in phase 2s+1, group 1 in phase 2s+2.  Both halves of the wave hold the same 32
+  // rows and store the same values.
   auto stats_load = [&](const char* sl) -> float {
     float v = 0.f;
     if constexpr (CSLOT) {
-      const int k = wave - 4;
+      const int k = wave;
       if (k < NSTAT) v = convert_one(k, reinterpret_cast<const float*>(sl + TILE));
     }
     return v;
   };
   auto stats_store = [&](int u, float v) {
     if constexpr (CSLOT) {
-      const int k = wave - 4;
+      const int k = wave;
       if (k < NSTAT) {
         cst[u][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
         if (k == 2) {
@@ -534,7 +534,6 @@ bwd_kernel(const BwdArgs a) {
       // the s = 0 gradient product, first receives a tile in phase 2.
       if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
         issue(PD, PD);
-        convert_stats(0, ring[0]);
         __syncthreads();
       }
       for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
@@ -545,17 +544,13 @@ bwd_kernel(const BwdArgs a) {
             // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
             if (grp == 0) issue(s + PD, (u + PD) % NBUF);
             matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
+            if (grp == 0) convert_stats(u, slot_ptr(u));  // tile s landed before this phase
             if (grp == 1) wait_tile();
             __syncthreads();
             // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
             if (s < ntile) {
-              float cv = 0.f;
-              if (grp == 1) {
-                issue(s + PD + 1, (u + PD + 1) % NBUF);
-                cv = stats_load(slot_ptr((u + 1) % NBUF));  // tile s+1 landed in the last phase
-              }
+              if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
               vector_phase(s, u, slot_ptr(u));
-              if (grp == 1) stats_store((u + 1) % NBUF, cv);
               if (grp == 0) wait_tile();
               __syncthreads();
             } else if (grp == 0) {
