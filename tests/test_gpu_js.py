@@ -141,3 +141,38 @@ def test_autograd_js_direction():
     for x, name, other, sc in ((ins[0], "dq_t", h64[1], w.scale_t), (ins[1], "dk_t", h64[0], w.scale_t),
                                (ins[2], "dq_s", h64[3], w.scale_s), (ins[3], "dk_s", h64[2], w.scale_s)):
         assert ratio_rows(x.grad.float().cpu().numpy(), rg[name], rt, grad_floor(0.5 * sc, ones, other)) <= 1.0, name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_js_grouped_keys_with_teacher_gradients(dtype):
+    """Grouped keys on both sides (teacher 2 key heads, student 1) with both gradient pairs: the
+    key-owner kernels make one pass per query head of the group; the oracle runs on keys expanded to
+    every query head, the expanded heads' dK summed per group."""
+    H, hk_t, hk_s = 4, 2, 1
+    w = wl.custom(1, H, 150, 150, 64, 64, True, dtype=dtype, recipe="independent", seed=66)
+    print(f"case {w.name} js hk_t={hk_t} hk_s={hk_s}", flush=True)
+    dev_in, host = device_inputs(w)
+    qt, kt, qs, ks = dev_in
+    kt, ks = kt[:, ::H // hk_t], ks[:, ::H // hk_s]
+    h64 = [a.astype(np.float64) for a in host]
+    ekt = np.repeat(h64[1][:, ::H // hk_t], H // hk_t, axis=1)
+    eks = np.repeat(h64[3][:, ::H // hk_s], H // hk_s, axis=1)
+    g = wl.full_g(w)
+    js, lt, ls, ht = S.js_fwd(qt, kt, qs, ks, causal=True)
+    grads = S.js_bwd(qt, kt, qs, ks, lt, ls, js, ht, torch.from_numpy(g).cuda(), causal=True, teacher_grads=True)
+    torch.cuda.synchronize()
+    rjs = oracle.js_forward(h64[0], ekt, h64[2], eks, w.scale_t, w.scale_s, True)[0]
+    rg = oracle.js_backward(h64[0], ekt, h64[2], eks, w.scale_t, w.scale_s, True, g, teacher=True)
+    rt = rtol_of(w)
+
+    def sumg(x, hk):
+        return x.reshape(1, hk, H // hk, w.Nk, -1).sum(axis=2)
+    c = lambda x: x.cpu().numpy()
+    r = dict(js=ratio_kl(c(js), rjs, rt),
+             dq_s=ratio_rows(c(grads[0]), rg["dq_s"], rt, grad_floor(0.5 * w.scale_s, g, eks)),
+             dk_s=ratio_rows(c(grads[1]), sumg(rg["dk_s"], hk_s), rt, grad_floor(0.5 * w.scale_s, g, h64[2])),
+             dq_t=ratio_rows(c(grads[2]), rg["dq_t"], rt, grad_floor(0.5 * w.scale_t, g, ekt)),
+             dk_t=ratio_rows(c(grads[3]), sumg(rg["dk_t"], hk_t), rt, grad_floor(0.5 * w.scale_t, g, h64[0])))
+    msg = report(f"js grouped {dtype}", **r)
+    print(msg, flush=True)
+    assert max(r.values()) <= 1.0, msg
