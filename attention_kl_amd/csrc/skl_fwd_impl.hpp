@@ -141,9 +141,9 @@ __device__ __forceinline__ void js_update(JsState& s, const f32x16& st, const f3
     const float x = fmaf(st[i], c_t, -lt), y = fmaf(ss[i], c_s, -ls);
     const float p = fast_exp2(x), q = fast_exp2(y);
     const float r = y - x;
-    const float w = 1.f - fast_log2(1.f + fast_exp2(-fabsf(r)));
-    at = fmaf(p, w - fmaxf(r, 0.f), at);
-    as = fmaf(q, w + fminf(r, 0.f), as);
+    const float lp = (1.f - fast_log2(1.f + fast_exp2(-fabsf(r)))) - fmaxf(r, 0.f);  // log2(P_t/M)
+    at = fmaf(p, lp, at);
+    as = fmaf(q, lp + r, as);  // log2(P_s/M) = log2(P_t/M) + r
   }
   s.at += at;
   s.as += as;
