@@ -4,8 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "skl_kernels.hpp"
 
@@ -35,6 +37,10 @@ int check_problem(const streamkl_problem_t* p, bool* empty) {
     if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0 || p->max_seqlen_q > p->Nq || p->max_seqlen_k > p->Nk)
       return STREAMKL_ERR_INVALID;
     if (!aligned(p->cu_seqlens_q, 4) || !aligned(p->cu_seqlens_k, 4)) return STREAMKL_ERR_UNSUPPORTED;
+  }
+  if (p->workspace != nullptr) {
+    if (p->workspace_floats < 0) return STREAMKL_ERR_INVALID;
+    if (!aligned(p->workspace, 16)) return STREAMKL_ERR_UNSUPPORTED;
   }
   *empty = (p->B == 0 || p->H == 0 || p->Nq == 0 || (packed && p->max_seqlen_q == 0));
   if (*empty) return STREAMKL_OK;
@@ -96,6 +102,10 @@ void fill_common(A& a, const streamkl_problem_t* p, const void* qt, const void* 
   a.mk = (int32_t)(packed ? p->max_seqlen_k : p->Nk);
   a.c_t = p->scale_t * 1.4426950408889634f;
   a.c_s = p->scale_s * 1.4426950408889634f;
+  if constexpr (std::is_same<A, skl::BwdArgs>::value) {
+    a.ws = p->workspace;
+    a.ws_floats = p->workspace != nullptr ? p->workspace_floats : 0;
+  }
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_LAUNCH; }
@@ -273,5 +283,23 @@ const char* streamkl_status_string(int status) {
 }
 
 int streamkl_version(void) { return STREAMKL_VERSION; }
+
+int64_t streamkl_workspace_floats(const streamkl_problem_t* p) {
+  bool empty = false;
+  if (check_problem(p, &empty) != STREAMKL_OK || empty) return 0;
+  // the key-owner grid (owned keys per workgroup: 256 for bf16, 128 for fp32) and the dK size of each
+  // grouped side, as the backward launcher computes them
+  const bool packed = p->cu_seqlens_q != nullptr;
+  const int64_t bw = p->dtype == STREAMKL_BF16 ? 256 : 128;
+  const int64_t nob = ((packed ? p->max_seqlen_k : p->Nk) + bw - 1) / bw, nb = packed ? 1 : p->B;
+  int64_t best = 0;
+  const int64_t hk[2] = {p->Hk_t > 0 ? p->Hk_t : p->H, p->Hk_s > 0 ? p->Hk_s : p->H};
+  const int64_t dd[2] = {p->d_t, p->d_s};
+  for (int side = 0; side < 2; ++side) {
+    const int64_t n = skl::split_wanted(p->H / hk[side], nob * p->B * hk[side]);
+    if (n > 1) best = std::max(best, n * nb * hk[side] * p->Nk * dd[side]);
+  }
+  return best;
+}
 
 }  // extern "C"

@@ -218,7 +218,10 @@ bwd_kernel(const BwdArgs a) {
   const int nbh = a.B * HX;
   const int nob = ((OWN_Q ? a.mq : a.mk) + BW - 1) / BW;
   const int bh = blockIdx.x % nbh;  // (batch, owned head)
-  const int oi = blockIdx.x / nbh;
+  // grouped keys: the group's passes may be split over NSP workgroups (adjacent in launch order)
+  const int NSP = GRP ? a.nsplit : 1;
+  const int sp = GRP ? (blockIdx.x / nbh) % NSP : 0;
+  const int oi = GRP ? blockIdx.x / nbh / NSP : blockIdx.x / nbh;
   // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
   const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
   const int b = bh / HX, ho = bh % HX;
@@ -500,7 +503,8 @@ bwd_kernel(const BwdArgs a) {
     if constexpr (sizeof(T) == 2) sched_read_ahead<NRG + NRL, 6>();
   };
 
-  for (int pass = 0; pass < GX; ++pass) {
+  const int pbeg = GRP ? sp * GX / NSP : 0, pend = GRP ? (sp + 1) * GX / NSP : 1;
+  for (int pass = pbeg; pass < pend; ++pass) {
     set_head(a, ho * GX + pass);
     set_rsrc();
     if constexpr (OWN_Q) {
@@ -578,12 +582,13 @@ bwd_kernel(const BwdArgs a) {
       }
     }
     wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
-    if (pass + 1 < GX) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
+    if (pass + 1 < pend) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
   }
 
   // JS: dS above is in log2 units and lacks the 1/2 of each half: ln 2 / 2 goes into the scale
   const float scale = (TEACHER ? a.scale_t : a.scale_s) * (JS ? 0.5f * kLn2 : 1.f);
-  float* out = (OWN_Q ? a.dq : a.dk) +
+  // a split group writes its partial dK into its part of the workspace (same layout as dK)
+  float* out = (OWN_Q ? a.dq : (GRP && NSP > 1 ? a.ws + sp * a.ws_part : a.dk)) +
                (((int64_t)sg.bs * HX + ho) * (OWN_Q ? a.Nq : a.Nk) + (OWN_Q ? sg.q0 : sg.k0)) * DX;
   // query owner: dS was formed without the row weight (it is one factor per output row)
   float rscale[16];
@@ -613,9 +618,17 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (!OWN_Q) {
     if (gx > 1) {
-      hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, false, true, JS>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s,
-                         a);
-      return hipGetLastError();
+      constexpr int DX = TE ? DT : DS;
+      const int64_t part = (int64_t)(a.cu_q ? 1 : a.B) * (a.H / gx) * a.Nk * DX;  // floats of dK
+      BwdArgs b = a;
+      b.nsplit = split_count(gx, nblk, part, a.ws, a.ws_floats);
+      b.ws_part = part;
+      if (nblk * b.nsplit > 0x7fffffff) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, false, true, JS>), dim3((unsigned)(nblk * b.nsplit)),
+                         dim3(BwdTile<T>::NT), 0, s, b);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || b.nsplit == 1) return e;
+      return launch_sum_parts(a.dk, a.ws, b.nsplit, part, s);
     }
   }
   hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, OWN_Q, false, JS>), dim3((unsigned)nblk), dim3(BwdTile<T>::NT), 0, s,

@@ -47,6 +47,13 @@ struct BwdArgs {
   const int32_t* cu_q;  // packed variable-length batch, as in FwdArgs
   const int32_t* cu_k;
   int32_t mq, mk;
+  // Grouped key heads, key owner: the passes over a group's query heads may be split over nsplit
+  // workgroups, each writing its partial dK to part (split) of ws (ws_part floats apart); the parts
+  // are then summed in a fixed order.  nsplit is set by the launcher (split_count).
+  float* ws;
+  int64_t ws_floats;
+  int64_t ws_part;
+  int32_t nsplit;
   float c_t, c_s;            // scale * log2(e)
   float scale_t, scale_s;
 };
@@ -67,6 +74,22 @@ __device__ __forceinline__ Segment segment_of(const A& a, int b) {
   return Segment{0, 0, a.Nq, a.Nk, b};
 }
 
+// Split of a grouped key-owner launch: enough workgroups to fill the chip (about 1024) where the
+// grid of owned key blocks is smaller, at most one split per query head of a group, and as many as
+// the workspace holds.  `part` = floats of one partial dK of that side (the dK output's size).
+constexpr int64_t kSplitTargetBlocks = 1024;
+inline int64_t split_wanted(int64_t group, int64_t blocks) {
+  if (group <= 1 || blocks <= 0) return 1;
+  const int64_t want = (kSplitTargetBlocks + blocks - 1) / blocks;
+  return want < group ? want : group;
+}
+inline int split_count(int64_t group, int64_t blocks, int64_t part, const float* ws, int64_t ws_floats) {
+  int64_t n = split_wanted(group, blocks);
+  if (ws == nullptr || part <= 0) return 1;
+  if (n * part > ws_floats) n = ws_floats / part;
+  return n < 2 ? 1 : (int)n;
+}
+
 // dtype: 0 fp32, 1 bf16.  d_t, d_s in {64, 128}.  Return hipErrorInvalidValue for
 // combinations that are not built (the C ABI rejects them before calling).
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int d_t, int d_s, bool causal, hipStream_t s);
@@ -75,6 +98,8 @@ hipError_t launch_bwd_dk(const BwdArgs& a, int dtype, int d_t, int d_s, bool cau
 // Jensen-Shannon: the forward's second pass (kl receives JS, js_t the teacher half; lse_t, lse_s are
 // read) and the backward kernels of sum_i g_i JS_i (kl = js_t, js = JS).
 hipError_t launch_js_fwd(const FwdArgs& a, int dtype, int d_t, int d_s, bool causal, hipStream_t s);
+// dst[i] = parts[i] + parts[n + i] + ... (nsplit parts, in that order); n a multiple of 4.
+hipError_t launch_sum_parts(float* dst, const float* parts, int nsplit, int64_t n, hipStream_t s);
 hipError_t launch_js_bwd_dq(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
 hipError_t launch_js_bwd_dk(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
 

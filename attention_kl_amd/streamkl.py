@@ -39,7 +39,8 @@ class Problem(ctypes.Structure):
                 ("stride_qt", _I64x3), ("stride_kt", _I64x3), ("stride_qs", _I64x3), ("stride_ks", _I64x3),
                 ("Hk_t", ctypes.c_int64), ("Hk_s", ctypes.c_int64),
                 ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
-                ("max_seqlen_q", ctypes.c_int64), ("max_seqlen_k", ctypes.c_int64)]
+                ("max_seqlen_q", ctypes.c_int64), ("max_seqlen_k", ctypes.c_int64),
+                ("workspace", ctypes.c_void_p), ("workspace_floats", ctypes.c_int64)]
 
     @property
     def packed(self) -> bool:
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         for f in ("streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_js_fwd",
                   "streamkl_js_bwd", "streamkl_version"):
             getattr(L, f).restype = ctypes.c_int
+        L.streamkl_workspace_floats.argtypes = [_P]
+        L.streamkl_workspace_floats.restype = ctypes.c_int64
         L.streamkl_status_string.argtypes = [ctypes.c_int]
         L.streamkl_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -100,6 +103,22 @@ def version() -> int:
 def _check(status: int, what: str):
     if status != OK:
         raise StreamKLError(status, f"{what}: {status_string(status)}")
+
+
+def attach_workspace(p: Problem, device, stream=None):
+    """Give p the workspace the library asks for (grouped key heads with few key heads: the key-owner
+    work of each group is then split over several workgroups).  Returns the tensor (or None), which
+    must stay alive until the launches that use it are enqueued; torch's allocator keeps it from
+    being reused before they run on its stream."""
+    import torch
+    n = lib().streamkl_workspace_floats(ctypes.byref(p))
+    if n <= 0:
+        return None
+    ws = torch.empty(n, dtype=torch.float32, device=device)
+    if stream is not None:
+        ws.record_stream(stream)
+    p.workspace, p.workspace_floats = ws.data_ptr(), n
+    return ws
 
 
 def _ptr(t) -> Optional[int]:
@@ -218,6 +237,7 @@ def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads
     out = list(out) + [None] * (4 - len(out))
     dq_s, dk_s = (out[0], out[1]) if student_grads else (None, None)
     dq_t, dk_t = (out[2], out[3]) if teacher_grads else (None, None)
+    ws = attach_workspace(p, qt.device, stream)  # noqa: F841 (kept alive through the call)
     _check(lib().streamkl_bwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
                               _ptr(kl), _ptr(g), _ptr(dq_s), _ptr(dk_s), _ptr(dq_t), _ptr(dk_t), _stream(stream)),
            "streamkl_bwd")
@@ -245,6 +265,7 @@ def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale
                      max_seqlen_k)
     if out is None:
         out = torch.empty(p.dk_shape(p.Hk_s, p.d_s), dtype=torch.float32, device=qt.device)
+    ws = attach_workspace(p, qt.device, stream)  # noqa: F841 (kept alive through the call)
     _check(lib().streamkl_bwd_dk(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
                                  _ptr(g), _ptr(out), _stream(stream)), "streamkl_bwd_dk")
     return out
@@ -284,6 +305,7 @@ def js_bwd(qt, kt, qs, ks, lse_t, lse_s, js, js_t, g, *, causal: bool, teacher_g
     out = list(out) + [None] * (4 - len(out))
     dq_s, dk_s = (out[0], out[1]) if student_grads else (None, None)
     dq_t, dk_t = (out[2], out[3]) if teacher_grads else (None, None)
+    ws = attach_workspace(p, qt.device, stream)  # noqa: F841 (kept alive through the call)
     _check(lib().streamkl_js_bwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
                                  _ptr(js), _ptr(js_t), _ptr(g), _ptr(dq_s), _ptr(dk_s), _ptr(dq_t), _ptr(dk_t),
                                  _stream(stream)), "streamkl_js_bwd")

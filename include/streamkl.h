@@ -46,7 +46,8 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10300 /* 1.3.0: Jensen-Shannon; 1.2.0: packed batches; 1.1.0: key heads */
+#define STREAMKL_VERSION 10400 /* 1.4.0: workspace for grouped keys; 1.3.0: Jensen-Shannon; 1.2.0: packed
+                                  batches; 1.1.0: key heads */
 
 typedef enum {
   STREAMKL_FP32 = 0, /* inputs float32; products on fp32 MFMA                */
@@ -104,7 +105,19 @@ typedef struct {
   const int32_t* cu_seqlens_q; /* packed batch: segment row offsets, DEVICE int32 [B + 1]; NULL =  */
   const int32_t* cu_seqlens_k; /* dense batch.  Both NULL or both non-NULL.                        */
   int64_t max_seqlen_q, max_seqlen_k; /* packed batch: longest segment (ignored when dense)         */
+  float* workspace;            /* optional DEVICE scratch (16-byte aligned), NULL = none: see below */
+  int64_t workspace_floats;    /* its size in floats                                               */
 } streamkl_problem_t;
+
+/* Workspace (grouped key heads only).  A key-owner launch whose gradient side has G > 1 query
+ * heads per key head makes G passes per workgroup; when the key heads are few the grid cannot fill
+ * the chip.  Given a workspace, the backward entry points split each group's passes over several
+ * workgroups, which write partial dK into the workspace, and then sum the parts in a fixed order
+ * into dk (the results are bitwise repeatable, but not bitwise equal to an unsplit run).
+ * streamkl_workspace_floats(p) is the size that allows the full split for p's shape and groupings
+ * (0 when no split helps); a smaller workspace gives a smaller split, none gives none.  The
+ * workspace is used in stream order: calls that overlap on different streams need their own.      */
+int64_t streamkl_workspace_floats(const streamkl_problem_t* p);
 
 /* Forward (S4): KL_i, LSE_t,i, LSE_s,i for every row, float32 [B, H, Nq] each.
  * One pass over the keys; per row only five running floats are kept.             */

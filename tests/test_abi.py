@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared) <= exported
-    assert S.version() == 10300
+    assert S.version() == 10400
 
 
 def test_status_strings():
@@ -219,3 +219,26 @@ def test_js_argument_rules():
     assert L.streamkl_js_bwd(ctypes.byref(p), *PTRS, *st[:4], None, *pair_s, None, None, None) == S.ERR_INVALID  # g
     assert L.streamkl_js_bwd(ctypes.byref(_problem(d_t=96)), *PTRS, *st, *pair_s, None, None, None) == \
         S.ERR_UNSUPPORTED
+
+
+def test_workspace_size_and_checks():
+    L = S.lib()
+    q = lambda **kw: L.streamkl_workspace_floats(ctypes.byref(_problem(**kw)))
+    big = dict(B=1, H=32, Nq=32768, Nk=32768, stride_qt=[32 * 32768 * 128, 32768 * 128, 128],
+               stride_kt=[32 * 32768 * 128, 32768 * 128, 128], stride_qs=[32 * 32768 * 128, 32768 * 128, 128],
+               stride_ks=[32 * 32768 * 128, 32768 * 128, 128])
+    assert q(**big) == 0                          # one key head per query head: nothing to split
+    assert q(**big, Hk_s=8) == 0                  # 8 key heads x 128 key blocks already fill the chip
+    # one student key head: 128 workgroups, split 8 ways towards ~1024 -> 8 partial dK of 32768 x 128
+    assert q(**big, Hk_s=1) == 8 * 32768 * 128
+    assert q(**big, Hk_t=2, Hk_s=1) == 8 * 32768 * 128  # the larger of the two sides
+    assert q(**big, Hk_s=1, dtype=S.FP32) == 4 * 32768 * 128  # fp32: 128 keys per workgroup, so 4-way
+    assert q(H=4, Hk_s=1) == 4 * 128 * 128        # a small problem: as many splits as query heads
+    assert q(B=0, H=4, Hk_s=1) == 0 and L.streamkl_workspace_floats(None) == 0
+    bad_ptr = [A + 2, A, A, A]
+    assert fwd_status(_problem(H=4, Hk_s=1, workspace=A + 8, workspace_floats=100), ptrs=bad_ptr) == \
+        S.ERR_UNSUPPORTED  # 8-byte aligned workspace
+    assert fwd_status(_problem(H=4, Hk_s=1, workspace=A + 0x100, workspace_floats=-1), ptrs=bad_ptr) == \
+        S.ERR_INVALID
+    assert fwd_status(_problem(H=4, Hk_s=1, workspace=A + 0x100, workspace_floats=100), ptrs=bad_ptr) == \
+        S.ERR_UNSUPPORTED  # a valid workspace: the problem checks pass

@@ -104,3 +104,37 @@ def test_autograd_with_grouped_student_keys():
     assert ratio_rows(ks.grad.float().cpu().numpy(), _sum_groups(rg["dk_s"], gs), rt,
                       grad_floor(w.scale_s, ones, h64[2])) <= 1.0
     assert ratio_rows(qs.grad.float().cpu().numpy(), rg["dq_s"], rt, grad_floor(w.scale_s, ones, h64[3])) <= 1.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_split_groups_match_unsplit_and_repeat_bitwise(dtype):
+    """With the workspace, each group's passes are split over several workgroups and the partial dK
+    summed in a fixed order: the same bits on every run, and the unsplit result to within rounding."""
+    import ctypes
+    w = wl.custom(1, 8, 300, 300, 128, 128, True, dtype=dtype, recipe="independent", seed=38)
+    print(f"case {w.name} split groups", flush=True)
+    (qt, kt, qs, ks), h64, (gt, gs) = _grouped_inputs(w, 8, 1)
+    kl, lt, ls = S.fwd(qt, kt, qs, ks, causal=True)
+    g = torch.from_numpy(wl.full_g(w)).cuda()
+    p = S.make_problem(qt, kt, qs, ks, True)
+    n = S.lib().streamkl_workspace_floats(ctypes.byref(p))
+    assert n == 8 * 1 * 1 * 300 * 128  # 8 splits (one per query head) of the one-key-head dK
+
+    def run(with_ws):
+        dk = torch.empty(1, 1, 300, 128, device="cuda")
+        ws = torch.empty(n, device="cuda") if with_ws else None
+        p.workspace, p.workspace_floats = (ws.data_ptr(), n) if with_ws else (None, 0)
+        st = S.lib().streamkl_bwd_dk(ctypes.byref(p), qt.data_ptr(), kt.data_ptr(), qs.data_ptr(), ks.data_ptr(),
+                                     lt.data_ptr(), ls.data_ptr(), g.data_ptr(), dk.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
+        assert st == S.OK
+        torch.cuda.synchronize()
+        return dk.cpu().numpy()
+    a, b, c = run(True), run(True), run(False)
+    np.testing.assert_array_equal(a, b)
+    rg = oracle.backward(*h64, w.scale_t, w.scale_s, True, wl.full_g(w))
+    ref = rg["dk_s"].reshape(1, 1, 8, 300, 128).sum(axis=2)
+    rt = rtol_of(w)
+    floor = grad_floor(w.scale_s, wl.full_g(w), h64[2])
+    assert ratio_rows(a, ref, rt, floor) <= 1.0 and ratio_rows(c, ref, rt, floor) <= 1.0
+    assert np.abs(a - c).max() <= 1e-5 * np.abs(c).max()  # float32 summation order only
