@@ -25,8 +25,9 @@
  * Conventions shared by every entry point.
  *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *    allocates nothing, frees nothing and keeps no state: the only HBM it touches
- *    beyond the inputs is the outputs the caller passes (S8: no O(Nq*Nk) buffer,
- *    not even a workspace).
+ *    beyond the inputs is the outputs the caller passes (S8: no O(Nq*Nk) buffer),
+ *    plus, for grouped key heads only, an optional caller workspace (see
+ *    streamkl_workspace_floats).
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and
  *    is asynchronous: the call returns after launch.  Kernel faults surface at the
  *    caller's next synchronisation, as for any HIP launch.
