@@ -287,8 +287,9 @@ int streamkl_version(void) { return STREAMKL_VERSION; }
 int64_t streamkl_workspace_floats(const streamkl_problem_t* p) {
   bool empty = false;
   if (check_problem(p, &empty) != STREAMKL_OK || empty) return 0;
-  // the key-owner grid (owned keys per workgroup: 256 for bf16, 128 for fp32) and the dK size of each
-  // grouped side, as the backward launcher computes them
+  // For each grouped side, the ungrouped dK (B H Nk d floats) the backward launcher can use to run
+  // the ungrouped kernel over every query head; where the group-sum grid cannot hold the key heads,
+  // the parts of the split the launcher would make (owned keys per workgroup: 256 bf16, 128 fp32).
   const bool packed = p->cu_seqlens_q != nullptr;
   const int64_t bw = p->dtype == STREAMKL_BF16 ? 256 : 128;
   const int64_t nob = ((packed ? p->max_seqlen_k : p->Nk) + bw - 1) / bw, nb = packed ? 1 : p->B;
@@ -296,7 +297,9 @@ int64_t streamkl_workspace_floats(const streamkl_problem_t* p) {
   const int64_t hk[2] = {p->Hk_t > 0 ? p->Hk_t : p->H, p->Hk_s > 0 ? p->Hk_s : p->H};
   const int64_t dd[2] = {p->d_t, p->d_s};
   for (int side = 0; side < 2; ++side) {
-    const int64_t n = skl::split_wanted(p->H / hk[side], nob * p->B * hk[side]);
+    const int64_t g = p->H / hk[side];
+    if (g <= 1) continue;
+    const int64_t n = nb * hk[side] <= 65535 ? g : skl::split_wanted(g, nob * p->B * hk[side]);
     if (n > 1) best = std::max(best, n * nb * hk[side] * p->Nk * dd[side]);
   }
   return best;

@@ -619,7 +619,21 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   if constexpr (!OWN_Q) {
     if (gx > 1) {
       constexpr int DX = TE ? DT : DS;
-      const int64_t part = (int64_t)(a.cu_q ? 1 : a.B) * (a.H / gx) * a.Nk * DX;  // floats of dK
+      const int64_t nb = a.cu_q ? 1 : a.B;
+      const int64_t part = nb * (a.H / gx) * a.Nk * DX;  // floats of dK
+      if (a.ws != nullptr && a.ws_floats >= part * gx && nb * (a.H / gx) <= 65535) {
+        // the ungrouped kernel over every query head (it reads key head h / g of each side), each
+        // head's contribution written to its own slice of an ungrouped dK in the workspace
+        BwdArgs b = a;
+        b.dk = a.ws;
+        const int64_t nblk_h = nblk * gx;
+        if (nblk_h > 0x7fffffff) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd_kernel<T, DT, DS, C, TE, false, false, JS>), dim3((unsigned)nblk_h),
+                           dim3(BwdTile<T>::NT), 0, s, b);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_group_sum(a.dk, a.ws, nb * (a.H / gx), gx, (int64_t)a.Nk * DX, s);
+      }
       BwdArgs b = a;
       b.nsplit = split_count(gx, nblk, part, a.ws, a.ws_floats);
       b.ws_part = part;

@@ -74,6 +74,11 @@ __device__ __forceinline__ Segment segment_of(const A& a, int b) {
   return Segment{0, 0, a.Nq, a.Nk, b};
 }
 
+// Grouped key heads, key owner, in order of preference by the caller's workspace:
+//   ws holds an ungrouped dK (B H Nk d floats): the ungrouped kernel runs over every query head,
+//     writing each head's contribution to its own slice, and the slices of a group are summed;
+//   ws holds S >= 2 partial dK: each group's passes are split over S workgroups, parts summed;
+//   no workspace: one workgroup makes all passes of its group.
 // Split of a grouped key-owner launch: enough workgroups to fill the chip (about 1024) where the
 // grid of owned key blocks is smaller, at most one split per query head of a group, and as many as
 // the workspace holds.  `part` = floats of one partial dK of that side (the dK output's size).
@@ -100,6 +105,8 @@ hipError_t launch_bwd_dk(const BwdArgs& a, int dtype, int d_t, int d_s, bool cau
 hipError_t launch_js_fwd(const FwdArgs& a, int dtype, int d_t, int d_s, bool causal, hipStream_t s);
 // dst[i] = parts[i] + parts[n + i] + ... (nsplit parts, in that order); n a multiple of 4.
 hipError_t launch_sum_parts(float* dst, const float* parts, int nsplit, int64_t n, hipStream_t s);
+// dst row r = src rows r G .. r G + G - 1 summed in that order (rows of `inner` floats, a multiple of 4).
+hipError_t launch_group_sum(float* dst, const float* src, int64_t rows, int groups, int64_t inner, hipStream_t s);
 hipError_t launch_js_bwd_dq(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
 hipError_t launch_js_bwd_dk(const BwdArgs& a, int dtype, int d_t, int d_s, bool causal, bool teacher, hipStream_t s);
 

@@ -110,14 +110,15 @@ typedef struct {
   int64_t workspace_floats;    /* its size in floats                                               */
 } streamkl_problem_t;
 
-/* Workspace (grouped key heads only).  A key-owner launch whose gradient side has G > 1 query
- * heads per key head makes G passes per workgroup; when the key heads are few the grid cannot fill
- * the chip.  Given a workspace, the backward entry points split each group's passes over several
- * workgroups, which write partial dK into the workspace, and then sum the parts in a fixed order
- * into dk (the results are bitwise repeatable, but not bitwise equal to an unsplit run).
- * streamkl_workspace_floats(p) is the size that allows the full split for p's shape and groupings
- * (0 when no split helps); a smaller workspace gives a smaller split, none gives none.  The
- * workspace is used in stream order: calls that overlap on different streams need their own.      */
+/* Workspace (grouped key heads only).  Without one, a key-owner launch whose gradient side has
+ * G > 1 query heads per key head makes G passes per workgroup, and when the key heads are few the
+ * grid cannot fill the chip.  With a workspace the size of an ungrouped dK (B H Nk d floats), the
+ * ungrouped kernel runs over every query head, each writing its contribution to its own slice, and
+ * the G slices of each key head are summed in head order into dk; with a smaller workspace each
+ * group's passes are split over as many workgroups as it holds partial dK, summed in a fixed order.
+ * Results are bitwise repeatable for a given workspace size (not bitwise equal across sizes).
+ * streamkl_workspace_floats(p) is the size of the best arrangement for p (0 when no side is
+ * grouped).  The workspace is used in stream order: overlapping calls need their own.            */
 int64_t streamkl_workspace_floats(const streamkl_problem_t* p);
 
 /* Forward (S4): KL_i, LSE_t,i, LSE_s,i for every row, float32 [B, H, Nq] each.

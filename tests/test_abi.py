@@ -227,13 +227,13 @@ def test_workspace_size_and_checks():
     big = dict(B=1, H=32, Nq=32768, Nk=32768, stride_qt=[32 * 32768 * 128, 32768 * 128, 128],
                stride_kt=[32 * 32768 * 128, 32768 * 128, 128], stride_qs=[32 * 32768 * 128, 32768 * 128, 128],
                stride_ks=[32 * 32768 * 128, 32768 * 128, 128])
-    assert q(**big) == 0                          # one key head per query head: nothing to split
-    assert q(**big, Hk_s=8) == 0                  # 8 key heads x 128 key blocks already fill the chip
-    # one student key head: 128 workgroups, split 8 ways towards ~1024 -> 8 partial dK of 32768 x 128
-    assert q(**big, Hk_s=1) == 8 * 32768 * 128
-    assert q(**big, Hk_t=2, Hk_s=1) == 8 * 32768 * 128  # the larger of the two sides
-    assert q(**big, Hk_s=1, dtype=S.FP32) == 4 * 32768 * 128  # fp32: 128 keys per workgroup, so 4-way
-    assert q(H=4, Hk_s=1) == 4 * 128 * 128        # a small problem: as many splits as query heads
+    assert q(**big) == 0                          # one key head per query head: no workspace
+    dk_full = 32 * 32768 * 128                    # an ungrouped dK of the workload: 32 query heads
+    assert q(**big, Hk_s=8) == dk_full            # each query head's contribution, then the group sums
+    assert q(**big, Hk_s=1) == dk_full
+    assert q(**big, Hk_t=2, Hk_s=1) == dk_full    # the larger of the two sides (both ungrouped dK here)
+    assert q(**big, Hk_s=1, dtype=S.FP32) == dk_full
+    assert q(H=4, Hk_s=1) == 4 * 128 * 128
     assert q(B=0, H=4, Hk_s=1) == 0 and L.streamkl_workspace_floats(None) == 0
     bad_ptr = [A + 2, A, A, A]
     assert fwd_status(_problem(H=4, Hk_s=1, workspace=A + 8, workspace_floats=100), ptrs=bad_ptr) == \
