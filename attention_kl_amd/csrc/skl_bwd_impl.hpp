@@ -34,6 +34,7 @@
 
 #include "skl_device.hpp"
 #include "skl_kernels.hpp"
+#include <type_traits>
 
 namespace skl {
 
@@ -58,15 +59,20 @@ struct BwdTile {
 };
 
 // dS of one 32 x 32 tile in the accumulator layout, kept from a vector phase to the next matrix
-// phase as the gradient product's A operand: bf16 hi + lo chunks, or fp32 values.
+// phase as the gradient product's A operand: bf16 hi + lo chunks or fp16 chunks (bf16 inputs), or
+// fp32 values.
 template <typename T>
 struct DsTile;
 template <>
 struct DsTile<__bf16> {
-  u32x4 hi[2], lo[2];
+  u32x4 hi[2], lo[2], h[2];
   __device__ __forceinline__ void set(const float* v) {
     split_bf16x8(v, hi[0], lo[0]);
     split_bf16x8(v + 8, hi[1], lo[1]);
+  }
+  __device__ __forceinline__ void set16(const float* v) {
+    h[0] = pack_f16x8(v);
+    h[1] = pack_f16x8(v + 8);
   }
 };
 template <>
@@ -76,6 +82,7 @@ struct DsTile<float> {
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = x[i];
   }
+  __device__ __forceinline__ void set16(const float* x) { set(x); }  // fp32 inputs have no fp16 product
 };
 
 // Per-lane byte offsets, inside a swizzled streamed tile of RB-byte rows, of the transpose-read
@@ -119,11 +126,21 @@ __device__ __forceinline__ void grad_mma(f32x16* out, const DsTile<__bf16>& ds, 
 
 // out[db] += dS . X[:, 32 db .. 32 db + 31] for one 32-row streamed tile.  dS is in the logit
 // accumulator layout (lane = owned row, element i = streamed row acc_row(i, hf)); X is the
-// streamed tile of the side being differentiated, row-major and swizzled in LDS at `xt`.
-template <typename T, int DX, int RB>
+// streamed tile of the side being differentiated, row-major and swizzled in LDS at `xt`.  F16: dS
+// and X are fp16 (X at `xt` is the converted copy of the tile), one product; otherwise bf16 X and
+// the hi + lo parts of dS.
+template <typename T, int DX, int RB, bool F16 = false>
 __device__ __forceinline__ void grad_product(f32x16* out, const DsTile<T>& ds, const char* xt,
                                              const int (*toff)[DX / 32], int lane) {
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (F16) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 bop[DX / 32];
+      grad_operands<DX, RB>(bop, xt, toff, c);
+#pragma unroll
+      for (int db = 0; db < DX / 32; ++db) mma_chunk<_Float16>(out[db], ds.h[c], bop[db]);
+    }
+  } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       u32x4 bop[DX / 32];
@@ -145,6 +162,48 @@ __device__ __forceinline__ void grad_product(f32x16* out, const DsTile<T>& ds, c
     }
   }
 }
+
+// Half `half` (HB bytes) of the gradient side of a streamed tile, converted from bf16 to fp16 in the
+// same layout by the 256 lanes of one wave group (t = 0..255), in steps that the fast matrix phase
+// spreads between its MFMAs: read, one step per word of two values, finish (write).  The conversion
+// is exact for magnitudes in [2^-17, 2^16) and for zero (fp16 keeps 11 significant bits against
+// bf16's 8); below, values round onto the fp16 subnormal grid (absolute error at most 2^-25), and
+// from 2^16 on they become infinite.  finish() returns true when this lane's values leave that
+// safe range: some magnitude reaches 2^16, or they are not all zero yet all below 2^-8 (so that an
+// absolute error of 2^-25 could exceed 2^-17 of the largest of them).
+template <int HB>
+struct HalfToF16 {
+  static constexpr int PER = HB / 256;  // bytes per lane
+  static constexpr int NWD = PER / 4;   // words (two values each) per lane
+  static_assert(PER == 16 || PER == 8, "tile half of 2 or 4 KB");
+  uint32_t w[NWD], r[NWD];
+  float m;
+  int o;
+  __device__ __forceinline__ void read(const char* src, int half, int t) {
+    o = half * HB + PER * t;
+    if constexpr (PER == 16) {
+      const u32x4 v = lds_read16(src + o);
+      w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src + o);
+      w[0] = v[0], w[1] = v[1];
+    }
+    m = 0.f;
+  }
+  __device__ __forceinline__ void step(int p) {
+    const float f0 = __uint_as_float(w[p] << 16), f1 = __uint_as_float(w[p] & 0xffff0000u);
+    const f16x2 h = {(_Float16)f0, (_Float16)f1};
+    r[p] = __builtin_bit_cast(uint32_t, h);
+    m = fmaxf(m, fmaxf(fabsf(f0), fabsf(f1)));
+  }
+  __device__ __forceinline__ bool finish(char* dst) {
+    if constexpr (PER == 16)
+      *reinterpret_cast<u32x4*>(dst + o) = u32x4{r[0], r[1], r[2], r[3]};
+    else
+      *reinterpret_cast<u32x2*>(dst + o) = u32x2{r[0], r[1]};
+    return (m > 0.f && m < 0x1p-8f) || !(m < 0x1p16f);
+  }
+};
 
 // Wait until at most N of this wave's vector-memory operations are outstanding, N wave-uniform
 // and below 16.
@@ -202,6 +261,17 @@ bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float cst[CSLOT ? NBUF : 1][4][32];
   __shared__ int cst_neg[CSLOT ? NBUF : 1];  // per slot: some streamed query of the tile has g < 0
   __shared__ __attribute__((aligned(16))) float wst[(!OWN_Q && NG == 1) ? NW : 1][4][32];
+  // Fast gradient product (student gradients of bf16 inputs): dS is rounded once to fp16 (2^-11
+  // relative), scaled by a power of two that keeps it inside the fp16 range, and the gradient side
+  // of each streamed tile is converted to fp16 in LDS (see convert_half), which halves the gradient
+  // product's MFMA work against the bf16 hi + lo form.  Each group converts half of a tile during
+  // its matrix phase of that tile; the copies of two consecutive tiles live at once.  A workgroup
+  // that meets a value outside the conversion's safe range, or ends with a non-finite gradient, is
+  // redone with the hi + lo form.
+  constexpr bool FAST = sizeof(T) == 2 && !TEACHER;
+  constexpr int HROW = BS * RBX;  // bytes of the gradient side of one streamed tile
+  __shared__ __attribute__((aligned(1024))) char h16[FAST ? 2 : 1][FAST ? HROW : 16];
+  __shared__ float gred[(FAST && !OWN_Q) ? NW : 1];  // per-wave maxima of |g| (key owner)
 
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
   // wave index in a scalar register: every branch on it (and on the group) is a scalar branch, so a
@@ -359,10 +429,14 @@ bwd_kernel(const BwdArgs a) {
   //   3: KL: KL + LSE_t - LSE_s (teacher).  JS: the gradient side's half KL(P || M) in log2 units,
   //      js_t for the teacher and 2 js - js_t for the student
   constexpr int NSTAT = (TEACHER || JS) ? 4 : 3;
+  // Fast path: dS is formed times 2^esh (an exponent offset, so no extra product): esh = 14 for the
+  // query owner, whose |dS| <= 1 (KL) or 2.6 (JS) before its row weight, and 14 - e for the key
+  // owner, where 2^e bounds the |g| of every streamed query of the workgroup.  0 otherwise.
+  float esh = 0.f;
   auto convert_one = [&](int k, const float* raw) -> float {
     const float g = raw[128 + r32];
-    if (k == 0) return raw[r32] * kLog2e - fast_log2(fabsf(g));
-    if (k == 1) return raw[64 + r32] * kLog2e - fast_log2(fabsf(g));
+    if (k == 0) return raw[r32] * kLog2e - fast_log2(fabsf(g)) - esh;
+    if (k == 1) return raw[64 + r32] * kLog2e - fast_log2(fabsf(g)) - esh;
     if (k == 2) return g;  // its sign is taken when stored
     if constexpr (JS) return (TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32])) * kLog2e;
     return raw[192 + r32] + raw[r32] - raw[64 + r32];
@@ -394,7 +468,8 @@ bwd_kernel(const BwdArgs a) {
   auto convert_stats = [&](int u, const char* sl) { stats_store(u, stats_load(sl)); };
 
   // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
-  auto vector_phase = [&](int s, int u, const char* sl) {
+  auto vector_phase = [&](int s, int u, const char* sl, auto f16c) {
+    constexpr bool F16 = decltype(f16c)::value;
     bool skip, full;
     tile_state(s, skip, full);
     if (NG == 1 && skip) return;  // ping-pong: a skipped tile goes through the masked path (all zero)
@@ -469,7 +544,10 @@ bwd_kernel(const BwdArgs a) {
         ds[i] = ok ? ds[i] : 0.f;
       }
     }
-    dsr.set(ds);
+    if constexpr (F16)
+      dsr.set16(ds);
+    else
+      dsr.set(ds);
   };
   // Matrix-core work of tile s (ring slot at sl): the gradient product, and the two logit products.
   auto grad_phase = [&](int s, const char* sl) {
@@ -502,15 +580,92 @@ bwd_kernel(const BwdArgs a) {
     tile_dot2_swz<T, DT, DS>(st, ss, sc, sc + BS * RBT, off_t, off_s, ot_r, os_r);
     if constexpr (sizeof(T) == 2) sched_read_ahead<NRG + NRL, 6>();
   };
+  bool risky = false;  // fast path: some converted value left the safe range (see HalfToF16)
+  // Fast matrix phase: gradient product of tile s-1 from its fp16 copy at hp, logit products of
+  // tile s (ring slot sc), and this group's half of tile s converted to fp16 at hd.  The order is
+  // fixed by scheduling barriers: LDS reads go out LA logit steps (of two MFMAs) ahead of their
+  // MFMAs; the conversion's read goes out with the first logit reads and its VALU steps ride behind
+  // logit MFMAs from step CD on, when the value has arrived.
+  auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd) {
+    if constexpr (FAST) {
+      constexpr int NDB = DX / 32, NT2 = RBT / 32, NS2 = RBS / 32, NM = NT2 > NS2 ? NT2 : NS2;
+      constexpr int LA = 3, CD = 2;
+      using Conv = HalfToF16<HROW / 2>;
+      const char* tt = sc;
+      const char* ts = sc + BS * RBT;
+      auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+      u32x4 b0[NDB], b1[NDB];
+      grad_operands<DX, RBX>(b0, hp, toff, 0);
+      fence();
+      grad_operands<DX, RBX>(b1, hp, toff, 1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[0], b0[db]);
+      fence();
+      u32x4 at[NM], as[NM];
+      auto lread = [&](int c) {
+        if (c < NT2) at[c] = lds_read16(tt + off_t[c]);
+        if (c < NS2) as[c] = lds_read16(ts + off_s[c]);
+      };
+#pragma unroll
+      for (int c = 0; c < LA; ++c) lread(c);
+      Conv cv;
+      cv.read(ts, grp, tid & 255);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[1], b1[db]);
+      fence();
+      st = f32x16{};
+      ss = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NM; ++c) {
+        if (c + LA < NM) lread(c + LA);
+        if (c < NT2) mma_chunk<T>(st, at[c], ot_r[c]);
+        if (c < NS2) mma_chunk<T>(ss, as[c], os_r[c]);
+        if (c >= CD && c - CD < Conv::NWD) cv.step(c - CD);
+        if (c - CD == Conv::NWD) risky |= cv.finish(hd);
+        fence();
+      }
+      if constexpr (NM - CD <= Conv::NWD) {  // short logit runs: whatever steps remain
+#pragma unroll
+        for (int p = NM - CD; p < Conv::NWD; ++p) cv.step(p);
+        risky |= cv.finish(hd);
+      }
+    }
+  };
 
   const int pbeg = GRP ? sp * GX / NSP : 0, pend = GRP ? (sp + 1) * GX / NSP : 1;
+  // Every pass over the stream, into dacc; F16: with the fast gradient product.
+  auto run = [&](auto f16c) {
+  constexpr bool F16 = decltype(f16c)::value;
+  if constexpr (F16 && !OWN_Q) {
+    // the largest |g| of the queries this workgroup streams, over all its passes, read up front
+    float gm = 0.f;
+    for (int pass = pbeg; pass < pend; ++pass) {
+      const float* gp = a.g + ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
+      for (int q = t_begin * BS + tid; q < n_str; q += 16 * NT) {  // 16 loads in flight per lane
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = gp[min(q + k * NT, n_str - 1)];  // unconditional loads
+#pragma unroll
+        for (int k = 0; k < 16; ++k) gm = fmaxf(gm, fabsf(v[k]));
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+    if (lane == 0) gred[wave] = gm;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) gm = fmaxf(gm, gred[w]);
+    esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // |g| < 2^e, e = frexp exponent of the max
+  } else {
+    esh = F16 ? 14.f : 0.f;
+  }
   for (int pass = pbeg; pass < pend; ++pass) {
     set_head(a, ho * GX + pass);
     set_rsrc();
     if constexpr (OWN_Q) {
       if (ovalid) {
-        own_lt = lse_t_bh[orow] * kLog2e;
-        own_ls = lse_s_bh[orow] * kLog2e;
+        own_lt = lse_t_bh[orow] * kLog2e - esh;
+        own_ls = lse_s_bh[orow] * kLog2e - esh;
         if constexpr (JS)
           own_c = (TEACHER ? kl_bh[orow] : fmaf(2.f, js_bh[orow], -kl_bh[orow])) * kLog2e;
         else if constexpr (TEACHER)
@@ -519,9 +674,16 @@ bwd_kernel(const BwdArgs a) {
     }
     {
       float z[16] = {};
-      dsr.set(z);
+      if constexpr (F16)
+        dsr.set16(z);
+      else
+        dsr.set(z);
     }
-    if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
+    if constexpr (F16) {  // zero the fp16 copy that the s = 0 gradient product reads (times a zero dS)
+      static_assert(HROW % 16 == 0, "copy fill");
+#pragma unroll
+      for (int o = 16 * tid; o < HROW; o += 16 * NT) *reinterpret_cast<u32x4*>(h16[1] + o) = u32x4{};
+    } else if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
       static_assert(TILE % 16 == 0, "slot fill");
 #pragma unroll
       for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
@@ -547,14 +709,17 @@ bwd_kernel(const BwdArgs a) {
           if (s <= ntile) {
             // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
             if (grp == 0) issue(s + PD, (u + PD) % NBUF);
-            matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
+            if constexpr (F16)
+              matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1]);
+            else
+              matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
             if (grp == 0) convert_stats(u, slot_ptr(u));  // tile s landed before this phase
             if (grp == 1) wait_tile();
             __syncthreads();
             // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
             if (s < ntile) {
               if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
-              vector_phase(s, u, slot_ptr(u));
+              vector_phase(s, u, slot_ptr(u), f16c);
               if (grp == 0) wait_tile();
               __syncthreads();
             } else if (grp == 0) {
@@ -573,7 +738,7 @@ bwd_kernel(const BwdArgs a) {
           if (s < ntile) {
             issue(s + PD, (u + PD) % NBUF);
             logit_phase(s, slot_ptr(u));
-            vector_phase(s, u, slot_ptr(u));
+            vector_phase(s, u, slot_ptr(u), f16c);
             grad_phase(s, slot_ptr(u));
             wait_tile();
             __syncthreads();
@@ -584,9 +749,29 @@ bwd_kernel(const BwdArgs a) {
     wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
     if (pass + 1 < pend) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
   }
+  };
+  if constexpr (FAST) {
+    run(std::true_type{});
+    // a streamed value outside the fp16 conversion's safe range, or a non-finite gradient (a
+    // non-finite input): redo the workgroup with the hi + lo product
+    bool bad = risky;
+#pragma unroll
+    for (int db = 0; db < DX / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bad |= !__builtin_isfinite(dacc[db][i]);
+    if (__syncthreads_or(bad)) {
+#pragma unroll
+      for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
+      run(std::false_type{});
+    }
+  } else {
+    run(std::false_type{});
+  }
+
 
   // JS: dS above is in log2 units and lacks the 1/2 of each half: ln 2 / 2 goes into the scale
-  const float scale = (TEACHER ? a.scale_t : a.scale_s) * (JS ? 0.5f * kLn2 : 1.f);
+  // fast path: dS was formed times 2^esh
+  const float scale = ldexpf((TEACHER ? a.scale_t : a.scale_s) * (JS ? 0.5f * kLn2 : 1.f), -(int)esh);
   // a split group writes its partial dK into its part of the workspace (same layout as dK)
   float* out = (OWN_Q ? a.dq : (GRP && NSP > 1 ? a.ws + sp * a.ws_part : a.dk)) +
                (((int64_t)sg.bs * HX + ho) * (OWN_Q ? a.Nq : a.Nk) + (OWN_Q ? sg.q0 : sg.k0)) * DX;

@@ -20,6 +20,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -40,6 +43,12 @@ template <>
 __device__ __forceinline__ void mma_chunk<__bf16>(f32x16& acc, const u32x4& a, const u32x4& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
                                                 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_chunk<_Float16>(f32x16& acc, const u32x4& a, const u32x4& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0,
+                                               0, 0);
 }
 
 template <>
@@ -231,17 +240,41 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Split 8 fp32 values into bf16 hi + lo parts (v ~= hi + lo to about 2^-16 relative).
+// Split 8 fp32 values into bf16 hi + lo parts (v ~= hi + lo to about 2^-16 relative).  Each pair
+// is rounded to bf16 once (hi); its two halves, widened back to fp32 by a shift and a mask, give
+// the remainders, which are rounded again (lo).
 __device__ __forceinline__ void split_bf16x8(const float* v, u32x4& hi, u32x4& lo) {
-  bf16x8 h, l;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 hb = (__bf16)v[e];
-    h[e] = hb;
-    l[e] = (__bf16)(v[e] - (float)hb);
+  for (int p = 0; p < 4; ++p) {
+    const bf16x2 h = {(__bf16)v[2 * p], (__bf16)v[2 * p + 1]};
+    const uint32_t hw = __builtin_bit_cast(uint32_t, h);
+    const float r0 = v[2 * p] - __uint_as_float(hw << 16);
+    const float r1 = v[2 * p + 1] - __uint_as_float(hw & 0xffff0000u);
+    const bf16x2 l = {(__bf16)r0, (__bf16)r1};
+    hi[p] = hw;
+    lo[p] = __builtin_bit_cast(uint32_t, l);
   }
-  hi = __builtin_bit_cast(u32x4, h);
-  lo = __builtin_bit_cast(u32x4, l);
+}
+
+// 8 fp32 values rounded to fp16 (nearest even; beyond the fp16 range they become +-inf).
+__device__ __forceinline__ u32x4 pack_f16x8(const float* v) {
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const f16x2 h = {(_Float16)v[2 * p], (_Float16)v[2 * p + 1]};
+    r[p] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
+}
+
+// bf16 values, two per word, as fp32 (a shift or a mask of each half).
+template <int NW>
+__device__ __forceinline__ void widen_bf16(const uint32_t* w, float* f) {
+#pragma unroll
+  for (int p = 0; p < NW; ++p) {
+    f[2 * p] = __uint_as_float(w[p] << 16);
+    f[2 * p + 1] = __uint_as_float(w[p] & 0xffff0000u);
+  }
 }
 
 }  // namespace skl
