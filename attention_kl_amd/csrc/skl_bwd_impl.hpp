@@ -589,7 +589,7 @@ bwd_kernel(const BwdArgs a) {
   auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd) {
     if constexpr (FAST) {
       constexpr int NDB = DX / 32, NT2 = RBT / 32, NS2 = RBS / 32, NM = NT2 > NS2 ? NT2 : NS2;
-      constexpr int LA = 3, CD = 2;
+      constexpr int LA = 2, CD = 2;
       using Conv = HalfToF16<HROW / 2>;
       const char* tt = sc;
       const char* ts = sc + BS * RBT;
