@@ -635,120 +635,120 @@ bwd_kernel(const BwdArgs a) {
   const int pbeg = GRP ? sp * GX / NSP : 0, pend = GRP ? (sp + 1) * GX / NSP : 1;
   // Every pass over the stream, into dacc; F16: with the fast gradient product.
   auto run = [&](auto f16c) {
-  constexpr bool F16 = decltype(f16c)::value;
-  if constexpr (F16 && !OWN_Q) {
-    // the largest |g| of the queries this workgroup streams, over all its passes, read up front
-    float gm = 0.f;
+    constexpr bool F16 = decltype(f16c)::value;
+    if constexpr (F16 && !OWN_Q) {
+      // the largest |g| of the queries this workgroup streams, over all its passes, read up front
+      float gm = 0.f;
+      for (int pass = pbeg; pass < pend; ++pass) {
+        const float* gp = a.g + ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
+        for (int q = t_begin * BS + tid; q < n_str; q += 16 * NT) {  // 16 loads in flight per lane
+          float v[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) v[k] = gp[min(q + k * NT, n_str - 1)];  // unconditional loads
+#pragma unroll
+          for (int k = 0; k < 16; ++k) gm = fmaxf(gm, fabsf(v[k]));
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+      if (lane == 0) gred[wave] = gm;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) gm = fmaxf(gm, gred[w]);
+      esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // |g| < 2^e, e = frexp exponent of the max
+    } else {
+      esh = F16 ? 14.f : 0.f;
+    }
     for (int pass = pbeg; pass < pend; ++pass) {
-      const float* gp = a.g + ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
-      for (int q = t_begin * BS + tid; q < n_str; q += 16 * NT) {  // 16 loads in flight per lane
-        float v[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = gp[min(q + k * NT, n_str - 1)];  // unconditional loads
-#pragma unroll
-        for (int k = 0; k < 16; ++k) gm = fmaxf(gm, fabsf(v[k]));
+      set_head(a, ho * GX + pass);
+      set_rsrc();
+      if constexpr (OWN_Q) {
+        if (ovalid) {
+          own_lt = lse_t_bh[orow] * kLog2e - esh;
+          own_ls = lse_s_bh[orow] * kLog2e - esh;
+          if constexpr (JS)
+            own_c = (TEACHER ? kl_bh[orow] : fmaf(2.f, js_bh[orow], -kl_bh[orow])) * kLog2e;
+          else if constexpr (TEACHER)
+            own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
+        }
       }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
-    if (lane == 0) gred[wave] = gm;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) gm = fmaxf(gm, gred[w]);
-    esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // |g| < 2^e, e = frexp exponent of the max
-  } else {
-    esh = F16 ? 14.f : 0.f;
-  }
-  for (int pass = pbeg; pass < pend; ++pass) {
-    set_head(a, ho * GX + pass);
-    set_rsrc();
-    if constexpr (OWN_Q) {
-      if (ovalid) {
-        own_lt = lse_t_bh[orow] * kLog2e - esh;
-        own_ls = lse_s_bh[orow] * kLog2e - esh;
-        if constexpr (JS)
-          own_c = (TEACHER ? kl_bh[orow] : fmaf(2.f, js_bh[orow], -kl_bh[orow])) * kLog2e;
-        else if constexpr (TEACHER)
-          own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
+      {
+        float z[16] = {};
+        if constexpr (F16)
+          dsr.set16(z);
+        else
+          dsr.set(z);
       }
-    }
-    {
-      float z[16] = {};
-      if constexpr (F16)
-        dsr.set16(z);
-      else
-        dsr.set(z);
-    }
-    if constexpr (F16) {  // zero the fp16 copy that the s = 0 gradient product reads (times a zero dS)
-      static_assert(HROW % 16 == 0, "copy fill");
+      if constexpr (F16) {  // zero the fp16 copy that the s = 0 gradient product reads (times a zero dS)
+        static_assert(HROW % 16 == 0, "copy fill");
 #pragma unroll
-      for (int o = 16 * tid; o < HROW; o += 16 * NT) *reinterpret_cast<u32x4*>(h16[1] + o) = u32x4{};
-    } else if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
-      static_assert(TILE % 16 == 0, "slot fill");
+        for (int o = 16 * tid; o < HROW; o += 16 * NT) *reinterpret_cast<u32x4*>(h16[1] + o) = u32x4{};
+      } else if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
+        static_assert(TILE % 16 == 0, "slot fill");
 #pragma unroll
-      for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
-    }
-    wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
-#pragma unroll
-    for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
-    wait_tile();
-    __syncthreads();
-    if constexpr (NG == 2) {
-      // Ring protocol (phases p = 0, 1, ...; tile s is read from phase 2s to 2s+3): tile s+PD is
-      // issued at the start of phase 2s into the slot of tile s-2, and each wave waits for its share
-      // of tile s+1 at the end of phase 2s+1, before that phase's barrier.  The last slot, read by
-      // the s = 0 gradient product, first receives a tile in phase 2.
-      if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
-        issue(PD, PD);
-        __syncthreads();
+        for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
       }
-      for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
+      wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
 #pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-          const int s = s0 + u;
-          if (s <= ntile) {
-            // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
-            if (grp == 0) issue(s + PD, (u + PD) % NBUF);
-            if constexpr (F16)
-              matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1]);
-            else
-              matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
-            if (grp == 0) convert_stats(u, slot_ptr(u));  // tile s landed before this phase
-            if (grp == 1) wait_tile();
-            __syncthreads();
-            // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
-            if (s < ntile) {
-              if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
-              vector_phase(s, u, slot_ptr(u), f16c);
-              if (grp == 0) wait_tile();
+      for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
+      wait_tile();
+      __syncthreads();
+      if constexpr (NG == 2) {
+        // Ring protocol (phases p = 0, 1, ...; tile s is read from phase 2s to 2s+3): tile s+PD is
+        // issued at the start of phase 2s into the slot of tile s-2, and each wave waits for its share
+        // of tile s+1 at the end of phase 2s+1, before that phase's barrier.  The last slot, read by
+        // the s = 0 gradient product, first receives a tile in phase 2.
+        if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
+          issue(PD, PD);
+          __syncthreads();
+        }
+        for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
+#pragma unroll
+          for (int u = 0; u < NBUF; ++u) {
+            const int s = s0 + u;
+            if (s <= ntile) {
+              // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
+              if (grp == 0) issue(s + PD, (u + PD) % NBUF);
+              if constexpr (F16)
+                matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1]);
+              else
+                matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
+              if (grp == 0) convert_stats(u, slot_ptr(u));  // tile s landed before this phase
+              if (grp == 1) wait_tile();
               __syncthreads();
-            } else if (grp == 0) {
-              __syncthreads();  // group 0's last phase, matching group 1's late start
+              // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
+              if (s < ntile) {
+                if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
+                vector_phase(s, u, slot_ptr(u), f16c);
+                if (grp == 0) wait_tile();
+                __syncthreads();
+              } else if (grp == 0) {
+                __syncthreads();  // group 0's last phase, matching group 1's late start
+              }
+            }
+          }
+        }
+      } else {
+        // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
+        // and tile s+1 waited for at its end.
+        for (int s0 = 0; s0 < ntile; s0 += NBUF) {
+#pragma unroll
+          for (int u = 0; u < NBUF; ++u) {
+            const int s = s0 + u;
+            if (s < ntile) {
+              issue(s + PD, (u + PD) % NBUF);
+              logit_phase(s, slot_ptr(u));
+              vector_phase(s, u, slot_ptr(u), f16c);
+              grad_phase(s, slot_ptr(u));
+              wait_tile();
+              __syncthreads();
             }
           }
         }
       }
-    } else {
-      // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
-      // and tile s+1 waited for at its end.
-      for (int s0 = 0; s0 < ntile; s0 += NBUF) {
-#pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-          const int s = s0 + u;
-          if (s < ntile) {
-            issue(s + PD, (u + PD) % NBUF);
-            logit_phase(s, slot_ptr(u));
-            vector_phase(s, u, slot_ptr(u), f16c);
-            grad_phase(s, slot_ptr(u));
-            wait_tile();
-            __syncthreads();
-          }
-        }
-      }
+      wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
+      if (pass + 1 < pend) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
     }
-    wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
-    if (pass + 1 < pend) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
-  }
   };
   if constexpr (FAST) {
     run(std::true_type{});
