@@ -205,6 +205,12 @@ struct HalfToF16 {
   }
 };
 
+// A bound, below 2^e with e = frexp exponent of the result, on |dS| of the KL teacher gradients
+// in row i.  With u = a - LSE_t <= 0 and v = b - LSE_s <= 0, dS = P_t (u - v - KL_i) and P_t = e^u:
+// P_t |u| <= 1/e, and the log-sum inequality over the other keys gives P_t (u - v) <= KL_i + 1/e, so
+// P_t |v| <= KL_i + 2/e and |dS| <= 2 KL_i + 3/e.  (The student's |dS| <= 1; both JS halves' <= 1.34.)
+__device__ __forceinline__ float teacher_ds_bound(float kl) { return 2.f * fabsf(kl) + 1.11f; }
+
 // Wait until at most N of this wave's vector-memory operations are outstanding, N wave-uniform
 // and below 16.
 __device__ __forceinline__ void wait_vmcnt_upto(int n) {
@@ -261,14 +267,15 @@ bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float cst[CSLOT ? NBUF : 1][4][32];
   __shared__ int cst_neg[CSLOT ? NBUF : 1];  // per slot: some streamed query of the tile has g < 0
   __shared__ __attribute__((aligned(16))) float wst[(!OWN_Q && NG == 1) ? NW : 1][4][32];
-  // Fast gradient product (student gradients of bf16 inputs): dS is rounded once to fp16 (2^-11
-  // relative), scaled by a power of two that keeps it inside the fp16 range, and the gradient side
+  // Fast gradient product (bf16 inputs): dS is rounded once to fp16 (2^-11 relative), scaled by a
+  // power of two that keeps it inside the fp16 range (see teacher_ds_bound), and the gradient side
   // of each streamed tile is converted to fp16 in LDS (see convert_half), which halves the gradient
   // product's MFMA work against the bf16 hi + lo form.  Each group converts half of a tile during
   // its matrix phase of that tile; the copies of two consecutive tiles live at once.  A workgroup
   // that meets a value outside the conversion's safe range, or ends with a non-finite gradient, is
   // redone with the hi + lo form.
-  constexpr bool FAST = sizeof(T) == 2 && !TEACHER;
+  constexpr bool FAST = sizeof(T) == 2;
+  constexpr bool KLT = TEACHER && !JS;  // KL teacher gradients: dS bounded per row by the row's KL
   constexpr int HROW = BS * RBX;  // bytes of the gradient side of one streamed tile
   __shared__ __attribute__((aligned(1024))) char h16[FAST ? 2 : 1][FAST ? HROW : 16];
   __shared__ float gred[(FAST && !OWN_Q) ? NW : 1];  // per-wave maxima of |g| (key owner)
@@ -429,10 +436,12 @@ bwd_kernel(const BwdArgs a) {
   //   3: KL: KL + LSE_t - LSE_s (teacher).  JS: the gradient side's half KL(P || M) in log2 units,
   //      js_t for the teacher and 2 js - js_t for the student
   constexpr int NSTAT = (TEACHER || JS) ? 4 : 3;
-  // Fast path: dS is formed times 2^esh (an exponent offset, so no extra product): esh = 14 for the
-  // query owner, whose |dS| <= 1 (KL) or 2.6 (JS) before its row weight, and 14 - e for the key
-  // owner, where 2^e bounds the |g| of every streamed query of the workgroup.  0 otherwise.
+  // Fast path: dS is formed times 2^esh (an exponent offset, so no extra product): for the query
+  // owner esh = 14 - e with 2^e above its rows' bound on |dS| before the row weight (e = 1, or per row
+  // for KL teacher gradients), for the key owner 14 - e with 2^e above |g| times that bound for every
+  // query the workgroup streams.  0 on the hi + lo path.
   float esh = 0.f;
+  bool fast_run = false;
   auto convert_one = [&](int k, const float* raw) -> float {
     const float g = raw[128 + r32];
     if (k == 0) return raw[r32] * kLog2e - fast_log2(fabsf(g)) - esh;
@@ -609,7 +618,7 @@ bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < LA; ++c) lread(c);
       Conv cv;
-      cv.read(ts, grp, tid & 255);
+      cv.read(TEACHER ? tt : ts, grp, tid & 255);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[1], b1[db]);
       fence();
@@ -637,16 +646,22 @@ bwd_kernel(const BwdArgs a) {
   auto run = [&](auto f16c) {
     constexpr bool F16 = decltype(f16c)::value;
     if constexpr (F16 && !OWN_Q) {
-      // the largest |g| of the queries this workgroup streams, over all its passes, read up front
+      // the largest |g| (times the row's bound on |dS|) of the queries this workgroup streams, over
+      // all its passes, read up front
       float gm = 0.f;
       for (int pass = pbeg; pass < pend; ++pass) {
-        const float* gp = a.g + ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
+        const int64_t r0 = ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
+        const float* gp = a.g + r0;
         for (int q = t_begin * BS + tid; q < n_str; q += 16 * NT) {  // 16 loads in flight per lane
-          float v[16];
+          float v[16], c[16];
 #pragma unroll
           for (int k = 0; k < 16; ++k) v[k] = gp[min(q + k * NT, n_str - 1)];  // unconditional loads
+          if constexpr (KLT) {
 #pragma unroll
-          for (int k = 0; k < 16; ++k) gm = fmaxf(gm, fabsf(v[k]));
+            for (int k = 0; k < 16; ++k) c[k] = a.kl[r0 + min(q + k * NT, n_str - 1)];
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k) gm = fmaxf(gm, fabsf(v[k]) * (KLT ? teacher_ds_bound(c[k]) : 1.f));
         }
       }
 #pragma unroll
@@ -655,17 +670,20 @@ bwd_kernel(const BwdArgs a) {
       __syncthreads();
 #pragma unroll
       for (int w = 0; w < NW; ++w) gm = fmaxf(gm, gred[w]);
-      esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // |g| < 2^e, e = frexp exponent of the max
+      esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // gm < 2^e, e = frexp exponent
     } else {
-      esh = F16 ? 14.f : 0.f;
+      esh = F16 ? 13.f : 0.f;  // |dS| < 2 (KL student, either JS half); KL teacher rows: below
     }
+    fast_run = F16;
     for (int pass = pbeg; pass < pend; ++pass) {
       set_head(a, ho * GX + pass);
       set_rsrc();
       if constexpr (OWN_Q) {
         if (ovalid) {
-          own_lt = lse_t_bh[orow] * kLog2e - esh;
-          own_ls = lse_s_bh[orow] * kLog2e - esh;
+          // KL teacher: this row's own shift, 14 - e with 2^e above the row's bound on |dS|
+          const float sh = (F16 && KLT) ? (float)(14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(kl_bh[orow]))) : esh;
+          own_lt = lse_t_bh[orow] * kLog2e - sh;
+          own_ls = lse_s_bh[orow] * kLog2e - sh;
           if constexpr (JS)
             own_c = (TEACHER ? kl_bh[orow] : fmaf(2.f, js_bh[orow], -kl_bh[orow])) * kLog2e;
           else if constexpr (TEACHER)
@@ -770,8 +788,7 @@ bwd_kernel(const BwdArgs a) {
 
 
   // JS: dS above is in log2 units and lacks the 1/2 of each half: ln 2 / 2 goes into the scale
-  // fast path: dS was formed times 2^esh
-  const float scale = ldexpf((TEACHER ? a.scale_t : a.scale_s) * (JS ? 0.5f * kLn2 : 1.f), -(int)esh);
+  const float scale = (TEACHER ? a.scale_t : a.scale_s) * (JS ? 0.5f * kLn2 : 1.f);
   // a split group writes its partial dK into its part of the workspace (same layout as dK)
   float* out = (OWN_Q ? a.dq : (GRP && NSP > 1 ? a.ws + sp * a.ws_part : a.dk)) +
                (((int64_t)sg.bs * HX + ho) * (OWN_Q ? a.Nq : a.Nk) + (OWN_Q ? sg.q0 : sg.k0)) * DX;
@@ -780,7 +797,10 @@ bwd_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = o0w + acc_row(i, hf);
-    rscale[i] = OWN_Q ? (r < n_own ? scale * g_bh[r] : 0.f) : scale;
+    // fast path: dS was formed times 2^esh, per row for the query owner of KL teacher gradients
+    int sh = (int)esh;
+    if (OWN_Q && KLT && fast_run && r < n_own) sh = 14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(kl_bh[r]));
+    rscale[i] = OWN_Q ? (r < n_own ? ldexpf(scale * g_bh[r], -sh) : 0.f) : ldexpf(scale, -sh);
   }
 #pragma unroll
   for (int db = 0; db < DX / 32; ++db) {
