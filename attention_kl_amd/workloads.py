@@ -81,7 +81,7 @@ def _causal_pairs(nq: int, nk: int) -> int:
 
 
 # The five synthetic configurations of the attention-KL workload, smallest first.
-CONFIGS: Dict[int, Workload] = {
+WORKLOADS: Dict[int, Workload] = {
     1: Workload("b1h2n128d64-fp32", 1, 2, 128, 128, 64, 64, False, "fp32", "noise", sigma=0.3, seed=1),
     2: Workload("b2h16n2048d128-causal", 2, 16, 2048, 2048, 128, 128, True, "bf16", "noise", sigma=0.1, seed=2),
     3: Workload("b1h32n32768d128-causal-peaky", 1, 32, 32768, 32768, 128, 128, True, "bf16", "independent",

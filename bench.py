@@ -206,14 +206,14 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-pmc":
         # python bench.py --ingest-pmc <fetch counter csv> <write counter csv> [workload id]
         from attention_kl_amd import workloads as wl
-        w = wl.CONFIGS[int(sys.argv[4]) if len(sys.argv) > 4 else 3]
+        w = wl.WORKLOADS[int(sys.argv[4]) if len(sys.argv) > 4 else 3]
         print(json.dumps(ingest_pmc(sys.argv[2], sys.argv[3], w.name), indent=1))
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="synthetic config id (3 = b1h32n32768d128 causal)")
+    ap.add_argument("--workload", type=int, default=3, help="synthetic workload id in workloads.WORKLOADS (3 = b1h32n32768d128 causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=12288)
     ap.add_argument("--no-autograd", action="store_true",
@@ -240,7 +240,7 @@ def main():
     from attention_kl_amd import streamkl as S
     from attention_kl_amd import workloads as wl
 
-    w = wl.CONFIGS[args.workload]
+    w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S.lib()  # fail loudly if the library is missing

@@ -55,7 +55,7 @@ def _check_full(w, teacher=False):
 
 
 SMALL = [
-    wl.CONFIGS[1],
+    wl.WORKLOADS[1],
     wl.custom(1, 2, 1, 1, 64, 64, True),
     wl.custom(1, 1, 2, 2, 128, 128, False),
     wl.custom(1, 1, 3, 3, 128, 128, True),
@@ -84,9 +84,9 @@ def test_teacher_gradients(w):
     _check_full(w, teacher=True)
 
 
-def test_config2_full():
+def test_b2h16n2048_causal_small_kl_full():
     """b2h16n2048d128 causal, student = teacher + 0.1 N(0,1): the small-KL cancellation regime."""
-    w = wl.CONFIGS[2]
+    w = wl.WORKLOADS[2]
     print(f"case {w.name}", flush=True)
     dev_in, host = device_inputs(w)
     (kl, lt, ls), grads = _run_gpu(w, dev_in)
@@ -200,20 +200,20 @@ def _rows(n, seed):
     return sorted(set([0, 1, 2, 31, 32, 63, 64, 127, 128, n // 2, n - 2, n - 1] + list(r)))
 
 
-def test_config3_full_size_sampled():
-    w = wl.CONFIGS[3]
+def test_b1h32n32768_causal_full_size_sampled():
+    w = wl.WORKLOADS[3]
     n = w.Nq
     _sampled(w, [(0, 0), (0, 17), (0, 31)], _rows(n, 3), [n - 1, n - 2, n - 31, n - 32, n - 64, n - 65, n - 130])
 
 
-def test_config4_full_size_sampled():
-    w = wl.CONFIGS[4]
+def test_b4h8n8192_two_head_dims_full_size_sampled():
+    w = wl.WORKLOADS[4]
     n = w.Nk
     _sampled(w, [(0, 0), (3, 7)], _rows(w.Nq, 4), [0, 1, 63, 64, 4095, n - 1])
 
 
-def test_config5_full_size_sampled():
-    w = wl.CONFIGS[5]
+def test_b1h8n131072_causal_full_size_sampled():
+    w = wl.WORKLOADS[5]
     n = w.Nq
     _sampled(w, [(0, 0), (0, 5)], _rows(n, 5), [n - 1, n - 2, n - 33, n - 100])
 

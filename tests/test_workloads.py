@@ -28,7 +28,7 @@ def test_heads_regenerate_independently():
 
 
 def test_recipes():
-    w = wl.CONFIGS[2]
+    w = wl.WORKLOADS[2]
     qt, kt, qs, ks = wl.head_f32(wl.custom(1, 1, 64, 64, 128, 128, True, recipe="noise", sigma=0.1, seed=2), 0, 0)
     assert 0.05 < np.std(qs - qt) < 0.15  # student = teacher + 0.1 N(0,1), bf16-rounded
     bits = wl.f32_to_bf16_bits(qt)
@@ -42,10 +42,10 @@ def test_recipes():
 
 
 def test_config_flops():
-    c3 = wl.CONFIGS[3]
+    c3 = wl.WORKLOADS[3]
     assert c3.pairs_per_head() == 32768 * 32769 // 2
     assert abs(c3.fwd_flops() - 8.796e12) / 8.796e12 < 1e-3
-    assert wl.CONFIGS[4].pairs_per_head() == 8192 * 8192
+    assert wl.WORKLOADS[4].pairs_per_head() == 8192 * 8192
     g = wl.head_g(c3, 0, 5)
     assert g.shape == (32768,) and g.min() >= 0.5 and g.max() <= 1.5
 
