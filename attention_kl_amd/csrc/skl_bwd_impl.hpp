@@ -12,16 +12,19 @@
 // One kernel template serves both halves.  Each wave owns 32 rows of the output
 // (query rows for dQ, key rows for dK) and keeps their Q or K slices in registers
 // as MFMA B operands; the other side streams through a 4-slot LDS ring filled by
-// buffer->LDS DMA.  Owning the output rows means no atomics and no workspace.
-// Both halves recompute both logit tiles.
+// buffer->LDS DMA.  Owning the output rows means no atomics (grouped key heads
+// may add a caller workspace of partial dK, summed in a fixed order).  Both halves
+// recompute both logit tiles.
 //
 // The logit tile is formed with the owned rows as columns, so each lane holds 16
 // streamed rows of one owned row; that register block is directly the A operand
 // of the gradient product (contraction over the streamed rows).  The B operand,
 // the streamed tile read with the streamed rows as the contraction index, comes
-// from the row-major LDS tile through transpose reads, so no transposed copy is
-// stored.  bf16: dS enters the MFMA as hi + lo bf16 parts (two products), so its
-// rounding contributes about 2^-16 relative instead of bf16's 2^-9.
+// from the LDS tile through transpose reads, so no transposed copy is stored.
+// bf16 inputs: dS enters the MFMA rounded once to fp16 at a power-of-two scale
+// against an fp16 copy of the streamed tile (2^-11 relative), or, for inputs
+// outside that product's range, as hi + lo bf16 parts (two products, about 2^-16)
+// instead of bf16's 2^-9.
 //
 // Per streamed tile s a wave runs a matrix phase, M(s) = gradient product of
 // tile s-1 then the two logit products of tile s, and a vector phase, V(s) = the
