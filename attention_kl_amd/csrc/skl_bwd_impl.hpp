@@ -478,6 +478,23 @@ bwd_kernel(const BwdArgs a) {
     }
   };
   auto convert_stats = [&](int u, const char* sl) { stats_store(u, stats_load(sl)); };
+  // The same conversion split for the fast matrix phase, which spreads it between its MFMAs: the raw
+  // values statistic k needs (LDS reads, issued early), then convert_one on them (consumed late).
+  auto stats_read = [&](const char* sl) -> f32x4 {
+    const int k = wave;
+    const float* raw = reinterpret_cast<const float*>(sl + TILE);
+    const int oa = 64 * k;                                  // lse_t, lse_s, g, kl / js_t
+    const int ob = k < 3 ? 128 : (JS ? 256 : 0);            // g, or js / lse_t
+    const int oc = 64;                                      // lse_s (KL teacher, k = 3)
+    return f32x4{raw[oa + r32], raw[ob + r32], raw[oc + r32], 0.f};
+  };
+  auto stats_convert = [&](const f32x4& rv) -> float {
+    const int k = wave;
+    if (k <= 1) return rv[0] * kLog2e - fast_log2(fabsf(rv[1])) - esh;
+    if (k == 2) return rv[0];
+    if constexpr (JS) return (TEACHER ? rv[0] : fmaf(2.f, rv[1], -rv[0])) * kLog2e;
+    return rv[0] + rv[1] - rv[2];
+  };
 
   // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
   auto vector_phase = [&](int s, int u, const char* sl, auto f16c) {
@@ -598,8 +615,10 @@ bwd_kernel(const BwdArgs a) {
   // fixed by scheduling barriers: LDS reads go out LA logit steps (of two MFMAs) ahead of their
   // MFMAs; the conversion's read goes out with the first logit reads and its VALU steps ride behind
   // logit MFMAs from step CD on, when the value has arrived.
-  auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd) {
+  auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd, int u) {
     if constexpr (FAST) {
+      // key owner: waves k < NSTAT of group 0 convert statistic k of tile s here (see stats_load)
+      const bool conv_st = CSLOT && grp == 0 && wave < NSTAT;
       constexpr int NDB = DX / 32, NT2 = RBT / 32, NS2 = RBS / 32, NM = NT2 > NS2 ? NT2 : NS2;
       constexpr int LA = 2, CD = 2;
       using Conv = HalfToF16<HROW / 2>;
@@ -622,6 +641,8 @@ bwd_kernel(const BwdArgs a) {
       for (int c = 0; c < LA; ++c) lread(c);
       Conv cv;
       cv.read(TEACHER ? tt : ts, grp, tid & 255);
+      f32x4 rv = {};
+      if (conv_st) rv = stats_read(sc);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[1], b1[db]);
       fence();
@@ -634,6 +655,7 @@ bwd_kernel(const BwdArgs a) {
         if (c < NS2) mma_chunk<T>(ss, as[c], os_r[c]);
         if (c >= CD && c - CD < Conv::NWD) cv.step(c - CD);
         if (c - CD == Conv::NWD) risky |= cv.finish(hd);
+        if (c == NM - 2 && conv_st) stats_store(u, stats_convert(rv));
         fence();
       }
       if constexpr (NM - CD <= Conv::NWD) {  // short logit runs: whatever steps remain
@@ -730,11 +752,12 @@ bwd_kernel(const BwdArgs a) {
             if (s <= ntile) {
               // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
               if (grp == 0) issue(s + PD, (u + PD) % NBUF);
-              if constexpr (F16)
-                matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1]);
-              else
+              if constexpr (F16) {
+                matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1], u);  // converts the statistics too
+              } else {
                 matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
-              if (grp == 0) convert_stats(u, slot_ptr(u));  // tile s landed before this phase
+                if (grp == 0) convert_stats(u, slot_ptr(u));  // tile s landed before this phase
+              }
               if (grp == 1) wait_tile();
               __syncthreads();
               // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
