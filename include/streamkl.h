@@ -52,7 +52,10 @@ extern "C" {
 
 typedef enum {
   STREAMKL_FP32 = 0, /* inputs float32; products on fp32 MFMA                */
-  STREAMKL_BF16 = 1  /* inputs bfloat16; products on bf16 MFMA, fp32 accumulate */
+  STREAMKL_BF16 = 1  /* inputs bfloat16; logit products on bf16 MFMA; the backward's gradient
+                        products on fp16 MFMA (dS rounded once, 2^-11 relative; the bf16 operand
+                        converted exactly) or, for values outside that range, bf16 hi + lo parts
+                        of dS; fp32 accumulation throughout */
 } streamkl_dtype_t;
 
 typedef enum {
