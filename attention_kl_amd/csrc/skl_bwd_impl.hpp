@@ -272,7 +272,7 @@ bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float wst[(!OWN_Q && NG == 1) ? NW : 1][4][32];
   // Fast gradient product (bf16 inputs): dS is rounded once to fp16 (2^-11 relative), scaled by a
   // power of two that keeps it inside the fp16 range (see teacher_ds_bound), and the gradient side
-  // of each streamed tile is converted to fp16 in LDS (see convert_half), which halves the gradient
+  // of each streamed tile is converted to fp16 in LDS (see HalfToF16), which halves the gradient
   // product's MFMA work against the bf16 hi + lo form.  Each group converts half of a tile during
   // its matrix phase of that tile; the copies of two consecutive tiles live at once.  A workgroup
   // that meets a value outside the conversion's safe range, or ends with a non-finite gradient, is
