@@ -41,7 +41,7 @@ def test_recipes():
     assert w.B * w.H * w.Nq == 65536
 
 
-def test_config_flops():
+def test_workload_flops():
     c3 = wl.WORKLOADS[3]
     assert c3.pairs_per_head() == 32768 * 32769 // 2
     assert abs(c3.fwd_flops() - 8.796e12) / 8.796e12 < 1e-3
