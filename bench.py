@@ -46,7 +46,9 @@ def kernel_flops(w, kernel: str, pairs=None) -> float:
     fwd:    both logit products, 2 (d_t + d_s) per allowed pair.
     bwd_dq: both logit products (the kernel has no other source of the logits) + dQ_s,
             2 (d_t + 2 d_s) per pair.   bwd_dk: the same with dK_s.
-    The hi/lo split of dS and masked-tile work are not counted.
+    bwd_teacher: both teacher kernels (dQ_t and dK_t), each 2 (2 d_t + d_s) per pair.
+    Masked-tile work, and the second gradient product of the hi + lo form (taken only by inputs outside
+    the fp16 product's range), are not counted.
     """
     pairs = w.pairs_per_head() * w.B * w.H if pairs is None else pairs
     if kernel == "fwd":
@@ -55,6 +57,8 @@ def kernel_flops(w, kernel: str, pairs=None) -> float:
         return 4.0 * pairs * (w.d_t + w.d_s)
     if kernel == "js_bwd":  # both backward kernels of the student side
         return 4.0 * pairs * (w.d_t + 2 * w.d_s)
+    if kernel == "bwd_teacher":
+        return 4.0 * pairs * (2 * w.d_t + w.d_s)
     return 2.0 * pairs * (w.d_t + 2 * w.d_s)
 
 
@@ -221,6 +225,8 @@ def main():
     ap.add_argument("--student-key-heads", type=int, default=None,
                     help="grouped student keys: K key heads shared by the H query heads (K divides H); key head j "
                          "is the workload's head j*H/K.  Default: one key head per query head")
+    ap.add_argument("--teacher-grads", action="store_true",
+                    help="KL step with the teacher's gradients too (two more backward kernels, timed together)")
     ap.add_argument("--divergence", choices=("kl", "js"), default="kl",
                     help="kl (default): KL(P_t || P_s); js: the Jensen-Shannon step (streamkl_js_fwd + streamkl_js_bwd)")
     ap.add_argument("--packed-mix", type=int, default=None, metavar="SEED",
@@ -279,6 +285,12 @@ def main():
     kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s, **seg)
     js = args.divergence == "js"
     ht = torch.empty_like(kl)  # JS: the teacher half KL(P_t || M)
+    teacher = args.teacher_grads
+    if teacher and (js or seg or hk_s != H):
+        print("bench.py: --teacher-grads goes with the dense KL step", file=sys.stderr)
+        sys.exit(2)
+    dqt = torch.empty(lead + (H, w.Nq, w.d_t), dtype=torch.float32, device=dev) if teacher else None
+    dkt = torch.empty(lead + (H, w.Nk, w.d_t), dtype=torch.float32, device=dev) if teacher else None
 
     def step(ev=None):
         if js:  # forward (two launches), then both student backward kernels
@@ -303,6 +315,11 @@ def main():
         S.bwd_dq(qt, kt, qs, ks, lt, ls, g, out=dq, **kw)
         if ev is not None:
             ev[3].record()
+        if teacher:
+            S.bwd(qt, kt, qs, ks, lt, ls, g, kl=kl, teacher_grads=True, student_grads=False,
+                  out=[None, None, dqt, dkt], **kw)
+            if ev is not None:
+                ev[4].record()
 
     for _ in range(args.warmup):
         step()
@@ -314,7 +331,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     free0 = torch.cuda.mem_get_info()[0]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5 if teacher else 4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -323,6 +340,8 @@ def main():
     wall = time.perf_counter() - t0
     extra_alloc = free0 - torch.cuda.mem_get_info()[0]
     per = {"js_fwd": [], "js_bwd": []} if js else {"fwd": [], "bwd_dk": [], "bwd_dq": []}
+    if teacher:
+        per["bwd_teacher"] = []
     for e in evs:
         if js:
             per["js_fwd"].append(e[0].elapsed_time(e[1]))
@@ -331,7 +350,9 @@ def main():
         per["fwd"].append(e[0].elapsed_time(e[1]))
         per["bwd_dk"].append(e[1].elapsed_time(e[2]))
         per["bwd_dq"].append(e[2].elapsed_time(e[3]))
-    step_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+        if teacher:
+            per["bwd_teacher"].append(e[3].elapsed_time(e[4]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
     kern = {}
     for k, v in per.items():
         ms = float(np.mean(v))
@@ -342,9 +363,13 @@ def main():
     # algorithmic work of the step: the two logit products once (JS: twice, a streaming JS needs both
     # log-sum-exps before its pass), then dQ_s and dK_s
     fwd_fl, bwd_fl = (4.0 if js else 2.0) * P * (w.d_t + w.d_s), 2.0 * P * (w.d_t + 3 * w.d_s)
+    if teacher:  # plus dQ_t and dK_t
+        bwd_fl += 4.0 * P * w.d_t
     fwd_ms = kern["js_fwd" if js else "fwd"]["ms"]
     bwd_ms = kern["js_bwd"]["ms"] if js else kern["bwd_dk"]["ms"] + kern["bwd_dq"]["ms"]
-    dominant = max(kern, key=lambda k: kern[k]["ms"])
+    if teacher:
+        bwd_ms += kern["bwd_teacher"]["ms"]
+    dominant = max((k for k in kern if k != "bwd_teacher"), key=lambda k: kern[k]["ms"])  # single launches
     dom_fl = kernel_flops(w, dominant, pairs)
     achieved = dom_fl / kern[dominant]["ms"] / 1e9
     roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": MI355X_PEAK_BF16_TFLOPS,
@@ -357,8 +382,9 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded N(0,1) bf16 inputs of the workload's shape)",
         "config": {"workload": w.name + (f"-hks{hk_s}" if hk_s != H else "") + (
-                       f"-packed{len(seg and lens)}seg" if seg else "") + ("-js" if js else ""), "B": B, "H": H,
-                   "N_Q": w.Nq, "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s, "causal": w.causal, "teacher_grads": False,
+                       f"-packed{len(seg and lens)}seg" if seg else "") + ("-js" if js else "") + ("-teacher" if teacher else ""),
+                   "B": B, "H": H,
+                   "N_Q": w.Nq, "N_K": w.Nk, "d_t": w.d_t, "d_s": w.d_s, "causal": w.causal, "teacher_grads": teacher,
                    "student_key_heads": hk_s, "divergence": args.divergence},
         "fwd_ms": fwd_ms, "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_fl / fwd_ms / 1e9, 2), "bwd_tflops": round(bwd_fl / bwd_ms / 1e9, 2),
