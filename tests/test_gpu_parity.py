@@ -158,13 +158,19 @@ def test_library_allocates_nothing():
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled
-def _sampled(w, heads, rows, keys):
-    print(f"case {w.name} (full size, sampled)", flush=True)
+def _sampled(w, heads, rows, keys, teacher=False):
+    """teacher: the teacher pair alone (dq_t, dk_t from one streamkl_bwd call), else the student pair."""
+    print(f"case {w.name} (full size, sampled) teacher={teacher}", flush=True)
     dev_in = device_inputs_bf16_bits(w)
     qt, kt, qs, ks = dev_in
     kl, lt, ls = S.fwd(qt, kt, qs, ks, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
     g = torch.from_numpy(wl.full_g(w)).cuda()
-    dq, dk, _, _ = S.bwd(qt, kt, qs, ks, lt, ls, g, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    grads = S.bwd(qt, kt, qs, ks, lt, ls, g, causal=w.causal, kl=kl, teacher_grads=teacher, student_grads=not teacher,
+                  scale_t=w.scale_t, scale_s=w.scale_s)
+    dq, dk = (grads[2], grads[3]) if teacher else (grads[0], grads[1])
+    assert (grads[0] is None) == teacher and (grads[2] is None) != teacher
+    xq, xk = (qt, kt) if teacher else (qs, ks)  # the side being differentiated
+    side = "t" if teacher else "s"
     torch.cuda.synchronize()
     rt = rtol_of(w)
     # properties over every row
@@ -174,10 +180,10 @@ def _sampled(w, heads, rows, keys):
     if w.causal:
         assert np.abs(klc[:, :, 0]).max() <= 1e-5  # one allowed key: KL = 0
     # sum_i q_i . dQ_i = sum_j k_j . dK_j (= scale sum_ij dS_ij q_i.k_j) per head
-    lhs = (qs.double() * dq.double()).sum(dim=(2, 3))
-    rhs = (ks.double() * dk.double()).sum(dim=(2, 3))
-    norm = (qs.double().norm(dim=3) * dq.double().norm(dim=3)).sum(dim=2) + \
-        (ks.double().norm(dim=3) * dk.double().norm(dim=3)).sum(dim=2)
+    lhs = (xq.double() * dq.double()).sum(dim=(2, 3))
+    rhs = (xk.double() * dk.double()).sum(dim=(2, 3))
+    norm = (xq.double().norm(dim=3) * dq.double().norm(dim=3)).sum(dim=2) + \
+        (xk.double().norm(dim=3) * dk.double().norm(dim=3)).sum(dim=2)
     assert float(((lhs - rhs).abs() / norm).max()) <= rt
     worst = {}
     gh = wl.full_g(w)
@@ -187,9 +193,12 @@ def _sampled(w, heads, rows, keys):
         worst["kl"] = max(worst.get("kl", 0), ratio_kl(klc[b, h, rows], rkl, rt))
         worst["lse"] = max(worst.get("lse", 0), ratio_lse(lt[b, h, rows].cpu().numpy(), rlt, rt),
                            ratio_lse(ls[b, h, rows].cpu().numpy(), rls, rt))
-        rg = oracle.backward_head(*hh, w.scale_t, w.scale_s, w.causal, gh[b, h], rows=rows, keys=keys)
-        worst["dq_s"] = max(worst.get("dq_s", 0), ratio_rows(dq[b, h, rows].cpu().numpy(), rg["dq_s"], rt))
-        worst["dk_s"] = max(worst.get("dk_s", 0), ratio_rows(dk[b, h, keys].cpu().numpy(), rg["dk_s"], rt))
+        rg = oracle.backward_head(*hh, w.scale_t, w.scale_s, w.causal, gh[b, h], teacher=teacher, rows=rows,
+                                  keys=keys)
+        worst["dq_" + side] = max(worst.get("dq_" + side, 0),
+                                  ratio_rows(dq[b, h, rows].cpu().numpy(), rg["dq_" + side], rt))
+        worst["dk_" + side] = max(worst.get("dk_" + side, 0),
+                                  ratio_rows(dk[b, h, keys].cpu().numpy(), rg["dk_" + side], rt))
     msg = report(w.name, **worst)
     print(msg, flush=True)
     assert max(worst.values()) <= 1.0, msg
@@ -204,6 +213,13 @@ def test_b1h32n32768_causal_full_size_sampled():
     w = wl.WORKLOADS[3]
     n = w.Nq
     _sampled(w, [(0, 0), (0, 17), (0, 31)], _rows(n, 3), [n - 1, n - 2, n - 31, n - 32, n - 64, n - 65, n - 130])
+
+
+def test_b1h32n32768_causal_teacher_gradients_full_size_sampled():
+    """The teacher pair at the bench size, launched as the bench's teacher-gradient step launches it."""
+    w = wl.WORKLOADS[3]
+    n = w.Nq
+    _sampled(w, [(0, 3), (0, 30)], _rows(n, 6), [n - 1, n - 2, n - 31, n - 32, n - 64, n - 65, n - 130], teacher=True)
 
 
 def test_b4h8n8192_two_head_dims_full_size_sampled():
