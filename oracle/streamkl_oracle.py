@@ -204,43 +204,62 @@ def _js_terms(la, lb, mask):
     return np.where(mask, la - lm, 0.0), np.where(mask, lb - lm, 0.0), pt, ps
 
 
-def js_forward_head(qt, kt, qs, ks, scale_t, scale_s, causal, block: int = ROW_BLOCK):
-    """Per-row JS, KL(P_t || M), KL(P_s || M), LSE_t, LSE_s (float64) of one head."""
+def js_forward_head(qt, kt, qs, ks, scale_t, scale_s, causal, rows: Optional[Iterable[int]] = None,
+                    block: int = ROW_BLOCK):
+    """Per-row JS, KL(P_t || M), KL(P_s || M), LSE_t, LSE_s (float64) of one head, for `rows`
+    (default: all)."""
     qt, kt, qs, ks = (np.asarray(x, np.float64) for x in (qt, kt, qs, ks))
     nq, _ = _check(qt, kt, qs, ks, causal)
-    out = [np.empty(nq) for _ in range(5)]
-    for r in _row_blocks(np.arange(nq), block):
+    rows = np.arange(nq) if rows is None else np.asarray(list(rows), dtype=np.int64)
+    out = [np.empty(len(rows)) for _ in range(5)]
+    pos = 0
+    for r in _row_blocks(rows, block):
         _, _, mask, la, lb, lse_t, lse_s, _ = _block_terms(qt, kt, qs, ks, float(scale_t), float(scale_s), causal, r)
         lrt, lrs, pt, ps = _js_terms(la, lb, mask)
         kt_m = (pt * lrt).sum(axis=1)
         ks_m = (ps * lrs).sum(axis=1)
         for o, v in zip(out, (0.5 * (kt_m + ks_m), kt_m, ks_m, lse_t, lse_s)):
-            o[r] = v
+            o[pos:pos + len(r)] = v
+        pos += len(r)
     return tuple(out)
 
 
 def js_backward_head(qt, kt, qs, ks, scale_t, scale_s, causal, g, teacher: bool = False,
+                     rows: Optional[Iterable[int]] = None, keys: Optional[Iterable[int]] = None,
                      block: int = ROW_BLOCK) -> Dict[str, np.ndarray]:
-    """Gradients of sum_i g_i JS_i for one head: dq_s, dk_s (and dq_t, dk_t when `teacher`)."""
+    """Gradients of sum_i g_i JS_i for one head: dq_s for `rows` and dk_s for `keys` (default all),
+    and dq_t, dk_t when `teacher`.  As in backward_head, every row that sees a requested key is
+    visited, since dK sums over them."""
     qt, kt, qs, ks = (np.asarray(x, np.float64) for x in (qt, kt, qs, ks))
     g = np.asarray(g, np.float64)
     nq, nk = _check(qt, kt, qs, ks, causal)
     s_t, s_s = float(scale_t), float(scale_s)
-    out = {"dq_s": np.zeros((nq, qs.shape[1])), "dk_s": np.zeros((nk, ks.shape[1]))}
+    qrows = np.arange(nq) if rows is None else np.asarray(list(rows), dtype=np.int64)
+    kcols = np.arange(nk) if keys is None else np.asarray(list(keys), dtype=np.int64)
+    visit = np.zeros(nq, bool)
+    visit[qrows] = True
+    if len(kcols):
+        visit[max(0, int(kcols.min()) - (nk - nq)) if causal else 0:] = True
+    qpos = {int(r): i for i, r in enumerate(qrows)}
+    out = {"dq_s": np.zeros((len(qrows), qs.shape[1])), "dk_s": np.zeros((len(kcols), ks.shape[1]))}
     if teacher:
-        out["dq_t"] = np.zeros((nq, qt.shape[1]))
-        out["dk_t"] = np.zeros((nk, kt.shape[1]))
-    for r in _row_blocks(np.arange(nq), block):
+        out["dq_t"] = np.zeros((len(qrows), qt.shape[1]))
+        out["dk_t"] = np.zeros((len(kcols), kt.shape[1]))
+    for r in _row_blocks(np.nonzero(visit)[0], block):
         _, _, mask, la, lb, _, _, kmax = _block_terms(qt, kt, qs, ks, s_t, s_s, causal, r)
         lrt, lrs, pt, ps = _js_terms(la, lb, mask)
         gr = g[r][:, None]
-        ds_s = gr * 0.5 * ps * (lrs - (ps * lrs).sum(axis=1, keepdims=True))
-        out["dq_s"][r] = s_s * (ds_s @ ks[:kmax])
-        out["dk_s"][:kmax] += s_s * (ds_s.T @ qs[r])
+        sides = [("s", gr * 0.5 * ps * (lrs - (ps * lrs).sum(axis=1, keepdims=True)), s_s, ks, qs)]
         if teacher:
-            ds_t = gr * 0.5 * pt * (lrt - (pt * lrt).sum(axis=1, keepdims=True))
-            out["dq_t"][r] = s_t * (ds_t @ kt[:kmax])
-            out["dk_t"][:kmax] += s_t * (ds_t.T @ qt[r])
+            sides.append(("t", gr * 0.5 * pt * (lrt - (pt * lrt).sum(axis=1, keepdims=True)), s_t, kt, qt))
+        sel = np.array([qpos.get(int(i), -1) for i in r])
+        hit = sel >= 0
+        kin = kcols < kmax
+        for side, ds, sc, kx, qx in sides:
+            if hit.any():
+                out["dq_" + side][sel[hit]] = sc * (ds[hit] @ kx[:kmax])
+            if kin.any():
+                out["dk_" + side][kin] += sc * (ds[:, kcols[kin]].T @ qx[r])
     return out
 
 

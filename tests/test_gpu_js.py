@@ -12,7 +12,8 @@ from attention_kl_amd import loss as L
 from attention_kl_amd import streamkl as S
 from attention_kl_amd import workloads as wl
 
-from parity import device_inputs, grad_floor, ratio_kl, ratio_lse, ratio_rows, report, rtol_of
+from parity import (device_inputs, device_inputs_bf16_bits, grad_floor, ratio_kl, ratio_lse, ratio_rows, report,
+                    rtol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +177,47 @@ def test_js_grouped_keys_with_teacher_gradients(dtype):
     msg = report(f"js grouped {dtype}", **r)
     print(msg, flush=True)
     assert max(r.values()) <= 1.0, msg
+
+
+def test_js_b1h32n32768_causal_full_size_sampled():
+    """The Jensen-Shannon step at the bench size, launched as `bench.py --divergence js` launches it:
+    properties over every row and head, and sampled rows and keys of two heads against the oracle."""
+    w = wl.WORKLOADS[3]
+    n = w.Nq
+    print(f"case {w.name} js (full size, sampled)", flush=True)
+    qt, kt, qs, ks = device_inputs_bf16_bits(w)
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    js, lt, ls, ht = S.js_fwd(qt, kt, qs, ks, **kw)
+    gh = wl.full_g(w)
+    dq, dk, _, _ = S.js_bwd(qt, kt, qs, ks, lt, ls, js, ht, torch.from_numpy(gh).cuda(), **kw)
+    torch.cuda.synchronize()
+    rt = rtol_of(w)
+    jsv, htv = js.cpu().numpy(), ht.cpu().numpy()
+    assert np.all(np.isfinite(jsv)) and bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all())
+    assert jsv.min() >= -1e-6 and jsv.max() <= math.log(2.0) + 1e-6
+    assert np.abs(jsv[:, :, 0]).max() <= 1e-6  # one allowed key: both rows are that key, JS = 0
+    # each half KL(P || M) lies in [0, ln 2] and JS is their mean, so the teacher half is at most 2 JS
+    assert htv.min() >= -1e-6 and np.all(htv <= 2.0 * jsv + 1e-5)
+    # sum_i q_i . dQ_i = sum_j k_j . dK_j per head (both are s_s sum_ij dS_ij q_i . k_j)
+    lhs = (qs.double() * dq.double()).sum(dim=(2, 3))
+    rhs = (ks.double() * dk.double()).sum(dim=(2, 3))
+    norm = (qs.double().norm(dim=3) * dq.double().norm(dim=3)).sum(dim=2) + \
+        (ks.double().norm(dim=3) * dk.double().norm(dim=3)).sum(dim=2)
+    assert float(((lhs - rhs).abs() / norm).max()) <= rt
+    extra = np.random.default_rng(7).choice(n, 12, replace=False)
+    rows = sorted(set([0, 1, 2, 31, 32, 63, 64, 127, 128, n // 2, n - 2, n - 1] + list(extra)))
+    keys = [n - 1, n - 2, n - 31, n - 32, n - 64, n - 65, n - 130]
+    worst = {}
+    for (b, h) in [(0, 0), (0, 21)]:
+        hh = wl.head_f64(w, b, h)
+        rjs, rht, _, rlt, rls = oracle.js_forward_head(*hh, w.scale_t, w.scale_s, w.causal, rows=rows)
+        worst["js"] = max(worst.get("js", 0), ratio_kl(jsv[b, h, rows], rjs, rt))
+        worst["js_t"] = max(worst.get("js_t", 0), ratio_kl(htv[b, h, rows], rht, rt))
+        worst["lse"] = max(worst.get("lse", 0), ratio_lse(lt[b, h, rows].cpu().numpy(), rlt, rt),
+                           ratio_lse(ls[b, h, rows].cpu().numpy(), rls, rt))
+        rg = oracle.js_backward_head(*hh, w.scale_t, w.scale_s, w.causal, gh[b, h], rows=rows, keys=keys)
+        worst["dq_s"] = max(worst.get("dq_s", 0), ratio_rows(dq[b, h, rows].cpu().numpy(), rg["dq_s"], rt))
+        worst["dk_s"] = max(worst.get("dk_s", 0), ratio_rows(dk[b, h, keys].cpu().numpy(), rg["dk_s"], rt))
+    msg = report(w.name + " js", **worst)
+    print(msg, flush=True)
+    assert max(worst.values()) <= 1.0, msg

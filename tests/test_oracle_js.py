@@ -134,3 +134,30 @@ def test_js_causal_single_key_rows_are_zero():
     r = js_backward_head(qt, kt, qs, ks, 0.5, 0.5, True, g, teacher=True)
     for v in r.values():
         np.testing.assert_array_equal(v, 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_js_row_blocking_and_subsets_agree(causal):
+    """Row blocks and row/key subsets (what the full-size GPU checks ask for) give the full result's
+    rows and keys."""
+    rng = np.random.default_rng(26)
+    nq, nk = 37, 45
+    arrs = rand_head(rng, nq, nk, 4, 4)
+    g = rng.uniform(0.5, 1.5, nq)
+    f1 = js_forward_head(*arrs, 0.5, 0.5, causal, block=1000)
+    f2 = js_forward_head(*arrs, 0.5, 0.5, causal, block=5)
+    rows = [0, 3, 36, 20]
+    f3 = js_forward_head(*arrs, 0.5, 0.5, causal, rows=rows)
+    for x, y, z in zip(f1, f2, f3):
+        np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-16)
+        np.testing.assert_allclose(x[rows], z, rtol=1e-13, atol=1e-16)
+    b1 = js_backward_head(*arrs, 0.5, 0.5, causal, g, teacher=True, block=1000)
+    b2 = js_backward_head(*arrs, 0.5, 0.5, causal, g, teacher=True, block=7)
+    keys = [44, 0, 30]
+    b3 = js_backward_head(*arrs, 0.5, 0.5, causal, g, teacher=True, rows=rows, keys=keys, block=6)
+    for k in b1:
+        np.testing.assert_allclose(b1[k], b2[k], rtol=1e-11, atol=1e-14)
+    for k in ("dq_s", "dq_t"):
+        np.testing.assert_allclose(b3[k], b1[k][rows], rtol=1e-11, atol=1e-14)
+    for k in ("dk_s", "dk_t"):
+        np.testing.assert_allclose(b3[k], b1[k][keys], rtol=1e-11, atol=1e-14)
