@@ -144,3 +144,46 @@ def test_workspace_arrangements_agree_and_repeat_bitwise(dtype):
     for x in (full, split, none):
         assert ratio_rows(x, ref, rt, floor) <= 1.0
         assert np.abs(x - none).max() <= 1e-5 * np.abs(none).max()  # float32 summation order only
+
+
+@pytest.mark.parametrize("hk_s", [8, 1])
+def test_grouped_student_keys_full_size_sampled(hk_s):
+    """The bench workload with K student key heads, as `bench.py --student-key-heads K` launches it
+    (key head j = the workload's student head j H/K, a strided view; the binding's workspace):
+    sampled rows of two query heads, and sampled keys of one key head summed over its whole group."""
+    from parity import device_inputs_bf16_bits
+    w = wl.WORKLOADS[3]
+    n, G = w.Nq, w.H // hk_s
+    print(f"case {w.name} Hk_s={hk_s} (full size, sampled)", flush=True)
+    qt, kt, qs, ks = device_inputs_bf16_bits(w)
+    ks = ks[:, ::G]
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    kl, lt, ls = S.fwd(qt, kt, qs, ks, **kw)
+    gh = wl.full_g(w)
+    dq, dk, _, _ = S.bwd(qt, kt, qs, ks, lt, ls, torch.from_numpy(gh).cuda(), **kw)
+    torch.cuda.synchronize()
+    assert dk.shape == (1, hk_s, n, w.d_s)
+    assert bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all()) and bool(torch.isfinite(kl).all())
+    rt = rtol_of(w)
+    extra = np.random.default_rng(8).choice(n, 10, replace=False)
+    rows = sorted(set([0, 1, 31, 32, 127, 128, n // 2, n - 2, n - 1] + list(extra)))
+    keys = [n - 1, n - 2, n - 33, n - 64, n - 130]
+    j = hk_s - 1  # the last key head: query heads j G .. j G + G - 1
+    ks_j = wl.head_f64(w, 0, j * G)[3]
+    worst, rdk = {}, np.zeros((len(keys), w.d_s))
+    for h in range(j * G, j * G + G):
+        qt_h, kt_h, qs_h, _ = wl.head_f64(w, 0, h)
+        check = h in (j * G, j * G + G - 1)
+        rg = oracle.backward_head(qt_h, kt_h, qs_h, ks_j, w.scale_t, w.scale_s, w.causal, gh[0, h],
+                                  rows=rows if check else [], keys=keys)
+        rdk += rg["dk_s"]
+        if check:
+            rkl, rlt, rls = oracle.forward_head(qt_h, kt_h, qs_h, ks_j, w.scale_t, w.scale_s, w.causal, rows=rows)
+            worst["kl"] = max(worst.get("kl", 0), ratio_kl(kl[0, h, rows].cpu().numpy(), rkl, rt))
+            worst["lse"] = max(worst.get("lse", 0), ratio_lse(lt[0, h, rows].cpu().numpy(), rlt, rt),
+                               ratio_lse(ls[0, h, rows].cpu().numpy(), rls, rt))
+            worst["dq_s"] = max(worst.get("dq_s", 0), ratio_rows(dq[0, h, rows].cpu().numpy(), rg["dq_s"], rt))
+    worst["dk_s"] = ratio_rows(dk[0, j, keys].cpu().numpy(), rdk, rt)
+    msg = report(f"{w.name} Hk_s={hk_s}", **worst)
+    print(msg, flush=True)
+    assert max(worst.values()) <= 1.0, msg

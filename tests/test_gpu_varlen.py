@@ -153,3 +153,46 @@ def test_autograd_on_a_packed_batch():
         assert ratio_rows(dk, rg["dk_s"], rt, grad_floor(sc, gw, s["qs"])) <= 1.0
         q0 += n
     assert abs(loss.item() - total) <= 2e-3 * max(abs(total), 1e-3) * 4
+
+
+def test_packed_length_mix_full_size_sampled():
+    """The bench workload's 32768 rows cut into the seeded length mix, as `bench.py --packed-mix 1`
+    launches it (the workload's generated tensors viewed as [N, H, d]): each segment is the problem
+    of its own rows and keys, checked on sampled rows and keys of three segments and two heads."""
+    from parity import device_inputs_bf16_bits, rtol_of
+    w = wl.WORKLOADS[3]
+    lens = wl.length_mix(w.Nq, 1)
+    cu_h = np.concatenate([[0], np.cumsum(lens)])
+    print(f"case {w.name} packed mix 1: {len(lens)} segments (full size, sampled)", flush=True)
+    qt, kt, qs, ks = (x[0].permute(1, 0, 2) for x in device_inputs_bf16_bits(w))
+    cu = torch.tensor(cu_h, dtype=torch.int32, device="cuda")
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s, cu_seqlens_q=cu, cu_seqlens_k=cu,
+              max_seqlen_q=max(lens), max_seqlen_k=max(lens))
+    kl, lt, ls = S.fwd(qt, kt, qs, ks, **kw)
+    gh = wl.full_g(w)
+    dq, dk, _, _ = S.bwd(qt, kt, qs, ks, lt, ls, torch.from_numpy(gh[0]).cuda(), **kw)
+    torch.cuda.synchronize()
+    assert kl.shape == (w.H, w.Nq) and dq.shape == (w.H, w.Nq, w.d_s)
+    assert bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all()) and bool(torch.isfinite(kl).all())
+    klc = kl.cpu().numpy()
+    assert np.abs(klc[:, cu_h[:-1]]).max() <= 1e-5  # each segment's first row sees one key: KL = 0
+    rt = rtol_of(w)
+    worst = {}
+    for s in sorted({int(np.argmax(lens)), int(np.argmin(lens)), len(lens) - 1}):
+        a, m = int(cu_h[s]), int(lens[s])
+        rows = sorted(set([0, 1, 31, 32, m // 2, m - 2, m - 1]))
+        keys = sorted(set([m - 1, m - 2, m - 33, m - 64]))
+        for h in (0, 19):
+            hh = [x[a:a + m] for x in wl.head_f64(w, 0, h)]
+            rkl, rlt, rls = oracle.forward_head(*hh, w.scale_t, w.scale_s, w.causal, rows=rows)
+            rg = oracle.backward_head(*hh, w.scale_t, w.scale_s, w.causal, gh[0, h, a:a + m], rows=rows, keys=keys)
+            r = [a + i for i in rows]
+            k = [a + i for i in keys]
+            worst["kl"] = max(worst.get("kl", 0), ratio_kl(klc[h, r], rkl, rt))
+            worst["lse"] = max(worst.get("lse", 0), ratio_lse(lt[h, r].cpu().numpy(), rlt, rt),
+                               ratio_lse(ls[h, r].cpu().numpy(), rls, rt))
+            worst["dq_s"] = max(worst.get("dq_s", 0), ratio_rows(dq[h, r].cpu().numpy(), rg["dq_s"], rt))
+            worst["dk_s"] = max(worst.get("dk_s", 0), ratio_rows(dk[h, k].cpu().numpy(), rg["dk_s"], rt))
+    msg = report(f"{w.name} packed mix 1", **worst)
+    print(msg, flush=True)
+    assert max(worst.values()) <= 1.0, msg
