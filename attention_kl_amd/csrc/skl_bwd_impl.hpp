@@ -29,10 +29,12 @@
 // Per streamed tile s a wave runs a matrix phase, M(s) = gradient product of
 // tile s-1 then the two logit products of tile s, and a vector phase, V(s) = the
 // probabilities and dS of tile s.  bf16 workgroups have eight waves in two
-// groups, one wave of each group per SIMD; group 1 starts one phase late and
-// every phase ends at a workgroup barrier, so on every SIMD one wave is in its
-// matrix phase while the other is in its vector phase (ping-pong) and the matrix
-// cores and the vector ALUs work at the same time.
+// groups, one wave of each group per SIMD, working in periods that end at a
+// workgroup barrier: in period s group 0 runs M(s) then V(s), group 1 V(s-1) then
+// M(s), so on every SIMD one wave is in its matrix phase while the other is in
+// its vector phase (ping-pong) and the matrix cores and the vector ALUs work at
+// the same time; within a period each wave goes on to its second phase as soon
+// as its first is done.
 #pragma once
 
 #include "skl_device.hpp"
@@ -264,12 +266,11 @@ bwd_kernel(const BwdArgs a) {
   constexpr int NRL = (RBT + RBS) / 32;                    // bf16 logit products: LDS reads = MFMAs
   static_assert(SLOT % 256 == 0, "ring slots start on a 256-byte bank window");
   __shared__ __attribute__((aligned(1024))) char ring[NBUF][SLOT];
-  // converted statistics (log2 units) of the streamed queries: per ring slot in the ping-pong (one
-  // wave of group 0 per statistic converts them a phase before use), per wave otherwise
-  constexpr bool CSLOT = !OWN_Q && NG == 2;
-  __shared__ __attribute__((aligned(16))) float cst[CSLOT ? NBUF : 1][4][32];
-  __shared__ int cst_neg[CSLOT ? NBUF : 1];  // per slot: some streamed query of the tile has g < 0
-  __shared__ __attribute__((aligned(16))) float wst[(!OWN_Q && NG == 1) ? NW : 1][4][32];
+  // converted statistics (log2 units) of the streamed queries, per wave: in the ping-pong each wave
+  // converts them in its own matrix phase of the tile, a phase before its vector phase reads them, so
+  // no other wave takes part; with one group, in the vector phase itself
+  constexpr bool MCONV = !OWN_Q && NG == 2;
+  __shared__ __attribute__((aligned(16))) float wst[!OWN_Q ? NW : 1][4][32];
   // Fast gradient product (bf16 inputs): dS is rounded once to fp16 (2^-11 relative), scaled by a
   // power of two that keeps it inside the fp16 range (see teacher_ds_bound), and the gradient side
   // of each streamed tile is converted to fp16 in LDS (see HalfToF16), which halves the gradient
@@ -361,7 +362,7 @@ bwd_kernel(const BwdArgs a) {
     t_begin = qmin / BS;
     t_end = (n_str + BS - 1) / BS;
   }
-  // never negative: the two groups' barrier counts (2 ntile + 3 each) stay equal even for rows
+  // never negative: the two groups' barrier counts (ntile + 2 each) stay equal even for rows
   // with no allowed key (an invalid segment of a packed batch)
   const int ntile = max(t_end - t_begin, 0);
 
@@ -453,47 +454,28 @@ bwd_kernel(const BwdArgs a) {
     if constexpr (JS) return (TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32])) * kLog2e;
     return raw[192 + r32] + raw[r32] - raw[64 + r32];
   };
-  // Ping-pong: wave k of group 0 converts statistic k of tile s during its matrix phase of that tile
-  // (phase 2s: the tile landed before it, and the wave's VALU is idle while its MFMAs run); group 0
-  // reads the values in phase 2s+1, group 1 in phase 2s+2.  Both halves of the wave hold the same 32
-  // rows and store the same values.
-  auto stats_load = [&](const char* sl) -> float {
-    float v = 0.f;
-    if constexpr (CSLOT) {
-      const int k = wave;
-      if (k < NSTAT) v = convert_one(k, reinterpret_cast<const float*>(sl + TILE));
-    }
-    return v;
-  };
-  auto stats_store = [&](int u, float v) {
-    if constexpr (CSLOT) {
-      const int k = wave;
-      if (k < NSTAT) {
-        cst[u][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
-        if (k == 2) {
-          const bool neg = __builtin_amdgcn_ballot_w64(v < 0.f) != 0;
-          if (lane == 0) cst_neg[u] = neg;
-        }
-      }
-    }
-  };
-  auto convert_stats = [&](int u, const char* sl) { stats_store(u, stats_load(sl)); };
-  // The same conversion split for the fast matrix phase, which spreads it between its MFMAs: the raw
-  // values statistic k needs (LDS reads, issued early), then convert_one on them (consumed late).
+  // Ping-pong: each wave converts the statistics of tile s in its own matrix phase of that tile (the
+  // tile landed before it, and the wave's VALU is mostly idle while its MFMAs run).  The two lane
+  // halves hold the same 32 rows and split the statistics: half hf converts k = hf (the exponent
+  // offsets) and k = 2 + hf (the sign of g; the KL or JS term when there are four).  The raw values
+  // are read early (stats_read), converted and stored late (stats_store); tile_neg tells the vector
+  // phase whether some row weight of the tile is negative.
+  bool tile_neg = false;
   auto stats_read = [&](const char* sl) -> f32x4 {
-    const int k = wave;
     const float* raw = reinterpret_cast<const float*>(sl + TILE);
-    const int oa = 64 * k;                                  // lse_t, lse_s, g, kl / js_t
-    const int ob = k < 3 ? 128 : (JS ? 256 : 0);            // g, or js / lse_t
-    const int oc = 64;                                      // lse_s (KL teacher, k = 3)
-    return f32x4{raw[oa + r32], raw[ob + r32], raw[oc + r32], 0.f};
+    float c3 = 0.f;
+    if constexpr (JS) c3 = TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32]);
+    else if constexpr (TEACHER) c3 = raw[192 + r32] + raw[r32] - raw[64 + r32];
+    return f32x4{raw[64 * hf + r32], raw[128 + r32], c3, 0.f};  // LSE of side hf, g, term 3
   };
-  auto stats_convert = [&](const f32x4& rv) -> float {
-    const int k = wave;
-    if (k <= 1) return rv[0] * kLog2e - fast_log2(fabsf(rv[1])) - esh;
-    if (k == 2) return rv[0];
-    if constexpr (JS) return (TEACHER ? rv[0] : fmaf(2.f, rv[1], -rv[0])) * kLog2e;
-    return rv[0] + rv[1] - rv[2];
+  auto stats_store = [&](const f32x4& rv) {
+    const float g = rv[1];
+    wst[wave][hf][r32] = rv[0] * kLog2e - fast_log2(fabsf(g)) - esh;
+    if (hf == 0)
+      wst[wave][2][r32] = g < 0.f ? -1.f : 1.f;
+    else if (NSTAT == 4)
+      wst[wave][3][r32] = JS ? rv[2] * kLog2e : rv[2];
+    tile_neg = __builtin_amdgcn_ballot_w64(g < 0.f) != 0;
   };
 
   // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
@@ -503,7 +485,7 @@ bwd_kernel(const BwdArgs a) {
     tile_state(s, skip, full);
     if (NG == 1 && skip) return;  // ping-pong: a skipped tile goes through the masked path (all zero)
     bool neg = false;  // some row weight of the tile is negative
-    if constexpr (!OWN_Q && !CSLOT) {  // statistics of the 32 streamed queries, converted by each wave
+    if constexpr (!OWN_Q && !MCONV) {  // statistics of the 32 streamed queries, converted by each wave
       const float* raw = reinterpret_cast<const float*>(sl + TILE);
 #pragma unroll
       for (int k = 0; k < NSTAT; ++k) {
@@ -512,7 +494,7 @@ bwd_kernel(const BwdArgs a) {
       }
       neg = __builtin_amdgcn_ballot_w64(raw[128 + r32] < 0.f) != 0;
     }
-    if constexpr (CSLOT) neg = __builtin_amdgcn_readfirstlane(cst_neg[u]) != 0;
+    if constexpr (MCONV) neg = tile_neg;
     const int sb = (t_begin + s) * BS;
     float ds[16];
 #pragma unroll
@@ -526,7 +508,7 @@ bwd_kernel(const BwdArgs a) {
         cc4 = f32x4{own_c, own_c, own_c, own_c};
       } else {
         const int ql = 8 * g4 + 4 * hf;
-        const float(*cs)[32] = CSLOT ? cst[u] : wst[CSLOT ? 0 : wave];
+        const float(*cs)[32] = wst[wave];
         lt4 = *reinterpret_cast<const f32x4*>(&cs[0][ql]);
         ls4 = *reinterpret_cast<const f32x4*>(&cs[1][ql]);
         cc4 = (TEACHER || JS) ? *reinterpret_cast<const f32x4*>(&cs[3][ql]) : f32x4{};
@@ -557,7 +539,7 @@ bwd_kernel(const BwdArgs a) {
     }
     if (neg) {  // key owner, a tile with a negative row weight: dS takes the sign of g
       asm volatile("");  // keep this a branch: taken only for such tiles
-      const float(*cs)[32] = CSLOT ? cst[u] : wst[CSLOT ? 0 : wave];
+      const float(*cs)[32] = wst[wave];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 sg4 = *reinterpret_cast<const f32x4*>(&cs[2][8 * g4 + 4 * hf]);
@@ -599,7 +581,7 @@ bwd_kernel(const BwdArgs a) {
   // products go out while the gradient MFMAs still run.  It has no branches: a tile that a wave
   // skips has an all-zero dS (its vector phase masks every element), at s = 0 the gradient
   // product adds a zero dS times ring slot 3 (zero-filled before the first barrier; tile 3 only
-  // arrives in phase 2), and at s = ntile the logit products (of a tile that has landed, so
+  // arrives in period 1), and at s = ntile the logit products (of a tile that has landed, so
   // finite) are not used.  Those cost under one percent of the MFMA work of a causal problem and
   // keep a single register assignment for the accumulators.
   auto matrix_phase = [&](const char* sp, const char* sc) {
@@ -617,8 +599,7 @@ bwd_kernel(const BwdArgs a) {
   // logit MFMAs from step CD on, when the value has arrived.
   auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd, int u) {
     if constexpr (FAST) {
-      // key owner: waves k < NSTAT of group 0 convert statistic k of tile s here (see stats_load)
-      const bool conv_st = CSLOT && grp == 0 && wave < NSTAT;
+      // key owner: this wave converts the statistics of tile s here (see stats_read)
       constexpr int NDB = DX / 32, NT2 = RBT / 32, NS2 = RBS / 32, NM = NT2 > NS2 ? NT2 : NS2;
       constexpr int LA = 2, CD = 2;
       using Conv = HalfToF16<HROW / 2>;
@@ -642,7 +623,7 @@ bwd_kernel(const BwdArgs a) {
       Conv cv;
       cv.read(TEACHER ? tt : ts, grp, tid & 255);
       f32x4 rv = {};
-      if (conv_st) rv = stats_read(sc);
+      if constexpr (MCONV) rv = stats_read(sc);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[1], b1[db]);
       fence();
@@ -655,7 +636,7 @@ bwd_kernel(const BwdArgs a) {
         if (c < NS2) mma_chunk<T>(ss, as[c], os_r[c]);
         if (c >= CD && c - CD < Conv::NWD) cv.step(c - CD);
         if (c - CD == Conv::NWD) risky |= cv.finish(hd);
-        if (c == NM - 2 && conv_st) stats_store(u, stats_convert(rv));
+        if (MCONV && c == NM - 2) stats_store(rv);
         fence();
       }
       if constexpr (NM - CD <= Conv::NWD) {  // short logit runs: whatever steps remain
@@ -737,37 +718,45 @@ bwd_kernel(const BwdArgs a) {
       wait_tile();
       __syncthreads();
       if constexpr (NG == 2) {
-        // Ring protocol (phases p = 0, 1, ...; tile s is read from phase 2s to 2s+3): tile s+PD is
-        // issued at the start of phase 2s into the slot of tile s-2, and each wave waits for its share
-        // of tile s+1 at the end of phase 2s+1, before that phase's barrier.  The last slot, read by
-        // the s = 0 gradient product, first receives a tile in phase 2.
-        if (grp == 1) {  // group 1 runs one phase behind: it sits out phase 0
-          issue(PD, PD);
-          __syncthreads();
-        }
+        // Periods s = 0 .. ntile, one workgroup barrier at the end of each.  In period s group 0 runs
+        // the matrix phase of tile s, then its vector phase; group 1 runs the vector phase of tile s-1,
+        // then the matrix phase of tile s, so on every SIMD one wave is in its matrix phase while the
+        // other is in its vector phase, and each wave moves on to its second phase as soon as it is
+        // done with the first.  No wave reads in a period what another wave writes in that period:
+        // a matrix phase reads tile s (landed and published by the previous barrier) and the fp16
+        // copy of tile s-1 (both halves written in period s-1), and writes its half of the copy of
+        // tile s into the other buffer; the statistics are the wave's own.  Ring: both groups issue
+        // their shares of tile s+PD at the start of period s (group 0 before its matrix phase, group
+        // 1 before its vector phase of tile s-1), into the slot of tile s-2, last read in period s-1;
+        // each wave waits for its share of tile s+1 before the barrier that ends period s.  The last
+        // slot, read by the s = 0 gradient product of the hi + lo path, first receives a tile in
+        // period 1.
+        if (grp == 1) issue(PD, PD);  // group 1's share of tile PD (period 0 has no vector phase for it)
         for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
 #pragma unroll
           for (int u = 0; u < NBUF; ++u) {
             const int s = s0 + u;
             if (s <= ntile) {
-              // matrix phase: phase 2s (group 0) or 2s+1 (group 1)
+              // matrix phase of tile s: first half of period s (group 0) or second half (group 1)
               if (grp == 0) issue(s + PD, (u + PD) % NBUF);
               if constexpr (F16) {
                 matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1], u);  // converts the statistics too
               } else {
                 matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
-                if (grp == 0) convert_stats(u, slot_ptr(u));  // tile s landed before this phase
+                if constexpr (MCONV) stats_store(stats_read(slot_ptr(u)));  // tile s landed before this phase
               }
-              if (grp == 1) wait_tile();
-              __syncthreads();
-              // vector phase: phase 2s+1 (group 0) or 2s+2 (group 1)
+              if (grp == 1) {  // the end of period s for group 1
+                wait_tile();
+                __syncthreads();
+              }
+              // vector phase of tile s: second half of period s (group 0) or first half of s+1 (group 1)
               if (s < ntile) {
                 if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
                 vector_phase(s, u, slot_ptr(u), f16c);
-                if (grp == 0) wait_tile();
+              }
+              if (grp == 0) {  // the end of period s for group 0 (ntile + 1 barriers for each group)
+                if (s < ntile) wait_tile();
                 __syncthreads();
-              } else if (grp == 0) {
-                __syncthreads();  // group 0's last phase, matching group 1's late start
               }
             }
           }
