@@ -216,6 +216,12 @@ struct HalfToF16 {
 // P_t |v| <= KL_i + 2/e and |dS| <= 2 KL_i + 3/e.  (The student's |dS| <= 1; both JS halves' <= 1.34.)
 __device__ __forceinline__ float teacher_ds_bound(float kl) { return 2.f * fabsf(kl) + 1.11f; }
 
+// log2|g| of a row weight, as the key owner folds it into the exponent offsets of the streamed
+// queries.  A zero weight gives -1e30 instead of -inf: the offsets stay finite, so both exponents
+// of such a row sink to about -1e30 and their probabilities to exact zeros, and their difference
+// (the Jensen-Shannon form's log-ratio r) stays finite instead of inf - inf.
+__device__ __forceinline__ float log2_weight(float g) { return fmaxf(fast_log2(fabsf(g)), -1.0e30f); }
+
 // Wait until at most N of this wave's vector-memory operations are outstanding, N wave-uniform
 // and below 16.
 __device__ __forceinline__ void wait_vmcnt_upto(int n) {
@@ -435,7 +441,7 @@ bwd_kernel(const BwdArgs a) {
   // Key owner: statistics of the streamed query rows, converted per tile to the units the vector
   // phase uses.  The row weight g enters the exponents: g P = sgn(g) exp2(x - (LSE log2 e - log2|g|)),
   // so dS needs no per-element product with g; only a tile holding a negative weight multiplies by
-  // the sign afterwards (g = 0 gives an exponent of -inf and a zero term).
+  // the sign afterwards (g = 0 gives an exponent near -1e30 and a zero term, see log2_weight).
   //   0: LSE_t log2 e - log2|g|   1: LSE_s log2 e - log2|g|   2: sgn(g)
   //   3: KL: KL + LSE_t - LSE_s (teacher).  JS: the gradient side's half KL(P || M) in log2 units,
   //      js_t for the teacher and 2 js - js_t for the student
@@ -448,8 +454,8 @@ bwd_kernel(const BwdArgs a) {
   bool fast_run = false;
   auto convert_one = [&](int k, const float* raw) -> float {
     const float g = raw[128 + r32];
-    if (k == 0) return raw[r32] * kLog2e - fast_log2(fabsf(g)) - esh;
-    if (k == 1) return raw[64 + r32] * kLog2e - fast_log2(fabsf(g)) - esh;
+    if (k == 0) return raw[r32] * kLog2e - log2_weight(g) - esh;
+    if (k == 1) return raw[64 + r32] * kLog2e - log2_weight(g) - esh;
     if (k == 2) return g;  // its sign is taken when stored
     if constexpr (JS) return (TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32])) * kLog2e;
     return raw[192 + r32] + raw[r32] - raw[64 + r32];
@@ -470,7 +476,7 @@ bwd_kernel(const BwdArgs a) {
   };
   auto stats_store = [&](const f32x4& rv) {
     const float g = rv[1];
-    wst[wave][hf][r32] = rv[0] * kLog2e - fast_log2(fabsf(g)) - esh;
+    wst[wave][hf][r32] = rv[0] * kLog2e - log2_weight(g) - esh;
     if (hf == 0)
       wst[wave][2][r32] = g < 0.f ? -1.f : 1.f;
     else if (NSTAT == 4)

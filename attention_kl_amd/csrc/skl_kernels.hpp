@@ -64,11 +64,16 @@ struct BwdArgs {
 struct Segment {
   int q0, k0, nq, nk, bs;
 };
+// Packed offsets are clamped into the packed axis (start in [0, N], end in [start, N]), so offsets
+// that break the rules (decreasing, negative, past N) give meaningless rows for that segment but
+// never an access outside the caller's buffers.
 template <class A>
 __device__ __forceinline__ Segment segment_of(const A& a, int b) {
   if (a.cu_q != nullptr) {
-    const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]), q1 = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]);
-    const int k0 = __builtin_amdgcn_readfirstlane(a.cu_k[b]), k1 = __builtin_amdgcn_readfirstlane(a.cu_k[b + 1]);
+    const int q0 = min(max(__builtin_amdgcn_readfirstlane(a.cu_q[b]), 0), a.Nq);
+    const int q1 = min(max(__builtin_amdgcn_readfirstlane(a.cu_q[b + 1]), q0), a.Nq);
+    const int k0 = min(max(__builtin_amdgcn_readfirstlane(a.cu_k[b]), 0), a.Nk);
+    const int k1 = min(max(__builtin_amdgcn_readfirstlane(a.cu_k[b + 1]), k0), a.Nk);
     return Segment{q0, k0, q1 - q0, k1 - k0, 0};
   }
   return Segment{0, 0, a.Nq, a.Nk, b};

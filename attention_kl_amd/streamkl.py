@@ -14,7 +14,8 @@ from typing import Optional, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libstreamkl.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "streamkl.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADER = os.path.join(INCLUDE, "streamkl.h")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
 FP32, BF16 = 0, 1
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, f).restype = ctypes.c_int
         L.streamkl_workspace_floats.argtypes = [_P]
         L.streamkl_workspace_floats.restype = ctypes.c_int64
+        L.streamkl_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, ctypes.POINTER(ctypes.c_double), _vp]
+        L.streamkl_probe_mfma.restype = ctypes.c_int
         L.streamkl_status_string.argtypes = [ctypes.c_int]
         L.streamkl_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -87,9 +90,13 @@ def lib() -> ctypes.CDLL:
 
 
 def declared_symbols() -> list:
-    """Entry points declared in include/streamkl.h."""
-    txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(streamkl_\w+)\s*\(", txt, re.M)))
+    """Entry points declared in the library's headers (include/*.h)."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            txt = open(os.path.join(INCLUDE, f)).read()
+            names |= set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(streamkl_\w+)\s*\(", txt, re.M))
+    return sorted(names)
 
 
 def status_string(status: int) -> str:
@@ -133,7 +140,8 @@ def _stream(stream) -> Optional[int]:
 
 def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
                  scale_s: Optional[float] = None, cu_seqlens_q=None, cu_seqlens_k=None,
-                 max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None) -> Problem:
+                 max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                 validate: bool = True) -> Problem:
     """Describe q [B, H, Nq, d] and k [B, Hk, Nk, d] tensors (d unit-stride) as a streamkl_problem_t.
 
     Each side's key-head count Hk (k.shape[1]) must divide H: query head h reads key head
@@ -141,8 +149,12 @@ def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
 
     Packed variable-length batch: pass cu_seqlens_q and cu_seqlens_k (int32 device tensors of
     length B + 1, the segments' row offsets) and q [Nq, H, d], k [Nk, Hk, d] holding every
-    segment's rows one after another.  max_seqlen_q / max_seqlen_k default to the longest segment
-    (read back from the device: a synchronisation)."""
+    segment's rows one after another.  The offsets are read back (a synchronisation) and checked:
+    non-negative, non-decreasing, within the packed rows, keys for every segment with queries (as
+    many as its queries when causal), and no segment longer than max_seqlen_q / max_seqlen_k, which
+    default to the longest segment; a ValueError is raised before anything is launched.
+    validate=False skips the read-back (both max_seqlen must then be given); the kernels clamp
+    every offset into the packed axis, so unchecked offsets cannot reach outside the buffers."""
     import torch
     packed = cu_seqlens_q is not None or cu_seqlens_k is not None
     if packed:
@@ -189,26 +201,52 @@ def make_problem(qt, kt, qs, ks, causal: bool, scale_t: Optional[float] = None,
     if packed:
         p.B = cu_seqlens_q.numel() - 1
         p.cu_seqlens_q, p.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
-
-        def longest(c):
-            return int((c[1:] - c[:-1]).max().item()) if c.numel() > 1 else 0
-        p.max_seqlen_q = longest(cu_seqlens_q) if max_seqlen_q is None else int(max_seqlen_q)
-        p.max_seqlen_k = longest(cu_seqlens_k) if max_seqlen_k is None else int(max_seqlen_k)
+        if validate:
+            # one read-back of both offset vectors (a synchronisation); the kernels themselves clamp
+            # every offset into the packed axis, so unchecked offsets cannot reach outside the buffers
+            lq, lk = _segment_lengths(cu_seqlens_q, Nq, "cu_seqlens_q"), _segment_lengths(cu_seqlens_k, Nk, "cu_seqlens_k")
+            for i, (nq, nk) in enumerate(zip(lq, lk)):
+                if nq > 0 and (nk == 0 or (causal and nk < nq)):
+                    raise ValueError(f"segment {i} has {nq} query rows and {nk} keys: "
+                                     + ("causal needs at least as many keys as queries" if nk else "rows without keys"))
+            for name, m, lens in (("max_seqlen_q", max_seqlen_q, lq), ("max_seqlen_k", max_seqlen_k, lk)):
+                if m is not None and lens and max(lens) > int(m):
+                    raise ValueError(f"{name} = {int(m)} is below the longest segment ({max(lens)})")
+            p.max_seqlen_q = (max(lq) if lq else 0) if max_seqlen_q is None else int(max_seqlen_q)
+            p.max_seqlen_k = (max(lk) if lk else 0) if max_seqlen_k is None else int(max_seqlen_k)
+        else:
+            if max_seqlen_q is None or max_seqlen_k is None:
+                raise ValueError("validate=False needs max_seqlen_q and max_seqlen_k")
+            p.max_seqlen_q, p.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
     return p
 
 
+def _segment_lengths(cu, n: int, name: str) -> list:
+    """Segment lengths of a packed axis of n rows from its offsets (read back to the host): the offsets
+    must start at 0 or above, never decrease and end at n or below."""
+    c = [int(v) for v in cu.cpu().tolist()]
+    if c and c[0] < 0:
+        raise ValueError(f"{name}[0] = {c[0]} is negative")
+    for i in range(len(c) - 1):
+        if c[i + 1] < c[i]:
+            raise ValueError(f"{name} decreases at entry {i + 1} ({c[i]} -> {c[i + 1]})")
+    if c and c[-1] > n:
+        raise ValueError(f"{name}[-1] = {c[-1]} is past the {n} packed rows")
+    return [c[i + 1] - c[i] for i in range(len(c) - 1)]
+
+
 _PACKED_DOC = """Packed variable-length batch: cu_seqlens_q, cu_seqlens_k (and optionally max_seqlen_q,
-    max_seqlen_k) as in make_problem; outputs then take the C ABI's packed layout: statistics
+    max_seqlen_k, validate) as in make_problem; outputs then take the C ABI's packed layout: statistics
     [H, Nq], dQ [H, Nq, d], dK [Hk, Nk, d]."""
 
 
 def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
-        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None
+        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True
         ) -> Tuple["torch.Tensor", "torch.Tensor", "torch.Tensor"]:
     """Per-row KL(P_t || P_s), LSE_t, LSE_s as float32 [B, H, Nq] (streamkl_fwd)."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                     max_seqlen_k)
+                     max_seqlen_k, validate)
     if out is None:
         out = tuple(torch.empty(p.stat_shape(), dtype=torch.float32, device=qt.device) for _ in range(3))
     kl, lse_t, lse_s = out
@@ -219,12 +257,12 @@ def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, s
 
 def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads: bool = False,
         student_grads: bool = True, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
-        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True):
     """Gradients of sum_i g_i KL_i (streamkl_bwd): (dq_s, dk_s, dq_t, dk_t), the pairs not asked for
     returned as None (student pair by default, teacher pair with teacher_grads=True)."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                     max_seqlen_k)
+                     max_seqlen_k, validate)
     dev = qt.device
     if out is None:
         out = [None, None, None, None]
@@ -245,11 +283,11 @@ def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads
 
 
 def bwd_dq(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None,
-           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True):
     """Student dQ only: the query-owner half of the backward (streamkl_bwd_dq)."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                     max_seqlen_k)
+                     max_seqlen_k, validate)
     if out is None:
         out = torch.empty(p.dq_shape(p.d_s), dtype=torch.float32, device=qt.device)
     _check(lib().streamkl_bwd_dq(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t), _ptr(lse_s),
@@ -258,11 +296,11 @@ def bwd_dq(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale
 
 
 def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None,
-           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True):
     """Student dK only: the key-owner half of the backward (streamkl_bwd_dk)."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                     max_seqlen_k)
+                     max_seqlen_k, validate)
     if out is None:
         out = torch.empty(p.dk_shape(p.Hk_s, p.d_s), dtype=torch.float32, device=qt.device)
     ws = attach_workspace(p, qt.device, stream)  # noqa: F841 (kept alive through the call)
@@ -272,12 +310,12 @@ def bwd_dk(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale
 
 
 def js_fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
-           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True):
     """Per-row Jensen-Shannon divergence (streamkl_js_fwd): (js, lse_t, lse_s, js_t), float32 in the
     layout of fwd's outputs; js_t is the teacher half KL(P_t || M), which js_bwd needs."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                     max_seqlen_k)
+                     max_seqlen_k, validate)
     if out is None:
         out = tuple(torch.empty(p.stat_shape(), dtype=torch.float32, device=qt.device) for _ in range(4))
     js, lse_t, lse_s, js_t = out
@@ -288,11 +326,11 @@ def js_fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None
 
 def js_bwd(qt, kt, qs, ks, lse_t, lse_s, js, js_t, g, *, causal: bool, teacher_grads: bool = False,
            student_grads: bool = True, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
-           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True):
     """Gradients of sum_i g_i JS_i (streamkl_js_bwd): (dq_s, dk_s, dq_t, dk_t) as bwd returns them."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                     max_seqlen_k)
+                     max_seqlen_k, validate)
     dev = qt.device
     if out is None:
         out = [None, None, None, None]

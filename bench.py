@@ -3,10 +3,16 @@
 One step = the whole path on one batch: the forward (per-row KL + both LSEs) and
 the student backward (dK_s then dQ_s), on the b1h32n32768d128 causal workload
 (teacher keys 1% scaled x4, independent student), bf16 inputs already resident in
-HBM.  Prints ONE JSON line.
+HBM.  Prints ONE JSON line; its `configs` object adds the same step timed on each
+of the five synthetic workloads.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
-                  [--copy-calibrate]
+                  [--no-configs] [--copy-calibrate]
+
+Work is counted as the method's algorithmic MFMA flops, each product once: the forward
+2 (d_t + d_s) per allowed pair (both logit products), the backward 2 (d_t + 3 d_s) (the two
+logit products, dQ_s and dK_s).  The two backward kernels each recompute both logit
+products; that repeat is overhead and shows as `issued_tflops` per kernel.
 """
 from __future__ import annotations
 
@@ -41,14 +47,15 @@ def source_sha(kernel: str) -> str:
 
 
 def kernel_flops(w, kernel: str, pairs=None) -> float:
-    """Algorithmic MFMA flops of one launch.
+    """MFMA flops one launch issues for the allowed pairs (its `issued_tflops`).
 
     fwd:    both logit products, 2 (d_t + d_s) per allowed pair.
     bwd_dq: both logit products (the kernel has no other source of the logits) + dQ_s,
             2 (d_t + 2 d_s) per pair.   bwd_dk: the same with dK_s.
     bwd_teacher: both teacher kernels (dQ_t and dK_t), each 2 (2 d_t + d_s) per pair.
     Masked-tile work, and the second gradient product of the hi + lo form (taken only by inputs outside
-    the fp16 product's range), are not counted.
+    the fp16 product's range), are not counted.  The method's own (algorithmic) count, which the
+    roofline fractions use, counts each product once: see step_flops.
     """
     pairs = w.pairs_per_head() * w.B * w.H if pairs is None else pairs
     if kernel == "fwd":
@@ -60,6 +67,37 @@ def kernel_flops(w, kernel: str, pairs=None) -> float:
     if kernel == "bwd_teacher":
         return 4.0 * pairs * (2 * w.d_t + w.d_s)
     return 2.0 * pairs * (w.d_t + 2 * w.d_s)
+
+
+def step_flops(w, pairs=None, js=False, teacher=False):
+    """Algorithmic MFMA flops of one step, each product counted once: forward 2 (d_t + d_s) per allowed
+    pair (JS: twice, a streaming JS needs both log-sum-exps before its pass), backward 2 (d_t + 3 d_s)
+    (two logit products, dQ_s, dK_s), plus 4 d_t for dQ_t and dK_t with teacher gradients."""
+    P = w.pairs_per_head() * w.B * w.H if pairs is None else pairs
+    fwd = (4.0 if js else 2.0) * P * (w.d_t + w.d_s)
+    bwd = 2.0 * P * (w.d_t + 3 * w.d_s) + (4.0 * P * w.d_t if teacher else 0.0)
+    return fwd, bwd
+
+
+def host_info():
+    """CPU model and BLAS library of the host (for the CPU baseline)."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas
 
 
 def cpu_baseline(w, budget_rows: int):
@@ -93,7 +131,9 @@ def cpu_baseline(w, budget_rows: int):
     fl_fwd = 2.0 * row_pairs * (w.d_t + w.d_s)
     fl_bwd = 2.0 * row_pairs * (w.d_t + 2 * w.d_s) + 2.0 * rk * w.d_s
     secs = t2 - t0
+    model, blas = host_info()
     return {"value": (fl_fwd + fl_bwd) / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "blas": blas,
             "sample": f"float64 oracle on head (0,0): forward of the last {budget_rows} query rows, backward "
                       f"(dQ_s of those rows, dK_s of the last {budget_rows} keys); {secs:.2f} s "
                       f"(fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s)",
@@ -206,6 +246,125 @@ def autograd_step(w, qt, kt, qs, ks, g, raw_ms: float, steps: int = 3, seg=None,
             "what": "attention_kl(...) then (kl * g).sum().backward(), bf16 gradients into q_s, k_s"}
 
 
+def _f32_or_bf16_inputs(w, dev):
+    """The workload's four inputs on the device (bf16 bit patterns shipped as int16, or float32)."""
+    import numpy as np
+    import torch
+    from attention_kl_amd import workloads as wl
+    if w.dtype == "bf16":
+        bits = wl.full_bf16_bits(w)
+        return tuple(torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in bits)
+    return tuple(torch.from_numpy(a).to(dev) for a in wl.full_f32(w))
+
+
+def warm_library(dev):
+    """One tiny forward and backward, so that loading the kernels' code objects (device memory of
+    their own) falls outside every measurement of what the path allocates."""
+    import torch
+    from attention_kl_amd import streamkl as S
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=dev)
+    kl, lt, ls = S.fwd(x, x, x, x, causal=True)
+    S.bwd(x, x, x, x, lt, ls, torch.ones_like(kl), causal=True, kl=kl, teacher_grads=True)
+    js, lt, ls, ht = S.js_fwd(x, x, x, x, causal=True)
+    S.js_bwd(x, x, x, x, lt, ls, js, ht, torch.ones_like(kl), causal=True)
+    torch.cuda.synchronize()
+
+
+def measured_peak(dev, iters: int = 4000, nblocks: int = 4096):
+    """Dense bf16 MFMA rate this GPU sustains (register operands, no memory traffic) and the shader
+    clock meanwhile, from the library's probe (include/streamkl_probe.h)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from attention_kl_amd import streamkl as S
+    sink = torch.empty(nblocks * 256, dtype=torch.float32, device=dev)
+    clk = torch.empty(2 * nblocks, dtype=torch.int64, device=dev)
+    khz = ctypes.c_double(0.0)
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):  # the first launch warms the clock up
+        assert S.lib().streamkl_probe_mfma(nblocks, iters, sink.data_ptr(), clk.data_ptr(), ctypes.byref(khz), s) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    assert S.lib().streamkl_probe_mfma(nblocks, iters, sink.data_ptr(), clk.data_ptr(), ctypes.byref(khz), s) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = nblocks * 4 * 4 * iters * 32768.0
+    c = clk.view(-1, 2).cpu().numpy().astype(np.float64)
+    ok = c[:, 1] > 0
+    ghz = float(np.median(c[ok, 0] / c[ok, 1]) * khz.value / 1e6) if ok.any() else None
+    return {"tflops": round(flops / ms / 1e9, 1), "clock_ghz": None if ghz is None else round(ghz, 3),
+            "published_tflops": MI355X_PEAK_BF16_TFLOPS,
+            "what": f"{nblocks} workgroups x 4 waves, 4 independent v_mfma_f32_32x32x16_bf16 chains of {iters} "
+                    "each on register operands; clock = shader-clock counter / constant-rate counter"}
+
+
+def time_step(w, dev, steps: int, warmup: int):
+    """Forward, dK_s, dQ_s of workload w, each launch timed with HIP events on the launch stream.
+
+    Returns per-kernel mean ms, the step's algorithmic TFLOP/s, fractions of the published and the
+    measured peak, the extra HBM the path holds and what the library itself allocated."""
+    import numpy as np
+    import torch
+    from attention_kl_amd import streamkl as S
+    from attention_kl_amd import workloads as wl
+    qt, kt, qs, ks = _f32_or_bf16_inputs(w, dev)
+    g = torch.from_numpy(wl.full_g(w)).to(dev)
+    kl = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    lt, ls = torch.empty_like(kl), torch.empty_like(kl)
+    dq = torch.empty((w.B, w.H, w.Nq, w.d_s), dtype=torch.float32, device=dev)
+    dk = torch.empty((w.B, w.H, w.Nk, w.d_s), dtype=torch.float32, device=dev)
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+
+    def step(ev=None):
+        ev and ev[0].record()
+        S.fwd(qt, kt, qs, ks, out=(kl, lt, ls), **kw)
+        ev and ev[1].record()
+        S.bwd_dk(qt, kt, qs, ks, lt, ls, g, out=dk, **kw)
+        ev and ev[2].record()
+        S.bwd_dq(qt, kt, qs, ks, lt, ls, g, out=dq, **kw)
+        ev and ev[3].record()
+
+    torch.cuda.synchronize()
+    free0, alloc0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated()
+    step()  # the first call: whatever the path allocates shows here
+    torch.cuda.synchronize()
+    lib_alloc = max(free0 - torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated() - alloc0)
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, k in
+          enumerate(("fwd", "bwd_dk", "bwd_dq"))}
+    step_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+    del qt, kt, qs, ks, g, kl, lt, ls, dq, dk
+    torch.cuda.empty_cache()
+    return ms, step_ms, int(lib_alloc)
+
+
+def config_entry(w, ms, step_ms, lib_alloc, peak=None, workspace_floats=0):
+    """The bench line's record of one workload: ms and algorithmic TFLOP/s of the forward, the backward
+    pair and the step, with their fractions of the published (and measured) peak."""
+    fwd_fl, bwd_fl = step_flops(w)
+    bwd_ms = ms["bwd_dk"] + ms["bwd_dq"]
+    mp = MI355X_PEAK_BF16_TFLOPS if w.dtype == "bf16" else MI355X_PEAK_FP32_MFMA_TFLOPS
+    e = {"fwd_ms": round(ms["fwd"], 4), "bwd_dk_ms": round(ms["bwd_dk"], 4), "bwd_dq_ms": round(ms["bwd_dq"], 4),
+         "bwd_ms": round(bwd_ms, 4), "step_ms": round(step_ms, 4),
+         "fwd_tflops": round(fwd_fl / ms["fwd"] / 1e9, 2), "bwd_tflops": round(bwd_fl / bwd_ms / 1e9, 2),
+         "step_tflops": round((fwd_fl + bwd_fl) / step_ms / 1e9, 2),
+         "fwd_frac": round(fwd_fl / ms["fwd"] / 1e9 / mp, 4), "bwd_frac": round(bwd_fl / bwd_ms / 1e9 / mp, 4),
+         "peak_tflops": mp, "dtype": w.dtype,
+         "extra_hbm_bytes": 12 * w.B * w.H * w.Nq + 4 * int(workspace_floats), "library_alloc_bytes": lib_alloc}
+    if peak and w.dtype == "bf16":
+        e["fwd_frac_of_measured_peak"] = round(fwd_fl / ms["fwd"] / 1e9 / peak["tflops"], 4)
+        e["bwd_frac_of_measured_peak"] = round(bwd_fl / bwd_ms / 1e9 / peak["tflops"], 4)
+    return e
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-pmc":
         # python bench.py --ingest-pmc <fetch counter csv> <write counter csv> [workload id]
@@ -219,6 +378,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload id in workloads.WORKLOADS (3 = b1h32n32768d128 causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other synthetic workloads (the line's `configs` object)")
+    ap.add_argument("--no-peak", action="store_true", help="skip the measured MFMA peak and clock")
     ap.add_argument("--cpu-rows", type=int, default=12288)
     ap.add_argument("--no-autograd", action="store_true",
                     help="skip timing the same step through the torch autograd wrapper (attention_kl_amd.loss)")
@@ -240,6 +402,8 @@ def main():
               "forward, but no multi-GPU run is implemented or measured here.", file=sys.stderr)
         sys.exit(2)
 
+    import ctypes
+
     import numpy as np
     import torch
 
@@ -250,12 +414,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S.lib()  # fail loudly if the library is missing
-    bits = wl.full_bf16_bits(w) if w.dtype == "bf16" else None
-    if bits is not None:
-        qt, kt, qs, ks = (torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in bits)
-        del bits
-    else:
-        qt, kt, qs, ks = (torch.from_numpy(a).to(dev) for a in wl.full_f32(w))
+    warm_library(dev)
+    qt, kt, qs, ks = _f32_or_bf16_inputs(w, dev)
     g = torch.from_numpy(wl.full_g(w)).to(dev)
     B, H = w.B, w.H
     hk_s = H if args.student_key_heads is None else args.student_key_heads
@@ -271,7 +431,9 @@ def main():
             sys.exit(2)
         lens = wl.length_mix(w.Nq, args.packed_mix)
         cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
-        seg = dict(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=max(lens), max_seqlen_k=max(lens))
+        # offsets built here, checked once below: the timed calls skip the binding's read-back
+        S.make_problem(*(x[0].permute(1, 0, 2) for x in (qt, kt, qs, ks)), w.causal, cu_seqlens_q=cu, cu_seqlens_k=cu)
+        seg = dict(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=max(lens), max_seqlen_k=max(lens), validate=False)
         qt, kt, qs, ks = (x[0].permute(1, 0, 2) for x in (qt, kt, qs, ks))  # [N, H, d] views, same memory
         g = g[0]
         per_seg = [(n * (n + 1) // 2) if w.causal else n * n for n in lens]
@@ -291,6 +453,10 @@ def main():
         sys.exit(2)
     dqt = torch.empty(lead + (H, w.Nq, w.d_t), dtype=torch.float32, device=dev) if teacher else None
     dkt = torch.empty(lead + (H, w.Nk, w.d_t), dtype=torch.float32, device=dev) if teacher else None
+    # the caller workspace the binding attaches for grouped keys (part of the path's extra HBM)
+    prob = S.make_problem(qt, kt, qs, ks, w.causal, w.scale_t, w.scale_s,
+                          **{k: v for k, v in seg.items()})
+    ws_floats = int(S.lib().streamkl_workspace_floats(ctypes.byref(prob)))
 
     def step(ev=None):
         if js:  # forward (two launches), then both student backward kernels
@@ -321,6 +487,13 @@ def main():
             if ev is not None:
                 ev[4].record()
 
+    # what the library path itself allocates: device memory taken around the first call (torch's
+    # caching allocator grows by the grouped-key workspace here, if any, and keeps it afterwards)
+    torch.cuda.synchronize()
+    free0, alloc0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated()
+    step()
+    torch.cuda.synchronize()
+    first_call_alloc = max(free0 - torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated() - alloc0)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -338,7 +511,7 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    extra_alloc = free0 - torch.cuda.mem_get_info()[0]
+    steady_alloc = free0 - torch.cuda.mem_get_info()[0]
     per = {"js_fwd": [], "js_bwd": []} if js else {"fwd": [], "bwd_dk": [], "bwd_dq": []}
     if teacher:
         per["bwd_teacher"] = []
@@ -357,24 +530,37 @@ def main():
     for k, v in per.items():
         ms = float(np.mean(v))
         fl = kernel_flops(w, k, pairs)
-        kern[k] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-                   "frac_of_bf16_peak": round(fl / ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4)}
+        kern[k] = {"ms": round(ms, 4), "issued_tflops": round(fl / ms / 1e9, 2),
+                   "issued_frac_of_bf16_peak": round(fl / ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4)}
     P = pairs if pairs is not None else w.pairs_per_head() * B * H
-    # algorithmic work of the step: the two logit products once (JS: twice, a streaming JS needs both
-    # log-sum-exps before its pass), then dQ_s and dK_s
-    fwd_fl, bwd_fl = (4.0 if js else 2.0) * P * (w.d_t + w.d_s), 2.0 * P * (w.d_t + 3 * w.d_s)
-    if teacher:  # plus dQ_t and dK_t
-        bwd_fl += 4.0 * P * w.d_t
+    fwd_fl, bwd_fl = step_flops(w, P, js=js, teacher=teacher)
     fwd_ms = kern["js_fwd" if js else "fwd"]["ms"]
     bwd_ms = kern["js_bwd"]["ms"] if js else kern["bwd_dk"]["ms"] + kern["bwd_dq"]["ms"]
     if teacher:
         bwd_ms += kern["bwd_teacher"]["ms"]
-    dominant = max((k for k in kern if k != "bwd_teacher"), key=lambda k: kern[k]["ms"])  # single launches
-    dom_fl = kernel_flops(w, dominant, pairs)
-    achieved = dom_fl / kern[dominant]["ms"] / 1e9
-    roof = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2), "peak": MI355X_PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MI355X_PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(dominant, w.name) if (hk_s == H and not seg and not js) else None}
+    plain = hk_s == H and not seg and not js and not teacher  # the kernels the traffic counters were taken on
+
+    def traffic(*ks_):
+        t = [load_traffic(k, w.name) for k in ks_]
+        return None if (not plain or any(x is None for x in t)) else sum(t)
+
+    peak = None if args.no_peak else measured_peak(dev)
+
+    def roof(kernel, fl, ms, tr):
+        a = fl / ms / 1e9
+        r = {"bound": "mfma", "kernel": kernel, "achieved": round(a, 2), "peak": MI355X_PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(a / MI355X_PEAK_BF16_TFLOPS, 4), "traffic": tr,
+             "flops_per_launch": fl, "ms_per_launch": round(ms, 4)}
+        if peak:
+            r["frac_of_measured_peak"] = round(a / peak["tflops"], 4)
+        return r
+
+    # the dominant kernel is the backward pair (its two launches together carry the backward's work,
+    # each product counted once); the forward, the spec kernel, gets its own entry
+    roof_bwd = roof("bwd_dk+bwd_dq" if not js else "js_bwd", bwd_fl if not teacher else step_flops(w, P)[1],
+                    kern["js_bwd"]["ms"] if js else kern["bwd_dk"]["ms"] + kern["bwd_dq"]["ms"],
+                    traffic("bwd_dk", "bwd_dq"))
+    roof_fwd = roof("js_fwd" if js else "fwd", fwd_fl, fwd_ms, traffic("fwd"))
     value = (fwd_fl + bwd_fl) / step_ms / 1e9
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -389,13 +575,36 @@ def main():
         "fwd_ms": fwd_ms, "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_fl / fwd_ms / 1e9, 2), "bwd_tflops": round(bwd_fl / bwd_ms / 1e9, 2),
         "fwd_frac_of_bf16_peak": round(fwd_fl / fwd_ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4),
-        "extra_hbm_bytes": 12 * B * H * w.Nq, "library_alloc_bytes": int(extra_alloc),
+        "bwd_frac_of_bf16_peak": round(bwd_fl / bwd_ms / 1e9 / MI355X_PEAK_BF16_TFLOPS, 4),
+        "extra_hbm_bytes": 12 * B * H * w.Nq + (4 * B * H * w.Nq if js else 0) + 4 * ws_floats,
+        "workspace_bytes": 4 * ws_floats,
+        "library_alloc_bytes": int(max(first_call_alloc, steady_alloc)),
         "materialised_bytes_avoided": 2 * 4 * P,
         "kernels": kern, "wall_s_timed": round(wall, 3),
-        "roofline": roof,
+        "roofline": roof_bwd,
+        "roofline_fwd": roof_fwd,
     }
+    if peak:
+        out["measured_peak"] = peak
+    plain_line = plain and args.workload == 3
     if not args.no_autograd:
         out["autograd"] = autograd_step(w, qt, kt, qs, ks, g, step_ms, seg=seg, direction=args.divergence)
+    del qt, kt, qs, ks, g, kl, lt, ls, dq, dk, dqt, dkt
+    torch.cuda.empty_cache()
+    if plain_line and not args.no_configs:
+        # the same step on every synthetic workload; this line's own numbers stand for workload 3
+        cfg = {}
+        for wid in sorted(wl.WORKLOADS):
+            wi = wl.WORKLOADS[wid]
+            if wid == args.workload:
+                ms = {k: kern[k]["ms"] for k in ("fwd", "bwd_dk", "bwd_dq")}
+                cfg[wi.name] = config_entry(wi, ms, step_ms, out["library_alloc_bytes"], peak)
+                continue
+            print(f"bench: timing {wi.name}", file=sys.stderr, flush=True)
+            big = wi.pairs_per_head() * wi.B * wi.H > 1e10
+            ms, sms, la = time_step(wi, dev, steps=min(args.steps, 5) if big else args.steps, warmup=min(args.warmup, 2))
+            cfg[wi.name] = config_entry(wi, ms, sms, la, peak)
+        out["configs"] = cfg
     if not args.no_cpu_baseline and not seg and not js:  # the CPU sample is of the dense KL workload's rows
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)

@@ -188,7 +188,7 @@ def test_python_binding_describes_a_packed_batch():
     k = torch.zeros(350, 2, 64)    # [N, Hk, d]
     cu_q = torch.tensor([0, 100, 100, 300], dtype=torch.int32)
     cu_k = torch.tensor([0, 150, 170, 350], dtype=torch.int32)
-    p = S.make_problem(q, k, q, k, True, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+    p = S.make_problem(q, k, q, k, False, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
     assert (p.B, p.H, p.Nq, p.Nk, p.Hk_t) == (3, 4, 300, 350, 2)
     assert (p.max_seqlen_q, p.max_seqlen_k) == (200, 180)
     assert list(p.stride_qt)[1:] == [64, 4 * 64]  # head and row strides of [N, H, d] (the b stride is unused)
@@ -199,6 +199,38 @@ def test_python_binding_describes_a_packed_batch():
         S.make_problem(q, k, q, k, True, cu_seqlens_q=cu_q.long(), cu_seqlens_k=cu_k)
     with pytest.raises(ValueError):  # packed inputs are [N, heads, d]
         S.make_problem(q[None], k[None], q[None], k[None], True, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+
+
+def test_python_binding_rejects_invalid_offsets():
+    """Offsets that break the packed-batch rules raise in the binding, before any launch (CPU
+    tensors here: the check is the read-back the binding makes anyway)."""
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(300, 2, 64)
+    k = torch.zeros(350, 2, 64)
+    t = lambda v: torch.tensor(v, dtype=torch.int32)
+    good_q, good_k = t([0, 100, 100, 300]), t([0, 150, 150, 350])
+    S.make_problem(q, k, q, k, True, cu_seqlens_q=good_q, cu_seqlens_k=good_k)
+    bad = [
+        (t([-1, 100, 100, 300]), good_k, {}),     # negative start
+        (t([0, 100, 90, 300]), good_k, {}),       # decreasing
+        (good_q, t([0, 150, 170, 351]), {}),      # past the packed key rows
+        (t([0, 100, 100, 301]), good_k, {}),      # past the packed query rows
+        (t([0, 100, 110, 300]), t([0, 150, 150, 350]), {}),  # a segment with queries and no keys
+        (t([0, 100, 100, 300]), t([0, 99, 170, 350]), {}),   # causal: fewer keys than queries
+        (good_q, good_k, dict(max_seqlen_q=150)),  # the grid would miss rows of the longest segment
+    ]
+    for cq, ck, kw in bad:
+        with pytest.raises(ValueError):
+            S.make_problem(q, k, q, k, True, cu_seqlens_q=cq, cu_seqlens_k=ck, **kw)
+        with pytest.raises(ValueError):
+            S.fwd(q, k, q, k, causal=True, cu_seqlens_q=cq, cu_seqlens_k=ck, **kw)
+    # not causal: fewer keys than queries is a valid segment
+    S.make_problem(q, k, q, k, False, cu_seqlens_q=t([0, 100, 100, 300]), cu_seqlens_k=t([0, 99, 170, 350]))
+    with pytest.raises(ValueError):  # skipping the read-back needs the maxima
+        S.make_problem(q, k, q, k, True, cu_seqlens_q=good_q, cu_seqlens_k=good_k, validate=False)
+    p = S.make_problem(q, k, q, k, True, cu_seqlens_q=good_q, cu_seqlens_k=good_k, validate=False,
+                       max_seqlen_q=200, max_seqlen_k=180)
+    assert (p.max_seqlen_q, p.max_seqlen_k) == (200, 180)
 
 
 def test_js_argument_rules():

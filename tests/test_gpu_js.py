@@ -12,7 +12,7 @@ from attention_kl_amd import loss as L
 from attention_kl_amd import streamkl as S
 from attention_kl_amd import workloads as wl
 
-from parity import (device_inputs, device_inputs_bf16_bits, grad_floor, ratio_kl, ratio_lse, ratio_rows, report,
+from parity import (all_pass, device_inputs, device_inputs_bf16_bits, grad_floor, ratio_kl, ratio_lse, ratio_rows, report,
                     rtol_of)
 
 pytestmark = pytest.mark.gpu
@@ -27,6 +27,8 @@ def _check(w, teacher, g=None):
     grads = S.js_bwd(qt, kt, qs, ks, lt, ls, js, ht, torch.from_numpy(g).cuda(), causal=w.causal,
                      teacher_grads=teacher, scale_t=w.scale_t, scale_s=w.scale_s)
     torch.cuda.synchronize()
+    for x in (js, ht, lt, ls, *grads):
+        assert x is None or bool(torch.isfinite(x).all()), "non-finite output"
     h64 = [a.astype(np.float64) for a in host]
     rjs, rht, _, rlt, rls = oracle.js_forward(*h64, w.scale_t, w.scale_s, w.causal)
     rg = oracle.js_backward(*h64, w.scale_t, w.scale_s, w.causal, g.astype(np.float64), teacher=teacher)
@@ -42,7 +44,7 @@ def _check(w, teacher, g=None):
                  dk_t=ratio_rows(c(grads[3]), rg["dk_t"], rt, grad_floor(0.5 * w.scale_t, ag, h64[0])))
     msg = report(w.name + " js", **r)
     print(msg, flush=True)
-    assert max(r.values()) <= 1.0, msg
+    assert all_pass(r), msg
     jsv = c(js)
     assert np.all(jsv >= -1e-6) and np.all(jsv <= math.log(2.0) + 1e-6)
 
@@ -69,6 +71,21 @@ def test_js_signed_row_weights():
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 7])))
     g = rng.standard_normal((w.B, w.H, w.Nq)).astype(np.float32)
     g[..., ::5] = 0.0
+    _check(w, teacher=True, g=g)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_js_zero_row_weights_stay_finite(dtype):
+    """Rows with g = 0 (a masked or sliced reduction): the key owner folds log2|g| into the streamed
+    queries' exponents, and for such rows both probabilities must come out as exact zeros without
+    an inf - inf in the JS log-ratio.  Whole 32-row tiles of zeros, single zero rows and signed
+    weights in one problem; every gradient finite and equal to the oracle's."""
+    w = wl.custom(1, 2, 200, 200, 128, 64, True, dtype=dtype, recipe="independent", seed=67)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 8])))
+    g = rng.uniform(0.5, 1.5, (w.B, w.H, w.Nq)).astype(np.float32)
+    g[..., 32:96] = 0.0
+    g[..., ::7] = 0.0
+    g[..., 150:160] *= -1.0
     _check(w, teacher=True, g=g)
 
 
@@ -122,7 +139,7 @@ def test_js_on_packed_and_grouped_inputs():
         q0 += n
     msg = report("packed js", **worst)
     print(msg, flush=True)
-    assert max(worst.values()) <= 1.0, msg
+    assert all_pass(worst), msg
 
 
 def test_autograd_js_direction():
@@ -176,7 +193,7 @@ def test_js_grouped_keys_with_teacher_gradients(dtype):
              dk_t=ratio_rows(c(grads[3]), sumg(rg["dk_t"], hk_t), rt, grad_floor(0.5 * w.scale_t, g, h64[0])))
     msg = report(f"js grouped {dtype}", **r)
     print(msg, flush=True)
-    assert max(r.values()) <= 1.0, msg
+    assert all_pass(r), msg
 
 
 def test_js_b1h32n32768_causal_full_size_sampled():
@@ -220,4 +237,4 @@ def test_js_b1h32n32768_causal_full_size_sampled():
         worst["dk_s"] = max(worst.get("dk_s", 0), ratio_rows(dk[b, h, keys].cpu().numpy(), rg["dk_s"], rt))
     msg = report(w.name + " js", **worst)
     print(msg, flush=True)
-    assert max(worst.values()) <= 1.0, msg
+    assert all_pass(worst), msg

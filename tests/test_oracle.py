@@ -310,3 +310,42 @@ def test_scale_folding_invariance():
     r2 = forward_head(qt * 2, kt, qs * 4, ks, 0.25, 0.0625, True)
     for x, y in zip(r1, r2):
         np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- the row-window runner of the GPU tests
+@pytest.mark.parametrize("nq,nk,causal,r0,teacher,js", [
+    (300, 300, True, 0, True, False),
+    (300, 300, True, 130, False, False),
+    (257, 400, True, 64, True, False),      # bottom-right alignment with more keys than queries
+    (200, 150, False, 0, True, False),
+    (300, 300, True, 0, True, True),
+    (220, 300, True, 100, False, True),
+])
+def test_row_window_runner_reassembles_the_whole_head(nq, nk, causal, r0, teacher, js):
+    """The full-size GPU tests run the oracle on row blocks of a head in threads (each block a
+    problem of its own rows and their keys) and sum the dK partials; here the result must equal the
+    oracle on the whole head to float64 rounding, for every row of the window and every key whose dK
+    the window completes."""
+    import oracle
+    from parity import oracle_window
+    rng = np.random.default_rng(nq + nk + r0)
+    head = rand_head(rng, nq, nk, 16, 8)
+    g = rng.uniform(0.5, 1.5, nq)
+    st, ss = 0.3, 0.4
+    win = oracle_window(head, st, ss, causal, g, r0=r0, teacher=teacher, js=js, block=48, workers=3)
+    rows = np.arange(r0, nq)
+    if js:
+        ref_f = oracle.js_forward_head(*head, st, ss, causal)
+        names = ("js", "js_t", "js_s", "lse_t", "lse_s")
+        ref_b = oracle.js_backward_head(*head, st, ss, causal, g, teacher=teacher)
+    else:
+        ref_f = oracle.forward_head(*head, st, ss, causal)
+        names = ("kl", "lse_t", "lse_s")
+        ref_b = backward_head(*head, st, ss, causal, g, teacher=teacher)
+    for n, v in zip(names, ref_f):
+        np.testing.assert_allclose(win[n], v[rows], rtol=1e-12, atol=1e-13)
+    k0 = win["k0"]
+    assert k0 == (r0 + nk - nq if causal else 0)
+    for sd in (("s", "t") if teacher else ("s",)):
+        np.testing.assert_allclose(win["dq_" + sd], ref_b["dq_" + sd][rows], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(win["dk_" + sd], ref_b["dk_" + sd][k0:], rtol=1e-11, atol=1e-13)
