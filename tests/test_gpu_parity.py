@@ -15,7 +15,7 @@ import oracle
 from attention_kl_amd import streamkl as S
 from attention_kl_amd import workloads as wl
 
-from parity import (all_pass, device_inputs, device_inputs_bf16_bits, grad_floor, ratio_kl, ratio_lse, ratio_rows, report,
+from parity import (all_pass, oracle_window, worst_of, device_inputs, device_inputs_bf16_bits, grad_floor, ratio_kl, ratio_lse, ratio_rows, report,
                     rtol_of)
 
 pytestmark = pytest.mark.gpu
@@ -157,25 +157,54 @@ def test_library_allocates_nothing():
     assert sum(o.numel() * 4 for o in outs) == 12 * w.B * w.H * w.Nq
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled
-def _sampled(w, heads, rows, keys, teacher=False):
-    """teacher: the teacher pair alone (dq_t, dk_t from one streamkl_bwd call), else the student pair."""
-    print(f"case {w.name} (full size, sampled) teacher={teacher}", flush=True)
+# ------------------------------------------------------------------ full-size workloads
+def _full_size(w, teacher=False, whole=(), window=(), r0=None, lead=0, sampled=(), rows=(), keys=(),
+               check_alloc=False):
+    """One full-size workload run as the bench runs it (streamkl_fwd, then streamkl_bwd_dk and
+    streamkl_bwd_dq; teacher: the teacher pair alone from one streamkl_bwd call, as the bench's
+    teacher step), then compared with the oracle:
+      whole:   heads compared over every row (KL, LSE_t, LSE_s, dQ) and every key (dK);
+      window:  heads compared over rows r0 .. Nq-1 and keys r0 + Nk - Nq .. Nk-1 (causal: every row that
+               sees those keys lies in the window, so their dK is complete), plus, when lead > 0, the
+               forward and dQ of rows 0 .. lead-1;
+      sampled: heads compared on the given rows and keys;
+    and properties checked over every row of every head.  check_alloc: the calls allocate no device
+    memory (outputs preallocated; the path's extra HBM is the 12 bytes per row of KL, LSE_t, LSE_s)."""
+    print(f"case {w.name} (full size) teacher={teacher} whole={whole} window={window} r0={r0}", flush=True)
     dev_in = device_inputs_bf16_bits(w)
     qt, kt, qs, ks = dev_in
-    kl, lt, ls = S.fwd(qt, kt, qs, ks, causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
-    g = torch.from_numpy(wl.full_g(w)).cuda()
-    grads = S.bwd(qt, kt, qs, ks, lt, ls, g, causal=w.causal, kl=kl, teacher_grads=teacher, student_grads=not teacher,
-                  scale_t=w.scale_t, scale_s=w.scale_s)
-    dq, dk = (grads[2], grads[3]) if teacher else (grads[0], grads[1])
-    assert (grads[0] is None) == teacher and (grads[2] is None) != teacher
-    xq, xk = (qt, kt) if teacher else (qs, ks)  # the side being differentiated
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    gh = wl.full_g(w)
+    g = torch.from_numpy(gh).cuda()
     side = "t" if teacher else "s"
+    dx = w.d_t if teacher else w.d_s
+    kl, lt, ls = (torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda") for _ in range(3))
+    dq = torch.empty((w.B, w.H, w.Nq, dx), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.B, w.H, w.Nk, dx), dtype=torch.float32, device="cuda")
+    if check_alloc:  # the same kernels once at a small size: code objects and the runtime's per-kernel
+        # private memory are set up before the measurement
+        sm = tuple(x[:, :1, :256].contiguous() for x in dev_in)
+        kls, lts, lss = S.fwd(*sm, **kw)
+        S.bwd(*sm, lts, lss, g[:, :1, :256].contiguous(), kl=kls, teacher_grads=teacher, student_grads=not teacher,
+              **kw)
+        torch.cuda.synchronize()
+        free0, alloc0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated()
+    S.fwd(qt, kt, qs, ks, out=(kl, lt, ls), **kw)
+    if teacher:
+        S.bwd(qt, kt, qs, ks, lt, ls, g, kl=kl, teacher_grads=True, student_grads=False, out=[None, None, dq, dk], **kw)
+    else:
+        S.bwd_dk(qt, kt, qs, ks, lt, ls, g, out=dk, **kw)
+        S.bwd_dq(qt, kt, qs, ks, lt, ls, g, out=dq, **kw)
     torch.cuda.synchronize()
+    if check_alloc:
+        assert torch.cuda.mem_get_info()[0] == free0, "the path allocated device memory"
+        assert torch.cuda.memory_allocated() == alloc0
+        assert sum(x.numel() * x.element_size() for x in (kl, lt, ls)) == 12 * w.B * w.H * w.Nq
+    xq, xk = (qt, kt) if teacher else (qs, ks)  # the side being differentiated
     rt = rtol_of(w)
     # properties over every row
     klc = kl.cpu().numpy()
-    assert np.all(np.isfinite(klc)) and np.all(torch.isfinite(dq).cpu().numpy()) and bool(torch.isfinite(dk).all())
+    assert np.all(np.isfinite(klc)) and bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all())
     assert klc.min() >= -1e-4
     if w.causal:
         assert np.abs(klc[:, :, 0]).max() <= 1e-5  # one allowed key: KL = 0
@@ -186,19 +215,33 @@ def _sampled(w, heads, rows, keys, teacher=False):
         (xk.double().norm(dim=3) * dk.double().norm(dim=3)).sum(dim=2)
     assert float(((lhs - rhs).abs() / norm).max()) <= rt
     worst = {}
-    gh = wl.full_g(w)
-    for (b, h) in heads:
+    c = lambda x: x.cpu().numpy()
+
+    def compare(tag, b, h, r, k, ref):
+        worst_of(worst, "kl" + tag, ratio_kl(klc[b, h, r], ref["kl"], rt))
+        worst_of(worst, "lse" + tag, ratio_lse(c(lt[b, h, r]), ref["lse_t"], rt), ratio_lse(c(ls[b, h, r]), ref["lse_s"], rt))
+        worst_of(worst, "dq_" + side + tag, ratio_rows(c(dq[b, h, r]), ref["dq_" + side], rt))
+        if k is not None:
+            worst_of(worst, "dk_" + side + tag, ratio_rows(c(dk[b, h, k]), ref["dk_" + side], rt))
+
+    for (b, h) in whole:
+        hh = wl.head_f64(w, b, h)
+        ref = oracle_window(hh, w.scale_t, w.scale_s, w.causal, gh[b, h], teacher=teacher)
+        compare("(whole)", b, h, slice(None), slice(None), ref)
+    for (b, h) in window:
+        hh = wl.head_f64(w, b, h)
+        ref = oracle_window(hh, w.scale_t, w.scale_s, w.causal, gh[b, h], r0=r0, teacher=teacher)
+        compare(f"(rows {r0}:)", b, h, slice(r0, None), slice(ref["k0"], None), ref)
+        if lead:
+            ref = oracle_window(tuple(x[:lead] for x in hh), w.scale_t, w.scale_s, w.causal, gh[b, h, :lead],
+                                teacher=teacher)
+            compare(f"(rows :{lead})", b, h, slice(0, lead), None, ref)
+    for (b, h) in sampled:
         hh = wl.head_f64(w, b, h)
         rkl, rlt, rls = oracle.forward_head(*hh, w.scale_t, w.scale_s, w.causal, rows=rows)
-        worst["kl"] = max(worst.get("kl", 0), ratio_kl(klc[b, h, rows], rkl, rt))
-        worst["lse"] = max(worst.get("lse", 0), ratio_lse(lt[b, h, rows].cpu().numpy(), rlt, rt),
-                           ratio_lse(ls[b, h, rows].cpu().numpy(), rls, rt))
         rg = oracle.backward_head(*hh, w.scale_t, w.scale_s, w.causal, gh[b, h], teacher=teacher, rows=rows,
                                   keys=keys)
-        worst["dq_" + side] = max(worst.get("dq_" + side, 0),
-                                  ratio_rows(dq[b, h, rows].cpu().numpy(), rg["dq_" + side], rt))
-        worst["dk_" + side] = max(worst.get("dk_" + side, 0),
-                                  ratio_rows(dk[b, h, keys].cpu().numpy(), rg["dk_" + side], rt))
+        compare("(sampled)", b, h, rows, keys, dict(kl=rkl, lse_t=rlt, lse_s=rls, **rg))
     msg = report(w.name, **worst)
     print(msg, flush=True)
     assert all_pass(worst), msg
@@ -209,29 +252,34 @@ def _rows(n, seed):
     return sorted(set([0, 1, 2, 31, 32, 63, 64, 127, 128, n // 2, n - 2, n - 1] + list(r)))
 
 
-def test_b1h32n32768_causal_full_size_sampled():
+def test_b1h32n32768_causal_whole_head():
+    """The bench workload: head 0 over all 32768 rows and keys (key j's dK sums a causal stream of
+    32768 - j query rows, up to 1024 tiles), and sampled rows and keys of two more heads."""
     w = wl.WORKLOADS[3]
     n = w.Nq
-    _sampled(w, [(0, 0), (0, 17), (0, 31)], _rows(n, 3), [n - 1, n - 2, n - 31, n - 32, n - 64, n - 65, n - 130])
+    _full_size(w, whole=[(0, 0)], sampled=[(0, 17), (0, 31)], rows=_rows(n, 3),
+               keys=[0, 1, 31, 32, n // 4, n // 2, n - 130, n - 1])
 
 
-def test_b1h32n32768_causal_teacher_gradients_full_size_sampled():
-    """The teacher pair at the bench size, launched as the bench's teacher-gradient step launches it."""
+def test_b1h32n32768_causal_teacher_gradients_whole_head():
+    """The teacher pair at the bench size, launched as the bench's teacher-gradient step launches it:
+    head 3 over every row and key."""
     w = wl.WORKLOADS[3]
-    n = w.Nq
-    _sampled(w, [(0, 3), (0, 30)], _rows(n, 6), [n - 1, n - 2, n - 31, n - 32, n - 64, n - 65, n - 130], teacher=True)
+    _full_size(w, teacher=True, whole=[(0, 3)])
 
 
-def test_b4h8n8192_two_head_dims_full_size_sampled():
+def test_b4h8n8192_two_head_dims_whole_heads():
+    """Teacher d = 128, student d = 64, not causal: two whole heads (every key sees all 8192 rows)."""
     w = wl.WORKLOADS[4]
-    n = w.Nk
-    _sampled(w, [(0, 0), (3, 7)], _rows(w.Nq, 4), [0, 1, 63, 64, 4095, n - 1])
+    _full_size(w, whole=[(0, 0), (3, 7)])
 
 
-def test_b1h8n131072_causal_full_size_sampled():
+def test_b1h8n131072_causal_long_streams_and_no_allocation():
+    """The 131072-row workload as the bench runs it, with no device allocation by the path: head 5
+    over its last 16384 rows and keys (dK of key 131072 - 16384 sums a stream of 16384 rows, 512
+    tiles; every dQ row there streams over 114688 or more keys) and its first 1024 rows."""
     w = wl.WORKLOADS[5]
-    n = w.Nq
-    _sampled(w, [(0, 0), (0, 5)], _rows(n, 5), [n - 1, n - 2, n - 33, n - 100])
+    _full_size(w, window=[(0, 5)], r0=w.Nq - 16384, lead=1024, check_alloc=True)
 
 
 @pytest.mark.parametrize("w", [wl.custom(1, 2, 300, 300, 128, 128, True, recipe="independent", seed=41),

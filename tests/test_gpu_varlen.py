@@ -155,15 +155,16 @@ def test_autograd_on_a_packed_batch():
     assert abs(loss.item() - total) <= 2e-3 * max(abs(total), 1e-3) * 4
 
 
-def test_packed_length_mix_full_size_sampled():
+def test_packed_length_mix_full_size():
     """The bench workload's 32768 rows cut into the seeded length mix, as `bench.py --packed-mix 1`
     launches it (the workload's generated tensors viewed as [N, H, d]): each segment is the problem
-    of its own rows and keys, checked on sampled rows and keys of three segments and two heads."""
+    of its own rows and keys, checked over every row and key of three segments (the longest, the
+    shortest, the last) in two heads."""
     from parity import device_inputs_bf16_bits, rtol_of
     w = wl.WORKLOADS[3]
     lens = wl.length_mix(w.Nq, 1)
     cu_h = np.concatenate([[0], np.cumsum(lens)])
-    print(f"case {w.name} packed mix 1: {len(lens)} segments (full size, sampled)", flush=True)
+    print(f"case {w.name} packed mix 1: {len(lens)} segments (full size)", flush=True)
     qt, kt, qs, ks = (x[0].permute(1, 0, 2) for x in device_inputs_bf16_bits(w))
     cu = torch.tensor(cu_h, dtype=torch.int32, device="cuda")
     kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s, cu_seqlens_q=cu, cu_seqlens_k=cu,
@@ -178,21 +179,17 @@ def test_packed_length_mix_full_size_sampled():
     assert np.abs(klc[:, cu_h[:-1]]).max() <= 1e-5  # each segment's first row sees one key: KL = 0
     rt = rtol_of(w)
     worst = {}
+    c = lambda x: x.cpu().numpy()
+    from parity import oracle_window, worst_of
     for s in sorted({int(np.argmax(lens)), int(np.argmin(lens)), len(lens) - 1}):
         a, m = int(cu_h[s]), int(lens[s])
-        rows = sorted(set([0, 1, 31, 32, m // 2, m - 2, m - 1]))
-        keys = sorted(set([m - 1, m - 2, m - 33, m - 64]))
-        for h in (0, 19):
-            hh = [x[a:a + m] for x in wl.head_f64(w, 0, h)]
-            rkl, rlt, rls = oracle.forward_head(*hh, w.scale_t, w.scale_s, w.causal, rows=rows)
-            rg = oracle.backward_head(*hh, w.scale_t, w.scale_s, w.causal, gh[0, h, a:a + m], rows=rows, keys=keys)
-            r = [a + i for i in rows]
-            k = [a + i for i in keys]
-            worst["kl"] = max(worst.get("kl", 0), ratio_kl(klc[h, r], rkl, rt))
-            worst["lse"] = max(worst.get("lse", 0), ratio_lse(lt[h, r].cpu().numpy(), rlt, rt),
-                               ratio_lse(ls[h, r].cpu().numpy(), rls, rt))
-            worst["dq_s"] = max(worst.get("dq_s", 0), ratio_rows(dq[h, r].cpu().numpy(), rg["dq_s"], rt))
-            worst["dk_s"] = max(worst.get("dk_s", 0), ratio_rows(dk[h, k].cpu().numpy(), rg["dk_s"], rt))
+        for h in (0, 19):  # the whole segment: every row and key
+            hh = tuple(x[a:a + m] for x in wl.head_f64(w, 0, h))
+            ref = oracle_window(hh, w.scale_t, w.scale_s, w.causal, gh[0, h, a:a + m])
+            worst_of(worst, "kl", ratio_kl(klc[h, a:a + m], ref["kl"], rt))
+            worst_of(worst, "lse", ratio_lse(c(lt[h, a:a + m]), ref["lse_t"], rt), ratio_lse(c(ls[h, a:a + m]), ref["lse_s"], rt))
+            worst_of(worst, "dq_s", ratio_rows(c(dq[h, a:a + m]), ref["dq_s"], rt))
+            worst_of(worst, "dk_s", ratio_rows(c(dk[h, a:a + m]), ref["dk_s"], rt))
     msg = report(f"{w.name} packed mix 1", **worst)
     print(msg, flush=True)
     assert all_pass(worst), msg
