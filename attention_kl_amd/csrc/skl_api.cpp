@@ -11,6 +11,8 @@
 
 #include "skl_kernels.hpp"
 
+static_assert(skl::kScratchFloats == STREAMKL_NOALLOC_SCRATCH_FLOATS, "scratch size of the header");
+
 namespace {
 
 constexpr int64_t kMaxDim = 0x7fffffff;
@@ -267,6 +269,28 @@ int streamkl_js_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_
   return STREAMKL_OK;
 }
 
+int streamkl_bwd_noalloc(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s,
+                         const void* k_s, const float* lse_t, const float* lse_s, const float* kl, const float* g,
+                         float* dq_s, float* dk_s, float* dq_t, float* dk_t, void* hip_stream) {
+  if (p != nullptr && p->workspace != nullptr) return STREAMKL_ERR_INVALID;  // the scratch takes its place
+  bool empty = false;
+  int st = check_problem(p, &empty);
+  if (st != STREAMKL_OK) return st;
+  streamkl_problem_t q = *p;
+  q.workspace_floats = 0;
+  // the arrangement streamkl_bwd takes with a caller workspace of the size streamkl_workspace_floats
+  // reports, so both entry points give the same bits
+  const int64_t need = streamkl_workspace_floats(p);
+  if (need > skl::kScratchFloats) return STREAMKL_ERR_SCRATCH;
+  if (need > 0 && !empty) {
+    float* ptr = nullptr;
+    if (skl::scratch_address(&ptr) != hipSuccess) return STREAMKL_ERR_LAUNCH;
+    q.workspace = ptr;  // the device copy's address, never the host-side symbol
+    q.workspace_floats = need;
+  }
+  return streamkl_bwd(&q, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g, dq_s, dk_s, dq_t, dk_t, hip_stream);
+}
+
 const char* streamkl_status_string(int status) {
   switch (status) {
     case STREAMKL_OK:
@@ -277,6 +301,9 @@ const char* streamkl_status_string(int status) {
       return "STREAMKL_ERR_UNSUPPORTED: head dim, dtype or alignment not supported";
     case STREAMKL_ERR_LAUNCH:
       return "STREAMKL_ERR_LAUNCH: HIP kernel launch failed";
+    case STREAMKL_ERR_SCRATCH:
+      return "STREAMKL_ERR_SCRATCH: the problem needs more scratch than the library's static array holds "
+             "(pass a workspace to streamkl_bwd instead)";
     default:
       return "STREAMKL: unknown status";
   }

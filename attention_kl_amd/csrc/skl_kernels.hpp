@@ -100,6 +100,11 @@ inline int split_count(int64_t group, int64_t blocks, int64_t part, const float*
   return n < 2 ? 1 : (int)n;
 }
 
+// Scratch of the allocation-free backward (skl_scratch.hip): kScratchFloats floats per GPU, resolved
+// for the current device by scratch_address (hipGetSymbolAddress on the first call per device).
+constexpr int64_t kScratchFloats = (int64_t)16 << 20;  // 64 MiB
+hipError_t scratch_address(float** out);
+
 // dtype: 0 fp32, 1 bf16.  d_t, d_s in {64, 128}.  Return hipErrorInvalidValue for
 // combinations that are not built (the C ABI rejects them before calling).
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int d_t, int d_s, bool causal, hipStream_t s);

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libstreamkl.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 HEADER = os.path.join(INCLUDE, "streamkl.h")
 
-OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_SCRATCH = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_FLOATS = 16 << 20  # STREAMKL_NOALLOC_SCRATCH_FLOATS
 FP32, BF16 = 0, 1
 
 
@@ -72,12 +73,13 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.streamkl_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.streamkl_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.streamkl_bwd_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.streamkl_bwd_dq.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.streamkl_bwd_dk.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.streamkl_js_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.streamkl_js_bwd.argtypes = [_P] + [_vp] * 14
         for f in ("streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk", "streamkl_js_fwd",
-                  "streamkl_js_bwd", "streamkl_version"):
+                  "streamkl_js_bwd", "streamkl_bwd_noalloc", "streamkl_version"):
             getattr(L, f).restype = ctypes.c_int
         L.streamkl_workspace_floats.argtypes = [_P]
         L.streamkl_workspace_floats.restype = ctypes.c_int64
@@ -280,6 +282,20 @@ def bwd(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, kl=None, teacher_grads
                               _ptr(kl), _ptr(g), _ptr(dq_s), _ptr(dk_s), _ptr(dq_t), _ptr(dk_t), _stream(stream)),
            "streamkl_bwd")
     return dq_s, dk_s, dq_t, dk_t
+
+
+def bwd_noalloc(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, out, kl=None, scale_t=None, scale_s=None,
+                stream=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True):
+    """streamkl_bwd_noalloc: bwd's gradients into the caller's `out` = [dq_s, dk_s, dq_t, dk_t] (a pair
+    None = not computed), with the grouped-key workspace taken from the library's static per-GPU
+    scratch instead of an allocation.  Nothing here or in the library allocates device memory."""
+    p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     max_seqlen_k, validate)
+    out = list(out) + [None] * (4 - len(out))
+    _check(lib().streamkl_bwd_noalloc(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(lse_t),
+                                      _ptr(lse_s), _ptr(kl), _ptr(g), *(_ptr(x) for x in out), _stream(stream)),
+           "streamkl_bwd_noalloc")
+    return tuple(out)
 
 
 def bwd_dq(qt, kt, qs, ks, lse_t, lse_s, g, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None,

@@ -27,7 +27,8 @@
  *    allocates nothing, frees nothing and keeps no state: the only HBM it touches
  *    beyond the inputs is the outputs the caller passes (S8: no O(Nq*Nk) buffer),
  *    plus, for grouped key heads only, an optional caller workspace (see
- *    streamkl_workspace_floats).
+ *    streamkl_workspace_floats) or, for streamkl_bwd_noalloc, a fixed scratch array
+ *    the library holds on each GPU.
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and
  *    is asynchronous: the call returns after launch.  Kernel faults surface at the
  *    caller's next synchronisation, as for any HIP launch.
@@ -35,8 +36,9 @@
  *    into), so they need no zeroing.  Outputs must not alias inputs.
  *  - Return value: STREAMKL_OK or an error code; nothing is launched when an
  *    argument check fails.  Nothing is printed and nothing is thrown.
- *  - Thread-safe: calls share no mutable state.  Results are bitwise
- *    deterministic (no atomics; fixed reduction order).
+ *  - Thread-safe: calls share no mutable state (streamkl_bwd_noalloc excepted: its
+ *    calls on one GPU share that GPU's scratch).  Results are bitwise deterministic
+ *    (no atomics; fixed reduction order).
  */
 #ifndef STREAMKL_H
 #define STREAMKL_H
@@ -47,8 +49,8 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10400 /* 1.4.0: workspace for grouped keys; 1.3.0: Jensen-Shannon; 1.2.0: packed
-                                  batches; 1.1.0: key heads */
+#define STREAMKL_VERSION 10500 /* 1.5.0: allocation-free backward; 1.4.0: workspace for grouped keys;
+                                  1.3.0: Jensen-Shannon; 1.2.0: packed batches; 1.1.0: key heads */
 
 typedef enum {
   STREAMKL_FP32 = 0, /* inputs float32; products on fp32 MFMA                */
@@ -71,7 +73,9 @@ typedef enum {
                                    cu_seqlens arrays), dtype unknown, or
                                    one (b, h) slice spanning 2 GiB or more ((N + 512) * n-stride
                                    * element size must stay below 2^31 bytes)                     */
-  STREAMKL_ERR_LAUNCH = 3       /* the HIP launch itself failed (hipGetLastError after launch)     */
+  STREAMKL_ERR_LAUNCH = 3,      /* the HIP launch itself failed (hipGetLastError after launch)     */
+  STREAMKL_ERR_SCRATCH = 4      /* streamkl_bwd_noalloc: the problem needs more scratch than the
+                                   library's static array holds (STREAMKL_NOALLOC_SCRATCH_FLOATS)   */
 } streamkl_status_t;
 
 /* Problem description.  Q tensors are [B, H, Nq, d], K tensors [B, Hk, Nk, d] with
@@ -91,9 +95,11 @@ typedef enum {
  * and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1, and is its own problem (its
  * keys only, causal alignment within it).  Both arrays are DEVICE int32 [B + 1],
  * non-decreasing, from >= 0 up to <= Nq (resp. Nk); max_seqlen_q / max_seqlen_k must
- * be >= every segment's length (they size the grid).  The kernels read the arrays as
- * given and do not check them: values outside these rules are undefined behaviour.
- * A segment with queries needs keys (and, causal, at least as many keys as
+ * be >= every segment's length (they size the grid).  The kernels clamp every offset
+ * into [0, Nq] (resp. [0, Nk]) and each segment's end to at least its start, so values
+ * outside these rules cannot make them touch memory outside the caller's buffers; the
+ * rows of such segments get unspecified outputs (the Python binding checks the rules on
+ * a read-back of both arrays and raises).  A segment with queries needs keys (and, causal, at least as many keys as
  * queries); otherwise its rows' outputs are unspecified (no other row is
  * affected).  Statistics and gradients take the layout of a one-entry batch:
  * kl, lse_t, lse_s, g float32 [H, Nq]; dq [H, Nq, d]; dk [Hk, Nk, d].              */
@@ -177,6 +183,27 @@ int streamkl_js_bwd(const streamkl_problem_t* p,
                     const float* lse_t, const float* lse_s, const float* js, const float* js_t,
                     const float* g, float* dq_s, float* dk_s, float* dq_t, float* dk_t,
                     void* hip_stream);
+
+/* Allocation-free backward, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs and rules
+ * as streamkl_bwd, and the same bits as streamkl_bwd given a workspace of streamkl_workspace_floats(p)
+ * floats, except that p->workspace must be NULL (else STREAMKL_ERR_INVALID): the only scratch the
+ * kernels use (grouped key heads' per-query-head dK before the group sum) is instead a fixed array
+ * of STREAMKL_NOALLOC_SCRATCH_FLOATS floats that the library keeps on every GPU it runs on, held until
+ * the process ends.  Its device address is resolved on the first call on each device (the current
+ * device; hip_stream must belong to it).  A problem whose streamkl_workspace_floats(p) exceeds the
+ * array is rejected with STREAMKL_ERR_SCRATCH before anything is launched.  Nothing is allocated or
+ * freed (no hipMalloc, no hipFree, no allocating library call).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (on different streams, or from different threads
+ * without ordering) race and give undefined results; calls in stream order are safe.  The array
+ * keeps the last call's contents; no call relies on them (every element a call reads it has
+ * written first).  Problems without grouped key heads use no scratch.                           */
+#define STREAMKL_NOALLOC_SCRATCH_FLOATS ((int64_t)16 << 20) /* 64 MiB per GPU */
+int streamkl_bwd_noalloc(const streamkl_problem_t* p,
+                         const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                         const float* lse_t, const float* lse_s, const float* kl, const float* g,
+                         float* dq_s, float* dk_s, float* dq_t, float* dk_t,
+                         void* hip_stream);
 
 /* Human-readable name of a status code (static storage; never NULL).            */
 const char* streamkl_status_string(int status);

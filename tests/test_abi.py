@@ -22,11 +22,11 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared) <= exported
-    assert S.version() == 10400
+    assert S.version() == 10500
 
 
 def test_status_strings():
-    for st in (S.OK, S.ERR_INVALID, S.ERR_UNSUPPORTED, S.ERR_LAUNCH, 99):
+    for st in (S.OK, S.ERR_INVALID, S.ERR_UNSUPPORTED, S.ERR_LAUNCH, S.ERR_SCRATCH, 99):
         assert S.status_string(st).startswith("STREAMKL")
 
 
