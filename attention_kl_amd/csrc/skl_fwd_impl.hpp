@@ -31,6 +31,11 @@
 
 namespace skl {
 
+// LDS operand reads in flight ahead of the logit MFMAs (bf16)
+#ifndef FWD_LA
+#define FWD_LA 4
+#endif
+
 template <typename T>
 struct FwdTile {
   static constexpr int BQ = 128;  // query rows per workgroup (4 wavefronts x 32)
@@ -254,8 +259,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
           const char* tile = slot_ptr(u);
           const int kb = t * BK;
           f32x16 st = {}, ss = {};
-          tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
-          tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
+          // both chains interleaved, each operand read issued a few MFMAs ahead of its use: with the
+          // reads one MFMA ahead each MFMA waited out an LDS latency, and the logit phase of a wave
+          // took several times its matrix cycles
+          tile_dot2_swz<T, DT, DS>(st, ss, tile, tile + BK * RBT, off_t, off_s, qt_r, qs_r);
+          if constexpr (sizeof(T) == 2) sched_read_ahead<(RBT + RBS) / 32, FWD_LA>();
           float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
           if constexpr (!JS) {
 #pragma unroll
