@@ -156,6 +156,7 @@ int streamkl_fwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, 
   a.lse_s = lse_s;
   a.ratio = p->scale_s / p->scale_t;
   a.scale_t = p->scale_t;
+  a.eq_ok = 1;
   return to_status(skl::launch_fwd(a, p->dtype, p->d_t, p->d_s, p->causal != 0, (hipStream_t)hip_stream));
 }
 

@@ -129,6 +129,44 @@ __device__ __forceinline__ void ref_renorm(RowState& s, int& emin) {
   emin = min(emin, min(et, es));
 }
 
+// Equal scales (s_t = s_s = s, so one c = s log2 e for both sides): the second MFMA chain continues
+// from the teacher logits with the student queries negated, so it yields dd = q_t.k_t - q_s.k_s, the
+// raw logit difference, and no per-element product forms it.  Both sides share one power-of-two
+// reference m: x = c st - m, y = x - c dd = c ss - m, and acc sums e dd.  Per element: two exponent
+// FMAs, two exp2, two sums and the accumulator FMA.
+__device__ __forceinline__ void ref_update_eq(RowState& s, const f32x16& st, const f32x16& dd, float c) {
+  float x = fmaf(st[0], c, -s.m_t);
+  float pt = fast_exp2(x);
+  float ps = fast_exp2(fmaf(dd[0], -c, x));
+  float pa = pt * dd[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    x = fmaf(st[i], c, -s.m_t);
+    const float e = fast_exp2(x);
+    const float f = fast_exp2(fmaf(dd[i], -c, x));
+    pt += e;
+    ps += f;
+    pa = fmaf(e, dd[i], pa);
+  }
+  s.l_t += pt;
+  s.l_s += ps;
+  s.acc += pa;
+}
+
+// The shared reference moves to the binary exponent of the larger sum (exact scalings); emin tracks
+// the smallest exponent either sum had against it, so a side that sinks far below the other is
+// caught by the end-of-loop check like a sum near the denormals.
+__device__ __forceinline__ void ref_renorm_eq(RowState& s, int& emin) {
+  const int et = __builtin_amdgcn_frexp_expf(s.l_t), es = __builtin_amdgcn_frexp_expf(s.l_s);
+  const int e = max(et, es);
+  s.l_t = __builtin_amdgcn_ldexpf(s.l_t, -e);
+  s.acc = __builtin_amdgcn_ldexpf(s.acc, -e);
+  s.l_s = __builtin_amdgcn_ldexpf(s.l_s, -e);
+  s.m_t += (float)e;
+  s.m_s = s.m_t;
+  emin = min(emin, min(et, es));
+}
+
 // Jensen-Shannon pass (second pass over the keys, with both log-sum-exps known from the KL
 // forward).  Per row, with x = log2 P_t, y = log2 P_s, r = y - x and M = (P_t + P_s)/2:
 //   log2(P_t/M) = w - max(r, 0),  log2(P_s/M) = w + min(r, 0),  w = 1 - log2(1 + 2^-|r|),
@@ -155,8 +193,9 @@ __device__ __forceinline__ void js_update(JsState& s, const f32x16& st, const f3
 }
 
 // JS: the Jensen-Shannon pass instead of the KL forward (lse_t, lse_s are read; kl receives JS and
-// js_t the teacher half KL(P_t || M)).
-template <typename T, int DT, int DS, bool CAUSAL, bool JS>
+// js_t the teacher half KL(P_t || M)).  EQ (KL forward, bf16, scale_t == scale_s): the logit
+// difference comes from the second MFMA chain (see ref_update_eq).
+template <typename T, int DT, int DS, bool CAUSAL, bool JS, bool EQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1, 3))) void fwd_kernel(
     const FwdArgs a) {
   constexpr int BQ = FwdTile<T>::BQ, BK = FwdTile<T>::BK, NBUF = FwdTile<T>::NBUF, NT = FwdTile<T>::NT;
@@ -199,6 +238,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   u32x4 qt_r[NCT / 2], qs_r[NCS / 2];
   load_row_regs<T, DT>(qt_r, qt + (int64_t)qrow * a.sqt[2], qrow < nq, hf);
   load_row_regs<T, DS>(qs_r, qs + (int64_t)qrow * a.sqs[2], qrow < nq, hf);
+  static_assert(!EQ || (!JS && sizeof(T) == 2), "the difference chain serves the bf16 KL forward");
+  if constexpr (EQ) {  // -q_s: flip the sign bit of both bf16 halves of every word (exact)
+#pragma unroll
+    for (int c = 0; c < NCS / 2; ++c) qs_r[c] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
 
   constexpr int KL_FAST = 0, KL_EXACT = 1, JS_PASS = 2;  // modes of the tile loop
   RowState rs{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
@@ -259,13 +303,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
           const char* tile = slot_ptr(u);
           const int kb = t * BK;
           f32x16 st = {}, ss = {};
-          // both chains interleaved, each operand read issued a few MFMAs ahead of its use: with the
-          // reads one MFMA ahead each MFMA waited out an LDS latency, and the logit phase of a wave
-          // took several times its matrix cycles
-          tile_dot2_swz<T, DT, DS>(st, ss, tile, tile + BK * RBT, off_t, off_s, qt_r, qs_r);
-          if constexpr (sizeof(T) == 2) sched_read_ahead<(RBT + RBS) / 32, FWD_LA>();
+          if constexpr (EQ) {
+            // ss holds dd = st - q_s.k_s: the student chain starts from the finished teacher logits
+            tile_dot_swz<T, DT>(st, tile, off_t, qt_r);
+            ss = st;
+            tile_dot_swz<T, DS>(ss, tile + BK * RBT, off_s, qs_r);
+            sched_read_ahead<(RBT + RBS) / 32, FWD_LA>();
+          } else {
+            // both chains interleaved, each operand read issued a few MFMAs ahead of its use: with the
+            // reads one MFMA ahead each MFMA waited out an LDS latency, and the logit phase of a wave
+            // took several times its matrix cycles
+            tile_dot2_swz<T, DT, DS>(st, ss, tile, tile + BK * RBT, off_t, off_s, qt_r, qs_r);
+            if constexpr (sizeof(T) == 2) sched_read_ahead<(RBT + RBS) / 32, FWD_LA>();
+          }
           float dif[16];  // (a - b) / scale_t, taken before masking so masked entries stay finite
-          if constexpr (!JS) {
+          if constexpr (!JS && !EQ) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               dif[i] = fmaf(ss[i], -a.ratio, st[i]);
@@ -288,16 +340,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
               // JS: a large finite logit instead of -inf gives P_t = P_s = 0 with a finite r, so
               // the term is an exact zero rather than 0 * NaN
               st[i] = ok ? st[i] : (JS ? -1e30f : -INFINITY);
-              ss[i] = ok ? ss[i] : (JS ? -1e30f : -INFINITY);
+              if constexpr (!EQ) ss[i] = ok ? ss[i] : (JS ? -1e30f : -INFINITY);  // EQ: dd stays finite
             }
           }
           if constexpr (MODE == JS_PASS) {
             js_update(js, st, ss, js_lt, js_ls, a.c_t, a.c_s);
             asm volatile("" ::"v"(js.at), "v"(js.as));
           } else {
-            if constexpr (MODE == KL_FAST) {
+            if constexpr (MODE == KL_FAST && EQ) {
+              ref_update_eq(rs, st, ss, a.c_t);
+              if (u == NBUF - 1) ref_renorm_eq(rs, emin);
+            } else if constexpr (MODE == KL_FAST) {
               ref_update(rs, st, ss, dif, a.c_t, a.c_s);
               if (u == NBUF - 1) ref_renorm(rs, emin);
+            } else if constexpr (EQ) {  // the exact rerun takes the student logits back from dd
+              f32x16 sl;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                sl[i] = st[i] - ss[i];
+                dif[i] = ss[i];
+              }
+              online_update(rs, st, sl, dif, a.c_t, a.c_s);
             } else {
               online_update(rs, st, ss, dif, a.c_t, a.c_s);
             }
@@ -363,7 +426,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const int64_t nblk = nqb * a.B * a.H;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C, JS>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s, a);
+  if constexpr (!JS && sizeof(T) == 2) {
+    if (a.c_t == a.c_s && a.eq_ok) {
+      hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C, false, true>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s,
+                         a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C, JS, false>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s, a);
   return hipGetLastError();
 }
 

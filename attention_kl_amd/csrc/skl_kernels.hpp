@@ -27,6 +27,10 @@ struct FwdArgs {
   float c_t, c_s;   // scale * log2(e): logits enter exp2 in these units
   float ratio;      // scale_s / scale_t
   float scale_t;
+  // KL forward with equal scales (bf16): the logit difference may come from a second MFMA chain
+  // (skl_fwd_impl.hpp, ref_update_eq).  The Jensen-Shannon forward's first pass leaves it off, so that
+  // identical rows keep bitwise-equal statistics there.
+  int32_t eq_ok;
 };
 
 struct BwdArgs {

@@ -108,16 +108,32 @@ def test_b2h16n2048_causal_small_kl_full():
     assert all_pass(worst), msg
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_teacher_equals_student_is_exactly_zero(causal):
-    w = wl.custom(1, 2, 200, 200, 128, 128, causal, recipe="same")
+def test_teacher_equals_student_gives_zero(causal, dtype):
+    """Identical teacher and student (KL = 0, every gradient 0).  fp32 inputs form both sides' logits
+    with the same instructions: bitwise-equal statistics, exact zeros.  The bf16 forward with equal
+    scales takes the logit difference from a second MFMA chain that starts from the finished teacher
+    logits, so for identical rows it is a few float32 roundings of the partial sums instead of 0: KL
+    and the gap between the two log-sum-exps stay within 1e-6 (absolute, and relative to the LSE),
+    and the gradients, which the backward forms from those statistics, within 1e-5 of their natural
+    size scale * max |g| * max row norm."""
+    w = wl.custom(1, 2, 200, 200, 128, 128, causal, dtype=dtype, recipe="same")
     print(f"case {w.name}", flush=True)
-    dev_in, _ = device_inputs(w)
+    dev_in, host = device_inputs(w)
     (kl, lt, ls), grads = _run_gpu(w, dev_in, teacher=True)
-    assert np.all(kl == 0.0)
-    np.testing.assert_array_equal(lt, ls)
-    for gr in grads:
-        assert np.all(gr == 0.0)
+    if dtype == "fp32":
+        assert np.all(kl == 0.0)
+        np.testing.assert_array_equal(lt, ls)
+        for gr in grads:
+            assert np.all(gr == 0.0)
+        return
+    assert np.abs(kl).max() <= 1e-6
+    assert np.all(np.abs(lt - ls) <= 1e-6 * np.maximum(1.0, np.abs(lt)))
+    gmax = float(np.abs(wl.full_g(w)).max())
+    for gr, other in zip(grads, (host[3], host[2], host[1], host[0])):  # dq_s, dk_s, dq_t, dk_t
+        natural = w.scale_s * gmax * float(np.linalg.norm(other, axis=-1).max())
+        assert np.linalg.norm(gr, axis=-1).max() <= 1e-5 * natural
 
 
 def test_deterministic_and_strided_layout():
