@@ -304,11 +304,17 @@ bwd_kernel(const BwdArgs a) {
   const int HX = GRP ? a.H / GX : a.H;  // heads of the owned rows
   const int nbh = a.B * HX;
   const int nob = ((OWN_Q ? a.mq : a.mk) + BW - 1) / BW;
-  const int bh = blockIdx.x % nbh;  // (batch, owned head)
+  // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8), each with its own L2:
+  // when the grid splits evenly (and keys are not grouped), XCD x takes the x-th eighth of the (head,
+  // owned block) list, so its resident workgroups share one head's streamed tiles in L2.
+  const int nblk = (int)gridDim.x;
+  const int L = (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8);
+  const bool xcd = !GRP && nblk % 8 == 0;
+  const int bh = xcd ? L / nob : blockIdx.x % nbh;  // (batch, owned head)
   // grouped keys: the group's passes may be split over NSP workgroups (adjacent in launch order)
   const int NSP = GRP ? a.nsplit : 1;
   const int sp = GRP ? (blockIdx.x / nbh) % NSP : 0;
-  const int oi = GRP ? blockIdx.x / nbh / NSP : blockIdx.x / nbh;
+  const int oi = xcd ? L % nob : (GRP ? blockIdx.x / nbh / NSP : blockIdx.x / nbh);
   // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
   const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
   const int b = bh / HX, ho = bh % HX;

@@ -214,8 +214,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: per-wave tests branch on SCC
   const int nbh = a.B * a.H;
   const int nqb = (a.mq + BQ - 1) / BQ;
-  const int bh = blockIdx.x % nbh;
-  const int qi = blockIdx.x / nbh;
+  // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8), each XCD with its own
+  // L2.  When the grid splits evenly, XCD x takes the x-th eighth of the (head, query block) list in
+  // order, so the workgroups resident on one XCD are query blocks of one head that read the same key
+  // tiles from that L2 (each head's blocks still longest first); otherwise heads are interleaved.
+  const int nblk = (int)gridDim.x;
+  const int L = (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8);
+  const bool xcd = nblk % 8 == 0;
+  const int bh = xcd ? L / nqb : blockIdx.x % nbh;
+  const int qi = xcd ? L % nqb : blockIdx.x / nbh;
   const int qb = CAUSAL ? (nqb - 1 - qi) : qi;  // causal: longest rows first
   const int b = bh / a.H, h = bh % a.H;
   const Segment sg = segment_of(a, b);

@@ -172,11 +172,13 @@ def _kernel_class(name: str):
 
 
 def _pmc_means(csv_path: str, counter: str):
-    """Mean per-dispatch value of one counter for each kernel class in a rocprofv3 counter CSV."""
+    """Mean per-dispatch value of one counter for each kernel class in a rocprofv3 counter CSV, over
+    the dispatches of that class with the largest grid (the workload's own launches, not the small
+    warm-up calls the bench makes first)."""
     import csv
     import collections
     per = collections.defaultdict(float)
-    cls = {}
+    cls, grid = {}, {}
     for r in csv.DictReader(open(csv_path)):
         if r["Counter_Name"] != counter:
             continue
@@ -185,9 +187,14 @@ def _pmc_means(csv_path: str, counter: str):
             continue
         per[r["Dispatch_Id"]] += float(r["Counter_Value"])
         cls[r["Dispatch_Id"]] = k
+        grid[r["Dispatch_Id"]] = int(r.get("Grid_Size") or 0)
+    top = collections.defaultdict(int)
+    for d, k in cls.items():
+        top[k] = max(top[k], grid[d])
     out = collections.defaultdict(list)
     for d, v in per.items():
-        out[cls[d]].append(v)
+        if grid[d] == top[cls[d]]:
+            out[cls[d]].append(v)
     return {k: sum(v) / len(v) for k, v in out.items()}
 
 
