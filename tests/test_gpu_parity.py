@@ -385,3 +385,71 @@ def test_extreme_logits_take_the_exact_path(dtype, kind):
     msg = report(f"extreme {kind} {dtype}", **r)
     print(msg, flush=True)
     assert all_pass(r), msg
+
+
+@pytest.mark.parametrize("alpha,beta", [(8.0, 8.0), (2.0, 2.0), (8.0, -0.5)])
+def test_teacher_and_student_logits_far_apart(alpha, beta):
+    """bf16 with equal scales takes the forward's difference chain, whose two sides share one
+    power-of-two reference.  Rows whose teacher logits sit near +alpha * 8 nats and student logits
+    near -beta * 8 nats (keys clustered around one direction u, teacher queries along +u, student
+    queries along -u): at (8, 8) the student's sum sinks about 180 binades below the teacher's, which
+    the kernel must notice and rerun with separate running maxima; (2, 2) and (8, -0.5) stay on the fast
+    path.  Against the float64 oracle, with the float32 rounding of logits of this size added to the
+    criteria as in test_extreme_logits_take_the_exact_path.
+
+    The keys cluster around u, so a gradient row sum_j dS_ij k_j cancels its u component about
+    tenfold and the relative criterion does not apply to it: the bf16 backward rounds dS once to fp16
+    (2^-11 relative per element), an error bound of 2^-11 scale sum_j |dS_ij| |k_j| per row whatever the
+    cancellation.  The gradients are held to 2^-10 times that sum (plus the relative term), computed
+    here in float64 from the two softmaxes of the definition."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([72, int(alpha * 10), int(beta * 10) + 50])))
+    B, H, N, d = 1, 2, 160, 64
+    u = rng.standard_normal((B, H, 1, d))
+    k = u + 0.1 * rng.standard_normal((B, H, N, d))
+    qt = alpha * u + 0.3 * rng.standard_normal((B, H, N, d))
+    qs = -beta * u + 0.3 * rng.standard_normal((B, H, N, d))
+    dev = [torch.from_numpy(a.astype(np.float32)).cuda().to(torch.bfloat16) for a in (qt, k, qs, k)]
+    host = [x.float().cpu().numpy().astype(np.float64) for x in dev]
+    print(f"case logits far apart alpha={alpha} beta={beta}", flush=True)
+    sc = 0.125
+    kl, lt, ls = S.fwd(*dev, causal=True, scale_t=sc, scale_s=sc)
+    g = torch.ones_like(kl)
+    dq, dk, _, _ = S.bwd(*dev, lt, ls, g, causal=True, scale_t=sc, scale_s=sc)
+    torch.cuda.synchronize()
+    rkl, rlt, rls = oracle.forward(*host, sc, sc, True)
+    rg = oracle.backward(*host, sc, sc, True, np.ones((B, H, N)))
+    rt = 2e-3
+    L = max(float(np.abs(host[0] @ host[1].transpose(0, 1, 3, 2)).max()),
+            float(np.abs(host[2] @ host[3].transpose(0, 1, 3, 2)).max()))  # largest raw logit
+    kl_abs = 4.0 * sc * L * math.sqrt(d) * 2.0 ** -24
+    rt_g = max(rt, sc * L * math.sqrt(d) * 2.0 ** -22)
+    c = lambda x: x.cpu().numpy()
+    for x in (kl, lt, ls, dq, dk):
+        assert np.all(np.isfinite(c(x)))
+    rms = np.maximum(np.sqrt((rkl ** 2).mean(axis=-1, keepdims=True)), 1e-3)
+    kl_ratio = float((np.abs(c(kl) - rkl) / (rt * np.abs(rkl) + rt * rms + kl_abs)).max())
+    # |dS| of the definition (g = 1): softmaxes of the causal rows in float64
+    mask = np.tril(np.ones((N, N), bool))
+    def softmax(q, kk):
+        a = np.where(mask, sc * q @ kk.transpose(0, 1, 3, 2), -np.inf)
+        a = a - a.max(-1, keepdims=True)
+        e = np.exp(a)
+        return e / e.sum(-1, keepdims=True)
+    ads = np.abs(softmax(host[2], host[3]) - softmax(host[0], host[1]))
+    kn, qn = np.linalg.norm(host[3], axis=-1), np.linalg.norm(host[2], axis=-1)
+    bound_q = 2.0 ** -10 * sc * (ads * kn[:, :, None, :]).sum(-1)   # per query row
+    bound_k = 2.0 ** -10 * sc * (ads * qn[:, :, :, None]).sum(-2)   # per key row
+
+    def ratio_bound(got, ref, bound, floor):
+        # the usual per-row criterion (relative to the row and to the head's rms row) plus the bound
+        err = np.linalg.norm(got - ref, axis=-1)
+        rn = np.linalg.norm(ref, axis=-1)
+        rms = np.maximum(np.sqrt((rn ** 2).mean(axis=-1, keepdims=True)), floor)
+        return float((err / (rt_g * rn + rt_g * rms + bound + 1e-30)).max())
+    ones = np.ones((B, H, N))
+    r = dict(kl=kl_ratio, lse_t=ratio_lse(c(lt), rlt, rt_g), lse_s=ratio_lse(c(ls), rls, rt_g),
+             dq=ratio_bound(c(dq), rg["dq_s"], bound_q, grad_floor(sc, ones, host[3])),
+             dk=ratio_bound(c(dk), rg["dk_s"], bound_k, grad_floor(sc, ones, host[2])))
+    msg = report(f"logits far apart {alpha} {beta}", **r)
+    print(msg, flush=True)
+    assert all_pass(r), msg
