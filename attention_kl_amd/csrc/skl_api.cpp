@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "skl_kernels.hpp"
@@ -123,8 +124,68 @@ int check_bwd(const streamkl_problem_t* p, const void* qt, const void* kt, const
   return check_f32(g);
 }
 
+// Per device: the compute-unit count, and a second stream with two events on which a backward call
+// runs its query-owner kernels beside its key-owner kernels (made at the first call that can use
+// them, kept until the process ends; default priority).
+struct DeviceSide {
+  int ncu = 0;
+  bool ready = false;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+DeviceSide g_side[kMaxDevices];
+
+// The current device's entry (caller holds g_side_mu), or null.  Failed HIP calls here are cleared
+// from the runtime's last-error state, so they never surface as the error of a later launch.
+DeviceSide* device_side(bool need_stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  DeviceSide& d = g_side[dev];
+  if (d.ncu == 0 && hipDeviceGetAttribute(&d.ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    d.ncu = 0;
+    (void)hipGetLastError();
+  }
+  if (need_stream && !d.ready) {
+    d.ready = hipStreamCreateWithFlags(&d.side, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&d.join, hipEventDisableTiming) == hipSuccess;
+    if (!d.ready) {  // tried again at the next call
+      (void)hipGetLastError();
+      if (d.join) (void)hipEventDestroy(d.join);
+      if (d.fork) (void)hipEventDestroy(d.fork);
+      if (d.side) (void)hipStreamDestroy(d.side);
+      d.side = nullptr, d.fork = nullptr, d.join = nullptr;
+      (void)hipGetLastError();
+    }
+  }
+  return &d;
+}
+
+// Workgroups of the query-owner (own_q) or key-owner backward kernel, counted over all query heads.
+int64_t bwd_blocks(const streamkl_problem_t* p, const skl::BwdArgs& a, bool own_q) {
+  const int bw = p->dtype == STREAMKL_BF16 ? skl::kBwdRowsBf16 : skl::kBwdRowsF32;
+  return (int64_t)(((own_q ? a.mq : a.mk) + bw - 1) / bw) * a.B * a.H;
+}
+
+// A backward grid is small when it fills the device at most twice over (one backward workgroup per
+// compute unit at a time): its causal blocks then go out longest first across heads (len_major), and
+// a call with both kernels runs them side by side (when both stream enough rows to pay the two
+// streams' handoff, about 15 us on MI355X), so that units freed by one kernel's short blocks take
+// the other's long ones.
+constexpr int kSideMinRows = 1024;
+bool small_grid(int64_t nblk) {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  const DeviceSide* d = device_side(false);
+  return d != nullptr && d->ncu > 0 && nblk <= 2 * (int64_t)d->ncu;
+}
+
 skl::BwdArgs bwd_args(const streamkl_problem_t* p, const void* qt, const void* kt, const void* qs, const void* ks,
-                      const float* lse_t, const float* lse_s, const float* kl, const float* g) {
+                      const float* lse_t, const float* lse_s, const float* kl, const float* g, bool own_q) {
   skl::BwdArgs a{};
   fill_common(a, p, qt, kt, qs, ks);
   a.lse_t = lse_t;
@@ -133,7 +194,31 @@ skl::BwdArgs bwd_args(const streamkl_problem_t* p, const void* qt, const void* k
   a.g = g;
   a.scale_t = p->scale_t;
   a.scale_s = p->scale_s;
+  a.len_major = small_grid(bwd_blocks(p, a, own_q)) ? 1 : 0;
   return a;
+}
+
+// Run on_main(s), then on_side(x), where x is the device's side stream if `fork` (both after all work
+// issued to s so far, and s then waits for x), else s itself.  Returns the first failure.
+template <class M, class S>
+int fork_join(hipStream_t s, bool fork, M&& on_main, S&& on_side) {
+  if (fork) {
+    std::lock_guard<std::mutex> lk(g_side_mu);  // one caller at a time records and waits on the events
+    DeviceSide* d = device_side(true);
+    if (d != nullptr && d->ready && hipEventRecord(d->fork, s) == hipSuccess &&
+        hipStreamWaitEvent(d->side, d->fork, 0) == hipSuccess) {
+      const int st1 = on_main(s);
+      const int st2 = on_side(d->side);
+      // s waits for the side stream whatever happened above
+      const bool joined = hipEventRecord(d->join, d->side) == hipSuccess && hipStreamWaitEvent(s, d->join, 0) == hipSuccess;
+      if (st1 != STREAMKL_OK) return st1;
+      if (st2 != STREAMKL_OK) return st2;
+      return joined ? STREAMKL_OK : STREAMKL_ERR_LAUNCH;
+    }
+    (void)hipGetLastError();
+  }
+  const int st = on_main(s);
+  return st != STREAMKL_OK ? st : on_side(s);
 }
 
 }  // namespace
@@ -166,7 +251,7 @@ int streamkl_bwd_dq(const streamkl_problem_t* p, const void* q_t, const void* k_
   int st = check_bwd(p, q_t, k_t, q_s, k_s, lse_t, lse_s, g, &empty);
   if (st != STREAMKL_OK || empty) return st;
   if ((st = check_f32(dq_s)) != STREAMKL_OK) return st;
-  skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, nullptr, g);
+  skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, nullptr, g, true);
   a.dq = dq_s;
   return to_status(skl::launch_bwd_dq(a, p->dtype, p->d_t, p->d_s, p->causal != 0, false, (hipStream_t)hip_stream));
 }
@@ -177,14 +262,19 @@ int streamkl_bwd_dk(const streamkl_problem_t* p, const void* q_t, const void* k_
   int st = check_bwd(p, q_t, k_t, q_s, k_s, lse_t, lse_s, g, &empty);
   if (st != STREAMKL_OK || empty) return st;
   if ((st = check_f32(dk_s)) != STREAMKL_OK) return st;
-  skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, nullptr, g);
+  skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, nullptr, g, false);
   a.dk = dk_s;
   return to_status(skl::launch_bwd_dk(a, p->dtype, p->d_t, p->d_s, p->causal != 0, false, (hipStream_t)hip_stream));
 }
 
-int streamkl_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s, const void* k_s,
-                 const float* lse_t, const float* lse_s, const float* kl, const float* g, float* dq_s, float* dk_s,
-                 float* dq_t, float* dk_t, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// streamkl_bwd; side: the query-owner kernels of a small problem may run on the device's side stream
+int bwd_impl(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+             const float* lse_t, const float* lse_s, const float* kl, const float* g, float* dq_s, float* dk_s,
+             float* dq_t, float* dk_t, void* hip_stream, bool side) {
   bool empty = false;
   int st = check_bwd(p, q_t, k_t, q_s, k_s, lse_t, lse_s, g, &empty);
   if (st != STREAMKL_OK) return st;
@@ -200,20 +290,47 @@ int streamkl_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, 
   }
   const hipStream_t s = (hipStream_t)hip_stream;
   const bool causal = p->causal != 0;
-  skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g);
-  if (student) {
-    a.dq = dq_s;
-    a.dk = dk_s;
-    if ((st = to_status(skl::launch_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
-    if ((st = to_status(skl::launch_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
-  }
-  if (teacher) {
-    a.dq = dq_t;
-    a.dk = dk_t;
-    if ((st = to_status(skl::launch_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, true, s))) != STREAMKL_OK) return st;
-    if ((st = to_status(skl::launch_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, true, s))) != STREAMKL_OK) return st;
-  }
-  return STREAMKL_OK;
+  skl::BwdArgs ak = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g, false);  // key owners
+  skl::BwdArgs aq = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g, true);   // query owners
+  ak.dq = aq.dq = nullptr;
+  // key-owner kernels on s, query-owner kernels beside them when both grids are small and both streams long
+  const bool fork = side && ak.len_major && aq.len_major && std::min(ak.mq, ak.mk) >= kSideMinRows;
+  return fork_join(
+      s, fork,
+      [&](hipStream_t x) {
+        int r = STREAMKL_OK;
+        if (student) {
+          ak.dk = dk_s;
+          r = to_status(skl::launch_bwd_dk(ak, p->dtype, p->d_t, p->d_s, causal, false, x));
+        }
+        if (r == STREAMKL_OK && teacher) {
+          ak.dk = dk_t;
+          r = to_status(skl::launch_bwd_dk(ak, p->dtype, p->d_t, p->d_s, causal, true, x));
+        }
+        return r;
+      },
+      [&](hipStream_t x) {
+        int r = STREAMKL_OK;
+        if (student) {
+          aq.dq = dq_s;
+          r = to_status(skl::launch_bwd_dq(aq, p->dtype, p->d_t, p->d_s, causal, false, x));
+        }
+        if (r == STREAMKL_OK && teacher) {
+          aq.dq = dq_t;
+          r = to_status(skl::launch_bwd_dq(aq, p->dtype, p->d_t, p->d_s, causal, true, x));
+        }
+        return r;
+      });
+}
+
+}  // namespace
+
+extern "C" {
+
+int streamkl_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s, const void* k_s,
+                 const float* lse_t, const float* lse_s, const float* kl, const float* g, float* dq_s, float* dk_s,
+                 float* dq_t, float* dk_t, void* hip_stream) {
+  return bwd_impl(p, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g, dq_s, dk_s, dq_t, dk_t, hip_stream, true);
 }
 
 int streamkl_js_fwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s, const void* k_s,
@@ -253,21 +370,37 @@ int streamkl_js_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_
   if (teacher && ((st = check_f32(dq_t)) != STREAMKL_OK || (st = check_f32(dk_t)) != STREAMKL_OK)) return st;
   const hipStream_t s = (hipStream_t)hip_stream;
   const bool causal = p->causal != 0;
-  skl::BwdArgs a = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, js_t, g);
-  a.js = js;
-  if (student) {
-    a.dq = dq_s;
-    a.dk = dk_s;
-    if ((st = to_status(skl::launch_js_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
-    if ((st = to_status(skl::launch_js_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, false, s))) != STREAMKL_OK) return st;
-  }
-  if (teacher) {
-    a.dq = dq_t;
-    a.dk = dk_t;
-    if ((st = to_status(skl::launch_js_bwd_dk(a, p->dtype, p->d_t, p->d_s, causal, true, s))) != STREAMKL_OK) return st;
-    if ((st = to_status(skl::launch_js_bwd_dq(a, p->dtype, p->d_t, p->d_s, causal, true, s))) != STREAMKL_OK) return st;
-  }
-  return STREAMKL_OK;
+  skl::BwdArgs ak = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, js_t, g, false);  // key owners
+  skl::BwdArgs aq = bwd_args(p, q_t, k_t, q_s, k_s, lse_t, lse_s, js_t, g, true);   // query owners
+  ak.js = aq.js = js;
+  ak.dq = aq.dq = nullptr;
+  const bool fork = ak.len_major && aq.len_major && std::min(ak.mq, ak.mk) >= kSideMinRows;
+  return fork_join(
+      s, fork,
+      [&](hipStream_t x) {
+        int r = STREAMKL_OK;
+        if (student) {
+          ak.dk = dk_s;
+          r = to_status(skl::launch_js_bwd_dk(ak, p->dtype, p->d_t, p->d_s, causal, false, x));
+        }
+        if (r == STREAMKL_OK && teacher) {
+          ak.dk = dk_t;
+          r = to_status(skl::launch_js_bwd_dk(ak, p->dtype, p->d_t, p->d_s, causal, true, x));
+        }
+        return r;
+      },
+      [&](hipStream_t x) {
+        int r = STREAMKL_OK;
+        if (student) {
+          aq.dq = dq_s;
+          r = to_status(skl::launch_js_bwd_dq(aq, p->dtype, p->d_t, p->d_s, causal, false, x));
+        }
+        if (r == STREAMKL_OK && teacher) {
+          aq.dq = dq_t;
+          r = to_status(skl::launch_js_bwd_dq(aq, p->dtype, p->d_t, p->d_s, causal, true, x));
+        }
+        return r;
+      });
 }
 
 int streamkl_bwd_noalloc(const streamkl_problem_t* p, const void* q_t, const void* k_t, const void* q_s,
@@ -289,7 +422,8 @@ int streamkl_bwd_noalloc(const streamkl_problem_t* p, const void* q_t, const voi
     q.workspace = ptr;  // the device copy's address, never the host-side symbol
     q.workspace_floats = need;
   }
-  return streamkl_bwd(&q, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g, dq_s, dk_s, dq_t, dk_t, hip_stream);
+  // no side stream: creating one may allocate, and the kernels' results do not depend on it
+  return bwd_impl(&q, q_t, k_t, q_s, k_s, lse_t, lse_s, kl, g, dq_s, dk_s, dq_t, dk_t, hip_stream, false);
 }
 
 const char* streamkl_status_string(int status) {

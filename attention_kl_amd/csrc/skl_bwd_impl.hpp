@@ -61,6 +61,7 @@ struct BwdTile {
   // next PD = NBUF - 2 tiles are in flight
   static constexpr int NBUF = 4;
   static constexpr int PD = NBUF - 2;
+  static_assert(BW == (sizeof(T) == 2 ? kBwdRowsBf16 : kBwdRowsF32), "rows per workgroup known to the launcher");
 };
 
 // dS of one 32 x 32 tile in the accumulator layout, kept from a vector phase to the next matrix
@@ -306,9 +307,14 @@ bwd_kernel(const BwdArgs a) {
   const int nob = ((OWN_Q ? a.mq : a.mk) + BW - 1) / BW;
   // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8), each with its own L2:
   // when the grid splits evenly (and keys are not grouped), XCD x takes the x-th eighth of the (head,
-  // owned block) list, so its resident workgroups share one head's streamed tiles in L2.
+  // owned block) list, so its resident workgroups share one head's streamed tiles in L2.  In that
+  // eighth the blocks go out head by head, longest stream first within a head; for a small grid
+  // (len_major) whose eighth holds whole heads, longest first across those heads, so that the XCD's
+  // longest streams all start first (for causal problems the block lengths differ up to N / 32 tiles).
   const int nblk = (int)gridDim.x;
-  const int L = (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8);
+  const int S8 = nblk / 8, j8 = (int)(blockIdx.x / 8);
+  const int hs = (a.len_major && S8 % nob == 0) ? S8 / nob : 1;  // whole heads in an XCD's eighth
+  const int L = (int)(blockIdx.x % 8) * S8 + (hs > 1 ? (j8 % hs) * nob + j8 / hs : j8);
   const bool xcd = !GRP && nblk % 8 == 0;
   const int bh = xcd ? L / nob : blockIdx.x % nbh;  // (batch, owned head)
   // grouped keys: the group's passes may be split over NSP workgroups (adjacent in launch order)
@@ -391,10 +397,8 @@ bwd_kernel(const BwdArgs a) {
       rst[4] = JS ? rsrc_words(js_bh, (uint32_t)n_str * 4u) : rst[2];
     }
   };
-  DmaT dma_t;
+  DmaT dma_t;  // per-lane offsets set at the start of each run (below)
   DmaS dma_s;
-  dma_t.init(str_pt, wave, lane);
-  dma_s.init(str_ps, wave, lane);
   auto slot_ptr = [&](int u) -> char* { return ring[u]; };
   auto issue = [&](int s, int u) {  // tile s of the workgroup's stream into ring slot u
     const int t = t_begin + s;
@@ -433,10 +437,19 @@ bwd_kernel(const BwdArgs a) {
   };
 
   int off_t[NCT / 2], off_s[NCS / 2];  // logit-product operand offsets (row r32 of a tile)
-  swz_operand_offsets<RBT, NCT / 2>(off_t, r32, hf);
-  swz_operand_offsets<RBS, NCS / 2>(off_s, r32, hf);
-  int toff[2][DX / 32];  // transpose-read offsets of the gradient product
-  tr_offsets<RBX, DX>(toff, lane);
+  int toff[2][DX / 32];                 // transpose-read offsets of the gradient product
+  // The per-lane offsets above and the DMA's are formed at the start of each run from an opaque copy
+  // of the lane index: formed once, the compiler kept some of them through the fast run for the
+  // hi + lo rerun and spilled them to scratch.
+  auto set_offsets = [&]() {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    dma_t.init(str_pt, wave, ln);
+    dma_s.init(str_ps, wave, ln);
+    swz_operand_offsets<RBT, NCT / 2>(off_t, ln & 31, ln >> 5);
+    swz_operand_offsets<RBS, NCS / 2>(off_s, ln & 31, ln >> 5);
+    tr_offsets<RBX, DX>(toff, ln);
+  };
 
   f32x16 dacc[DX / 32];
 #pragma unroll
@@ -663,6 +676,7 @@ bwd_kernel(const BwdArgs a) {
   // Every pass over the stream, into dacc; F16: with the fast gradient product.
   auto run = [&](auto f16c) {
     constexpr bool F16 = decltype(f16c)::value;
+    set_offsets();
     if constexpr (F16 && !OWN_Q) {
       // the largest |g| (times the row's bound on |dS|) of the queries this workgroup streams, over
       // all its passes, read up front

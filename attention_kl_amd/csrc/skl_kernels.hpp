@@ -58,9 +58,14 @@ struct BwdArgs {
   int64_t ws_floats;
   int64_t ws_part;
   int32_t nsplit;
+  // Small grids (set by the launcher): inside each XCD's share of whole heads, workgroups go out in order
+  // of stream length across those heads instead of head by head (see bwd_kernel).
+  int32_t len_major;
   float c_t, c_s;            // scale * log2(e)
   float scale_t, scale_s;
 };
+// Owned rows per backward workgroup: 8 waves of 32 (bf16) or 4 (fp32).
+constexpr int kBwdRowsBf16 = 256, kBwdRowsF32 = 128;
 
 // Rows of batch entry b.  Dense: all Nq query and Nk key rows, at batch index b of the strides.
 // Packed: the segment's rows, which start at row q0 / k0 of the packed axis (batch index 0).  The

@@ -348,6 +348,25 @@ def time_step(w, dev, steps: int, warmup: int):
     ms = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, k in
           enumerate(("fwd", "bwd_dk", "bwd_dq"))}
     step_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+
+    # the backward as one streamkl_bwd call, as the autograd wrapper makes it: for small problems its
+    # two kernels run side by side on two streams, so only the call as a whole is timed
+    def step_call(ev=None):
+        ev and ev[0].record()
+        S.fwd(qt, kt, qs, ks, out=(kl, lt, ls), **kw)
+        ev and ev[1].record()
+        S.bwd(qt, kt, qs, ks, lt, ls, g, out=[dq, dk], **kw)
+        ev and ev[2].record()
+
+    for _ in range(warmup + 1):
+        step_call()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step_call(e)
+    torch.cuda.synchronize()
+    ms["bwd_call"] = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms["step_call"] = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
     del qt, kt, qs, ks, g, kl, lt, ls, dq, dk
     torch.cuda.empty_cache()
     return ms, step_ms, int(lib_alloc)
@@ -365,6 +384,8 @@ def config_entry(w, ms, step_ms, lib_alloc, peak=None, workspace_floats=0):
          "step_tflops": round((fwd_fl + bwd_fl) / step_ms / 1e9, 2),
          "fwd_frac": round(fwd_fl / ms["fwd"] / 1e9 / mp, 4), "bwd_frac": round(bwd_fl / bwd_ms / 1e9 / mp, 4),
          "peak_tflops": mp, "dtype": w.dtype,
+         **({"bwd_call_ms": round(ms["bwd_call"], 4), "step_call_ms": round(ms["step_call"], 4),
+             "step_call_tflops": round((fwd_fl + bwd_fl) / ms["step_call"] / 1e9, 2)} if "bwd_call" in ms else {}),
          "extra_hbm_bytes": 12 * w.B * w.H * w.Nq + 4 * int(workspace_floats), "library_alloc_bytes": lib_alloc}
     if peak and w.dtype == "bf16":
         e["fwd_frac_of_measured_peak"] = round(fwd_fl / ms["fwd"] / 1e9 / peak["tflops"], 4)

@@ -24,11 +24,14 @@
  *
  * Conventions shared by every entry point.
  *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *    allocates nothing, frees nothing and keeps no state: the only HBM it touches
- *    beyond the inputs is the outputs the caller passes (S8: no O(Nq*Nk) buffer),
- *    plus, for grouped key heads only, an optional caller workspace (see
+ *    allocates no memory and frees nothing: the only HBM it touches beyond the
+ *    inputs is the outputs the caller passes (S8: no O(Nq*Nk) buffer), plus, for
+ *    grouped key heads only, an optional caller workspace (see
  *    streamkl_workspace_floats) or, for streamkl_bwd_noalloc, a fixed scratch array
- *    the library holds on each GPU.
+ *    the library holds on each GPU.  Its only other state, per device: a second HIP
+ *    stream (default priority) and two events, made by the first streamkl_bwd or
+ *    streamkl_js_bwd call that runs kernels side by side and kept until the process
+ *    ends.
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and
  *    is asynchronous: the call returns after launch.  Kernel faults surface at the
  *    caller's next synchronisation, as for any HIP launch.
@@ -36,9 +39,10 @@
  *    into), so they need no zeroing.  Outputs must not alias inputs.
  *  - Return value: STREAMKL_OK or an error code; nothing is launched when an
  *    argument check fails.  Nothing is printed and nothing is thrown.
- *  - Thread-safe: calls share no mutable state (streamkl_bwd_noalloc excepted: its
- *    calls on one GPU share that GPU's scratch).  Results are bitwise deterministic
- *    (no atomics; fixed reduction order).
+ *  - Thread-safe (the side stream and its events are used under a lock;
+ *    streamkl_bwd_noalloc's calls on one GPU share that GPU's scratch).  Results are
+ *    bitwise deterministic (no atomics; fixed reduction order) and do not depend on
+ *    which stream a kernel ran on.
  */
 #ifndef STREAMKL_H
 #define STREAMKL_H
@@ -49,7 +53,7 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10500 /* 1.5.0: allocation-free backward; 1.4.0: workspace for grouped keys;
+#define STREAMKL_VERSION 10600 /* 1.6.0: small backward problems on two streams; 1.5.0: allocation-free backward; 1.4.0: workspace for grouped keys;
                                   1.3.0: Jensen-Shannon; 1.2.0: packed batches; 1.1.0: key heads */
 
 typedef enum {
@@ -142,8 +146,17 @@ int streamkl_fwd(const streamkl_problem_t* p,
  * per-row weights g.  Outputs come in pairs, each pair both NULL (not computed)
  * or both non-NULL (written): dq_s, dk_s the student gradients, dq_t, dk_t the
  * teacher gradients.  One pointer of a pair NULL, or both pairs NULL, =
- * STREAMKL_ERR_INVALID.  Launches, for each pair asked for, the key-owner then
- * the query-owner kernel on hip_stream (student pair first).                     */
+ * STREAMKL_ERR_INVALID.  Launches the key-owner kernel of each pair asked for
+ * (student first) on hip_stream, then the query-owner kernels.  When both grids
+ * are small (each at most twice the device's compute units in workgroups, where
+ * causal blocks of unequal length leave units idle) and both stream at least 1024
+ * rows (the longest query and key segments) the query-owner kernels go to
+ * the device's side stream instead and run beside the key-owner ones: the side
+ * stream first waits for everything issued to hip_stream before the call, and
+ * hip_stream then waits for the side stream's kernels (event record and wait, so
+ * a HIP graph capture of hip_stream takes both).  Calls that overlap in time share
+ * the side stream in the order they reach it; a capture of hip_stream should not
+ * overlap another thread's uncaptured calls on the same device.                  */
 int streamkl_bwd(const streamkl_problem_t* p,
                  const void* q_t, const void* k_t, const void* q_s, const void* k_s,
                  const float* lse_t, const float* lse_s, const float* kl, const float* g,
@@ -177,7 +190,8 @@ int streamkl_js_fwd(const streamkl_problem_t* p,
 /* Gradients of sum_i g_i JS_i.  Needs streamkl_js_fwd's lse_t, lse_s, js and js_t;
  * the gradient pairs follow the rules of streamkl_bwd:
  *   dS_t = g_i P_t (log(P_t/M) - KL(P_t || M)_i) / 2,   dS_s = g_i P_s (log(P_s/M) - KL(P_s || M)_i) / 2,
- * then dQ, dK as for the KL backward.                                            */
+ * then dQ, dK as for the KL backward, with the kernels on the streams streamkl_bwd
+ * uses.                                                                           */
 int streamkl_js_bwd(const streamkl_problem_t* p,
                     const void* q_t, const void* k_t, const void* q_s, const void* k_s,
                     const float* lse_t, const float* lse_s, const float* js, const float* js_t,
@@ -187,7 +201,8 @@ int streamkl_js_bwd(const streamkl_problem_t* p,
 /* Allocation-free backward, for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs and rules
  * as streamkl_bwd, and the same bits as streamkl_bwd given a workspace of streamkl_workspace_floats(p)
- * floats, except that p->workspace must be NULL (else STREAMKL_ERR_INVALID): the only scratch the
+ * floats (all kernels on hip_stream: this entry point creates no side stream), except that
+ * p->workspace must be NULL (else STREAMKL_ERR_INVALID): the only scratch the
  * kernels use (grouped key heads' per-query-head dK before the group sum) is instead a fixed array
  * of STREAMKL_NOALLOC_SCRATCH_FLOATS floats that the library keeps on every GPU it runs on, held until
  * the process ends.  Its device address is resolved on the first call on each device (the current
