@@ -752,8 +752,8 @@ bwd_kernel(const BwdArgs a) {
         // a matrix phase reads tile s (landed and published by the previous barrier) and the fp16
         // copy of tile s-1 (both halves written in period s-1), and writes its half of the copy of
         // tile s into the other buffer; the statistics are the wave's own.  Ring: both groups issue
-        // their shares of tile s+PD at the start of period s (group 0 before its matrix phase, group
-        // 1 before its vector phase of tile s-1), into the slot of tile s-2, last read in period s-1;
+        // their shares of tile s+PD in period s (group 0 after its matrix phase, group 1 before its
+        // vector phase of tile s-1), into the slot of tile s-2, last read in period s-1;
         // each wave waits for its share of tile s+1 before the barrier that ends period s.  The last
         // slot, read by the s = 0 gradient product of the hi + lo path, first receives a tile in
         // period 1.
@@ -764,7 +764,6 @@ bwd_kernel(const BwdArgs a) {
             const int s = s0 + u;
             if (s <= ntile) {
               // matrix phase of tile s: first half of period s (group 0) or second half (group 1)
-              if (grp == 0) issue(s + PD, (u + PD) % NBUF);
               if constexpr (F16) {
                 matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1], u);  // converts the statistics too
               } else {
@@ -775,6 +774,9 @@ bwd_kernel(const BwdArgs a) {
                 wait_tile();
                 __syncthreads();
               }
+              // group 0's share of tile s+PD, after its matrix phase: issued at the start of the period
+              // together with group 1's share, the DMA instructions of all eight waves queued at once
+              if (grp == 0) issue(s + PD, (u + PD) % NBUF);
               // vector phase of tile s: second half of period s (group 0) or first half of s+1 (group 1)
               if (s < ntile) {
                 if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
