@@ -88,3 +88,43 @@ def test_graph_capture_takes_both_streams():
         graph.replay()
         torch.cuda.synchronize()
         assert _same_bits(outs, ref), f"replay {r}"
+
+
+def test_calls_from_two_threads_on_two_streams():
+    """Two host threads, each on its own stream, calling the backward at once: they share the device's
+    second stream and its events under the library's lock, and each gets the bits of a lone call."""
+    import threading
+    print("case two threads", flush=True)
+    probs = [_problem(20 + k) for k in range(2)]
+    refs, fwds = [], []
+    for w, x, g in probs:
+        kl, lt, ls = S.fwd(*x, causal=True)
+        fwds.append((kl, lt, ls))
+        refs.append(S.bwd(*x, lt, ls, g, kl=kl, causal=True, teacher_grads=True))
+    torch.cuda.synchronize()
+    results = [[None] * 6 for _ in probs]
+    errors = []
+
+    def worker(k):
+        try:
+            w, x, g = probs[k]
+            kl, lt, ls = fwds[k]
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                for r in range(6):
+                    results[k][r] = S.bwd(*x, lt, ls, g, kl=kl, causal=True, teacher_grads=True, out=_empty_grads(w))
+            st.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(2):
+        for r in range(6):
+            assert _same_bits(results[k][r], refs[k]), f"thread {k} call {r}"
