@@ -154,8 +154,9 @@ __device__ __forceinline__ void ref_update_eq(RowState& s, const f32x16& st, con
 }
 
 // The shared reference moves to the binary exponent of the larger sum (exact scalings); emin tracks
-// the smallest exponent either sum had against it, so a side that sinks far below the other is
-// caught by the end-of-loop check like a sum near the denormals.
+// the smallest exponent either sum had against the old reference (a sum near the denormals).  A side
+// that sinks far below the other is caught at the end of the loop, where the smaller sum must stay
+// within 2^-100 of the larger one (ref_gap_bad).
 __device__ __forceinline__ void ref_renorm_eq(RowState& s, int& emin) {
   const int et = __builtin_amdgcn_frexp_expf(s.l_t), es = __builtin_amdgcn_frexp_expf(s.l_s);
   const int e = max(et, es);
@@ -165,6 +166,14 @@ __device__ __forceinline__ void ref_renorm_eq(RowState& s, int& emin) {
   s.m_t += (float)e;
   s.m_s = s.m_t;
   emin = min(emin, min(et, es));
+}
+
+// End of the loop with a shared reference (the loop ends on a renormalisation, so the larger sum is in
+// [0.5, 1)): a smaller sum below 2^-100 of it, or at zero, has lost its precision in this lane half,
+// even where the merged row (the other half) looks normal.  Without this test a row of three tiles or
+// fewer, whose only renormalisation leaves the student's sum a denormal, came out as -inf.
+__device__ __forceinline__ bool ref_gap_bad(const RowState& s) {
+  return fmaxf(s.l_t, s.l_s) > 0.f && fminf(s.l_t, s.l_s) < 0x1p-100f;
 }
 
 // Jensen-Shannon pass (second pass over the keys, with both log-sum-exps known from the KL
@@ -406,11 +415,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   };
   rs = RowState{0.f, 0.f, 0.f, 0.f, 0.f};  // power-of-two references start at 2^0
   tile_loop(std::integral_constant<int, KL_FAST>{});
+  const bool half_bad = EQ && ref_gap_bad(rs);  // this lane half's own sums, before the merge
   merge();
   // A row whose sums left the safe range (an overflow, or a sum that came near the denormals) is
   // redone by the whole workgroup with running maxima; realistic logits never get there.
-  const bool risky = !(__builtin_isfinite(Lt) && __builtin_isfinite(Ls) && __builtin_isfinite(A)) || emin < -100 ||
-                     (qrow < nq && (Lt == 0.f || Ls == 0.f));
+  const bool risky = half_bad || !(__builtin_isfinite(Lt) && __builtin_isfinite(Ls) && __builtin_isfinite(A)) ||
+                     emin < -100 || (qrow < nq && (Lt == 0.f || Ls == 0.f));
   if (__syncthreads_or(risky)) {
     rs = RowState{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
     tile_loop(std::integral_constant<int, KL_EXACT>{});

@@ -77,6 +77,23 @@ def test_small_and_ragged(w):
     _check_full(w)
 
 
+# Mid-size problems in full (512 to 1300 keys, a few workgroups): ragged tile counts, unequal head dims
+# (no difference chain), more keys than queries under the causal mask, the small-KL regime, logits
+# with a few large peaks.
+MID = [
+    wl.custom(1, 2, 600, 600, 128, 128, True, recipe="independent"),
+    wl.custom(1, 1, 1030, 1030, 128, 64, False, recipe="independent"),
+    wl.custom(2, 2, 520, 1300, 128, 128, True, recipe="independent"),
+    wl.custom(1, 2, 700, 700, 128, 128, True, sigma=0.1),
+    wl.custom(1, 1, 800, 800, 128, 128, True, recipe="independent", peak_frac=0.02, peak_scale=4.0),
+]
+
+
+@pytest.mark.parametrize("w", MID, ids=lambda w: w.name)
+def test_mid_size(w):
+    _check_full(w)
+
+
 @pytest.mark.parametrize("w", [wl.custom(1, 2, 129, 129, 128, 128, True, recipe="independent"),
                                wl.custom(1, 1, 70, 70, 128, 64, False, recipe="independent"),
                                wl.custom(1, 1, 33, 33, 64, 64, True, dtype="fp32")], ids=lambda w: w.name)
@@ -108,9 +125,10 @@ def test_b2h16n2048_causal_small_kl_full():
     assert all_pass(worst), msg
 
 
+@pytest.mark.parametrize("n", [200, 700])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_teacher_equals_student_gives_zero(causal, dtype):
+def test_teacher_equals_student_gives_zero(causal, dtype, n):
     """Identical teacher and student (KL = 0, every gradient 0).  fp32 inputs form both sides' logits
     with the same instructions: bitwise-equal statistics, exact zeros.  The bf16 forward with equal
     scales takes the logit difference from a second MFMA chain that starts from the finished teacher
@@ -118,7 +136,7 @@ def test_teacher_equals_student_gives_zero(causal, dtype):
     and the gap between the two log-sum-exps stay within 1e-6 (absolute, and relative to the LSE),
     and the gradients, which the backward forms from those statistics, within 1e-5 of their natural
     size scale * max |g| * max row norm."""
-    w = wl.custom(1, 2, 200, 200, 128, 128, causal, dtype=dtype, recipe="same")
+    w = wl.custom(1, 2, n, n, 128, 128, causal, dtype=dtype, recipe="same")
     print(f"case {w.name}", flush=True)
     dev_in, host = device_inputs(w)
     (kl, lt, ls), grads = _run_gpu(w, dev_in, teacher=True)
@@ -387,23 +405,27 @@ def test_extreme_logits_take_the_exact_path(dtype, kind):
     assert all_pass(r), msg
 
 
-@pytest.mark.parametrize("alpha,beta", [(8.0, 8.0), (2.0, 2.0), (8.0, -0.5)])
-def test_teacher_and_student_logits_far_apart(alpha, beta):
+@pytest.mark.parametrize("alpha,beta,N", [(8.0, 8.0, 160), (2.0, 2.0, 160), (8.0, -0.5, 160), (8.0, 8.0, 640),
+                                          (7.0, 7.0, 90)])
+def test_teacher_and_student_logits_far_apart(alpha, beta, N):
     """bf16 with equal scales takes the forward's difference chain, whose two sides share one
     power-of-two reference.  Rows whose teacher logits sit near +alpha * 8 nats and student logits
     near -beta * 8 nats (keys clustered around one direction u, teacher queries along +u, student
     queries along -u): at (8, 8) the student's sum sinks about 180 binades below the teacher's, which
     the kernel must notice and rerun with separate running maxima; (2, 2) and (8, -0.5) stay on the fast
-    path.  Against the float64 oracle, with the float32 rounding of logits of this size added to the
-    criteria as in test_extreme_logits_take_the_exact_path.
+    path; (8, 8) at 640 rows takes the rerun over rows of up to 20 tiles.  (7, 7) at 90 rows puts one head's gap between the two log-sum-exps at 137-141
+    binades: after the only renormalisation of a three-tile row the student's sum against the shared
+    reference is a denormal, not zero, which must also send the row to the rerun (it gave -inf
+    before each lane half's smaller sum was checked against the shared reference).  Against the float64 oracle, with the float32 rounding of logits of this size
+    added to the criteria as in test_extreme_logits_take_the_exact_path.
 
     The keys cluster around u, so a gradient row sum_j dS_ij k_j cancels its u component about
     tenfold and the relative criterion does not apply to it: the bf16 backward rounds dS once to fp16
     (2^-11 relative per element), an error bound of 2^-11 scale sum_j |dS_ij| |k_j| per row whatever the
     cancellation.  The gradients are held to 2^-10 times that sum (plus the relative term), computed
     here in float64 from the two softmaxes of the definition."""
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([72, int(alpha * 10), int(beta * 10) + 50])))
-    B, H, N, d = 1, 2, 160, 64
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([72, int(alpha * 10), int(beta * 10) + 50] + ([N] if N != 160 else []))))
+    B, H, d = 1, 2, 64
     u = rng.standard_normal((B, H, 1, d))
     k = u + 0.1 * rng.standard_normal((B, H, N, d))
     qt = alpha * u + 0.3 * rng.standard_normal((B, H, N, d))
@@ -450,6 +472,6 @@ def test_teacher_and_student_logits_far_apart(alpha, beta):
     r = dict(kl=kl_ratio, lse_t=ratio_lse(c(lt), rlt, rt_g), lse_s=ratio_lse(c(ls), rls, rt_g),
              dq=ratio_bound(c(dq), rg["dq_s"], bound_q, grad_floor(sc, ones, host[3])),
              dk=ratio_bound(c(dk), rg["dk_s"], bound_k, grad_floor(sc, ones, host[2])))
-    msg = report(f"logits far apart {alpha} {beta}", **r)
+    msg = report(f"logits far apart {alpha} {beta} N={N}", **r)
     print(msg, flush=True)
     assert all_pass(r), msg
