@@ -184,6 +184,12 @@ bool small_grid(int64_t nblk) {
   return d != nullptr && d->ncu > 0 && nblk <= 2 * (int64_t)d->ncu;
 }
 
+// Small forward grids (at most twice the device's compute units in workgroups of 128 query rows, so two
+// workgroups to a CU): the two that share a CU pair a long causal query block with a short one.
+int fwd_fold(const skl::FwdArgs& a) {
+  return small_grid((int64_t)((a.mq + 127) / 128) * a.B * a.H) ? 1 : 0;
+}
+
 skl::BwdArgs bwd_args(const streamkl_problem_t* p, const void* qt, const void* kt, const void* qs, const void* ks,
                       const float* lse_t, const float* lse_s, const float* kl, const float* g, bool own_q) {
   skl::BwdArgs a{};
@@ -242,6 +248,7 @@ int streamkl_fwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, 
   a.ratio = p->scale_s / p->scale_t;
   a.scale_t = p->scale_t;
   a.eq_ok = 1;
+  a.fold = fwd_fold(a);
   return to_status(skl::launch_fwd(a, p->dtype, p->d_t, p->d_s, p->causal != 0, (hipStream_t)hip_stream));
 }
 
@@ -351,6 +358,7 @@ int streamkl_js_fwd(const streamkl_problem_t* p, const void* q_t, const void* k_
   a.ratio = p->scale_s / p->scale_t;
   a.scale_t = p->scale_t;
   const hipStream_t s = (hipStream_t)hip_stream;
+  a.fold = fwd_fold(a);
   if ((st = to_status(skl::launch_fwd(a, p->dtype, p->d_t, p->d_s, p->causal != 0, s))) != STREAMKL_OK) return st;
   return to_status(skl::launch_js_fwd(a, p->dtype, p->d_t, p->d_s, p->causal != 0, s));
 }

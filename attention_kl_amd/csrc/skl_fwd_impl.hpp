@@ -227,8 +227,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   // L2.  When the grid splits evenly, XCD x takes the x-th eighth of the (head, query block) list in
   // order, so the workgroups resident on one XCD are query blocks of one head that read the same key
   // tiles from that L2 (each head's blocks still longest first); otherwise heads are interleaved.
+  // Within an XCD the workgroups go to its CUs round-robin (position j to CU j mod the XCD's CUs), so
+  // in a small grid with two workgroups per CU whose eighth holds whole heads, positions j and j + S/2
+  // share a CU: with `fold`, the first half goes out longest first across the heads and the second
+  // half shortest first, so each CU's two query blocks hold about the same number of key tiles
+  // (head by head, causal, the CU of position 0 held the two longest).
   const int nblk = (int)gridDim.x;
-  const int L = (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8);
+  const int S8 = nblk / 8, j8 = (int)(blockIdx.x / 8);
+  int pos = j8;  // position in the XCD's eighth, head-major
+  if (a.fold && S8 % nqb == 0 && S8 % 2 == 0) {
+    const int hs = S8 / nqb;                                     // whole heads in the eighth
+    const int pp = j8 < S8 / 2 ? j8 : (S8 + S8 / 2 - 1 - j8);  // rank by length
+    pos = (pp % hs) * nqb + pp / hs;
+  }
+  const int L = (int)(blockIdx.x % 8) * S8 + pos;
   const bool xcd = nblk % 8 == 0;
   const int bh = xcd ? L / nqb : blockIdx.x % nbh;
   const int qi = xcd ? L % nqb : blockIdx.x / nbh;

@@ -31,6 +31,9 @@ struct FwdArgs {
   // (skl_fwd_impl.hpp, ref_update_eq).  The Jensen-Shannon forward's first pass leaves it off, so that
   // identical rows keep bitwise-equal statistics there.
   int32_t eq_ok;
+  // Small grids (set by the launcher): the two workgroups that share a CU pair a long query block with
+  // a short one (see fwd_kernel); otherwise an XCD's share goes out head by head.
+  int32_t fold;
 };
 
 struct BwdArgs {
