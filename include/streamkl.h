@@ -156,7 +156,9 @@ int streamkl_fwd(const streamkl_problem_t* p,
  * hip_stream then waits for the side stream's kernels (event record and wait, so
  * a HIP graph capture of hip_stream takes both).  Calls that overlap in time share
  * the side stream in the order they reach it; a capture of hip_stream should not
- * overlap another thread's uncaptured calls on the same device.                  */
+ * overlap another thread's uncaptured calls on the same device.  Should recording
+ * or waiting on the join event fail, the call returns STREAMKL_ERR_LAUNCH and the
+ * caller must synchronise the device before using the outputs.                   */
 int streamkl_bwd(const streamkl_problem_t* p,
                  const void* q_t, const void* k_t, const void* q_s, const void* k_s,
                  const float* lse_t, const float* lse_s, const float* kl, const float* g,
