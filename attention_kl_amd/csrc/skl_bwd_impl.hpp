@@ -400,19 +400,28 @@ bwd_kernel(const BwdArgs a) {
   DmaT dma_t;  // per-lane offsets set at the start of each run (below)
   DmaS dma_s;
   auto slot_ptr = [&](int u) -> char* { return ring[u]; };
-  auto issue = [&](int s, int u) {  // tile s of the workgroup's stream into ring slot u
+  // This wave's share of tile s of the workgroup's stream into ring slot u, in two parts: part 0 the
+  // teacher rows (and, key owner, the statistics), part 1 the student rows.
+  auto issue_part = [&](int s, int u, auto part) {
     const int t = t_begin + s;
     char* sl = slot_ptr(u);
     const bool whole = (t + 1) * BS <= n_str;
-    dma_t.issue(rs_t, t * BS * (int)str_pt, whole, sl, wave);
-    dma_s.issue(rs_s, t * BS * (int)str_ps, whole, sl + BS * RBT, wave);
-    if constexpr (!OWN_Q) {
-      if (wave == 0) {
-        const int vo = (t * BS + lane) * 4;  // lanes 32..63 fetch the next tile's rows: unused
+    if constexpr (decltype(part)::value == 0) {
+      dma_t.issue(rs_t, t * BS * (int)str_pt, whole, sl, wave);
+      if constexpr (!OWN_Q) {
+        if (wave == 0) {
+          const int vo = (t * BS + lane) * 4;  // lanes 32..63 fetch the next tile's rows: unused
 #pragma unroll
-        for (int k = 0; k < NIS; ++k) dma_dword(rst[k], vo, sl + TILE + k * 256);
+          for (int k = 0; k < NIS; ++k) dma_dword(rst[k], vo, sl + TILE + k * 256);
+        }
       }
+    } else {
+      dma_s.issue(rs_s, t * BS * (int)str_ps, whole, sl + BS * RBT, wave);
     }
+  };
+  auto issue = [&](int s, int u) {
+    issue_part(s, u, std::integral_constant<int, 0>{});
+    issue_part(s, u, std::integral_constant<int, 1>{});
   };
   // this wave's DMA of the older of its two newest tiles has landed (the newest may be in flight)
   auto wait_tile = [&]() {
@@ -621,12 +630,15 @@ bwd_kernel(const BwdArgs a) {
   // tile s (ring slot sc), and this group's half of tile s converted to fp16 at hd.  The order is
   // fixed by scheduling barriers: LDS reads go out LA logit steps (of two MFMAs) ahead of their
   // MFMAs; the conversion's read goes out with the first logit reads and its VALU steps ride behind
-  // logit MFMAs from step CD on, when the value has arrived.
-  auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd, int u) {
+  // logit MFMAs from step CD on, when the value has arrived.  dma(part) queues the two parts of this
+  // wave's share of a later tile behind the logit MFMAs of steps DM0 and DM1: a DMA instruction can
+  // wait at issue while the memory pipeline takes other waves' DMA, and there the matrix core keeps
+  // working through the MFMAs already issued.
+  auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd, int u, auto&& dma) {
     if constexpr (FAST) {
       // key owner: this wave converts the statistics of tile s here (see stats_read)
       constexpr int NDB = DX / 32, NT2 = RBT / 32, NS2 = RBS / 32, NM = NT2 > NS2 ? NT2 : NS2;
-      constexpr int LA = 2, CD = 2;
+      constexpr int LA = 2, CD = 2, DM0 = 1, DM1 = NM > 4 ? 4 : NM - 1;
       using Conv = HalfToF16<HROW / 2>;
       const char* tt = sc;
       const char* ts = sc + BS * RBT;
@@ -662,6 +674,8 @@ bwd_kernel(const BwdArgs a) {
         if (c >= CD && c - CD < Conv::NWD) cv.step(c - CD);
         if (c - CD == Conv::NWD) risky |= cv.finish(hd);
         if (MCONV && c == NM - 2) stats_store(rv);
+        if (c == DM0) dma(std::integral_constant<int, 0>{});
+        if (c == DM1) dma(std::integral_constant<int, 1>{});
         fence();
       }
       if constexpr (NM - CD <= Conv::NWD) {  // short logit runs: whatever steps remain
@@ -752,12 +766,12 @@ bwd_kernel(const BwdArgs a) {
         // a matrix phase reads tile s (landed and published by the previous barrier) and the fp16
         // copy of tile s-1 (both halves written in period s-1), and writes its half of the copy of
         // tile s into the other buffer; the statistics are the wave's own.  Ring: both groups issue
-        // their shares of tile s+PD in period s (group 0 after its matrix phase, group 1 before its
-        // vector phase of tile s-1), into the slot of tile s-2, last read in period s-1;
-        // each wave waits for its share of tile s+1 before the barrier that ends period s.  The last
-        // slot, read by the s = 0 gradient product of the hi + lo path, first receives a tile in
-        // period 1.
-        if (grp == 1) issue(PD, PD);  // group 1's share of tile PD (period 0 has no vector phase for it)
+        // their shares of tile s+PD in period s, into the slot of tile s-2, last read in period s-1
+        // (fast path: within the matrix phase of tile s; hi + lo path: group 0 after its matrix
+        // phase, group 1 before its vector phase of tile s-1); each wave waits for its share of
+        // tile s+1 before the barrier that ends period s.  The last slot, read by the s = 0
+        // gradient product of the hi + lo path, first receives a tile in period 1.
+        if (!F16 && grp == 1) issue(PD, PD);  // group 1's share of tile PD (period 0 has no vector phase for it)
         for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
 #pragma unroll
           for (int u = 0; u < NBUF; ++u) {
@@ -765,7 +779,8 @@ bwd_kernel(const BwdArgs a) {
             if (s <= ntile) {
               // matrix phase of tile s: first half of period s (group 0) or second half (group 1)
               if constexpr (F16) {
-                matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1], u);  // converts the statistics too
+                matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1], u,  // converts the statistics too
+                               [&](auto part) { issue_part(s + PD, (u + PD) % NBUF, part); });
               } else {
                 matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
                 if constexpr (MCONV) stats_store(stats_read(slot_ptr(u)));  // tile s landed before this phase
@@ -774,12 +789,13 @@ bwd_kernel(const BwdArgs a) {
                 wait_tile();
                 __syncthreads();
               }
-              // group 0's share of tile s+PD, after its matrix phase: issued at the start of the period
-              // together with group 1's share, the DMA instructions of all eight waves queued at once
-              if (grp == 0) issue(s + PD, (u + PD) % NBUF);
+              // hi + lo path: group 0's share of tile s+PD after its matrix phase (issued at the start of
+              // the period together with group 1's share, the DMA instructions of all eight waves
+              // queued at once)
+              if (!F16 && grp == 0) issue(s + PD, (u + PD) % NBUF);
               // vector phase of tile s: second half of period s (group 0) or first half of s+1 (group 1)
               if (s < ntile) {
-                if (grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
+                if (!F16 && grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
                 vector_phase(s, u, slot_ptr(u), f16c);
               }
               if (grp == 0) {  // the end of period s for group 0 (ntile + 1 barriers for each group)
