@@ -302,6 +302,7 @@ int bwd_impl(const streamkl_problem_t* p, const void* q_t, const void* k_t, cons
   ak.dq = aq.dq = nullptr;
   // key-owner kernels on s, query-owner kernels beside them when both grids are small and both streams long
   const bool fork = side && ak.len_major && aq.len_major && std::min(ak.mq, ak.mk) >= kSideMinRows;
+  ak.pair = aq.pair = fork ? 1 : 0;  // causal blocks in long + short pairs: half of each grid, side by side
   return fork_join(
       s, fork,
       [&](hipStream_t x) {
@@ -383,6 +384,7 @@ int streamkl_js_bwd(const streamkl_problem_t* p, const void* q_t, const void* k_
   ak.js = aq.js = js;
   ak.dq = aq.dq = nullptr;
   const bool fork = ak.len_major && aq.len_major && std::min(ak.mq, ak.mk) >= kSideMinRows;
+  ak.pair = aq.pair = fork ? 1 : 0;
   return fork_join(
       s, fork,
       [&](hipStream_t x) {

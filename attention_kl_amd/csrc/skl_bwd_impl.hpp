@@ -291,10 +291,10 @@ bwd_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char h16[FAST ? 2 : 1][FAST ? HROW : 16];
   __shared__ float gred[(FAST && !OWN_Q) ? NW : 1];  // per-wave maxima of |g| (key owner)
 
-  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
+  const int tid0 = threadIdx.x;
   // wave index in a scalar register: every branch on it (and on the group) is a scalar branch, so a
   // barrier inside one is executed only by the waves that take it
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int grp = NG == 2 ? (wave >> 2) : 0;
   // Heads: query head h reads teacher key head h / gt and student key head h / gs.  A query-owner
   // workgroup serves one query head.  A key-owner workgroup owns key rows of one key head of the
@@ -305,6 +305,10 @@ bwd_kernel(const BwdArgs a) {
   const int HX = GRP ? a.H / GX : a.H;  // heads of the owned rows
   const int nbh = a.B * HX;
   const int nob = ((OWN_Q ? a.mq : a.mk) + BW - 1) / BW;
+  // Paired (causal, dense, both kernels of a small problem side by side): workgroup slot oi of a head
+  // runs block oi and then block nob-1-oi, a long causal stream and a short one, so that every slot
+  // of the head streams about as many tiles; the middle block of an odd count runs alone.
+  const int nsl = a.pair ? (nob + 1) / 2 : nob;  // workgroup slots per head
   // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8), each with its own L2:
   // when the grid splits evenly (and keys are not grouped), XCD x takes the x-th eighth of the (head,
   // owned block) list, so its resident workgroups share one head's streamed tiles in L2.  In that
@@ -313,571 +317,587 @@ bwd_kernel(const BwdArgs a) {
   // longest streams all start first (for causal problems the block lengths differ up to N / 32 tiles).
   const int nblk = (int)gridDim.x;
   const int S8 = nblk / 8, j8 = (int)(blockIdx.x / 8);
-  const int hs = (a.len_major && S8 % nob == 0) ? S8 / nob : 1;  // whole heads in an XCD's eighth
-  const int L = (int)(blockIdx.x % 8) * S8 + (hs > 1 ? (j8 % hs) * nob + j8 / hs : j8);
+  const int hs = (a.len_major && S8 % nsl == 0) ? S8 / nsl : 1;  // whole heads in an XCD's eighth
+  const int L = (int)(blockIdx.x % 8) * S8 + (hs > 1 ? (j8 % hs) * nsl + j8 / hs : j8);
   const bool xcd = !GRP && nblk % 8 == 0;
-  const int bh = xcd ? L / nob : blockIdx.x % nbh;  // (batch, owned head)
+  const int bh = xcd ? L / nsl : blockIdx.x % nbh;  // (batch, owned head)
   // grouped keys: the group's passes may be split over NSP workgroups (adjacent in launch order)
   const int NSP = GRP ? a.nsplit : 1;
   const int sp = GRP ? (blockIdx.x / nbh) % NSP : 0;
-  const int oi = xcd ? L % nob : (GRP ? blockIdx.x / nbh / NSP : blockIdx.x / nbh);
-  // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
-  const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
-  const int b = bh / HX, ho = bh % HX;
-  const Segment sg = segment_of(a, b);
-  const int n_own = OWN_Q ? sg.nq : sg.nk, n_str = OWN_Q ? sg.nk : sg.nq;
-  if (ob * BW >= n_own) return;  // past the end of a shorter segment of a packed batch (whole workgroup)
-  const int off = sg.nk - sg.nq;
+  const int oi0 = xcd ? L % nsl : (GRP ? blockIdx.x / nbh / NSP : blockIdx.x / nbh);
+  const int njob = (CAUSAL && !GRP && a.pair && nob - 1 - oi0 != oi0) ? 2 : 1;
+  for (int jb = 0; jb < njob; ++jb) {
+    // no wave reads the LDS of the last block any more (its loop ended on a barrier): the ring may refill
+    if (jb > 0) __syncthreads();
+    const int oi = jb == 0 ? oi0 : nob - 1 - oi0;
+    // Per block, the lane index comes from an opaque copy, so that nothing derived from it is
+    // invariant over the loop: hoisted out of it, such values held registers through the tile loops
+    // and spilled there.
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, hf = lane >> 5, r32 = lane & 31;
+    // causal: the longest streams first (late query blocks for dQ, early key blocks for dK)
+    const int ob = (CAUSAL && OWN_Q) ? (nob - 1 - oi) : oi;
+    const int b = bh / HX, ho = bh % HX;
+    const Segment sg = segment_of(a, b);
+    const int n_own = OWN_Q ? sg.nq : sg.nk, n_str = OWN_Q ? sg.nk : sg.nq;
+    if (ob * BW >= n_own) return;  // past the end of a shorter segment of a packed batch (whole workgroup)
+    const int off = sg.nk - sg.nq;
 
-  const int64_t own_pt = OWN_Q ? a.sqt[2] : a.skt[2], own_ps = OWN_Q ? a.sqs[2] : a.sks[2];
-  const int64_t str_pt = (OWN_Q ? a.skt[2] : a.sqt[2]) * (int64_t)sizeof(T);
-  const int64_t str_ps = (OWN_Q ? a.sks[2] : a.sqs[2]) * (int64_t)sizeof(T);
+    const int64_t own_pt = OWN_Q ? a.sqt[2] : a.skt[2], own_ps = OWN_Q ? a.sqs[2] : a.sks[2];
+    const int64_t str_pt = (OWN_Q ? a.skt[2] : a.sqt[2]) * (int64_t)sizeof(T);
+    const int64_t str_ps = (OWN_Q ? a.sks[2] : a.sqs[2]) * (int64_t)sizeof(T);
 
-  const int o0 = ob * BW;
-  const int o0w = o0 + wave * 32;
-  const int orow = o0w + r32;
-  const bool ovalid = orow < n_own;
-  u32x4 ot_r[NCT / 2], os_r[NCS / 2];
+    const int o0 = ob * BW;
+    const int o0w = o0 + wave * 32;
+    const int orow = o0w + r32;
+    const bool ovalid = orow < n_own;
+    u32x4 ot_r[NCT / 2], os_r[NCS / 2];
 
-  // Per query head hq (one pass): the streamed operands, this wave's owned rows of both sides (the
-  // other side's key head can change from pass to pass), and the row statistics of head hq.
-  const T *str_t, *str_s;
-  const float *lse_t_bh, *lse_s_bh, *g_bh, *kl_bh, *js_bh;
-  auto set_head = [&](const BwdArgs& A, int hq) {
-    const T* qt = reinterpret_cast<const T*>(A.qt) + sg.bs * A.sqt[0] + hq * A.sqt[1] + sg.q0 * A.sqt[2];
-    const T* kt = reinterpret_cast<const T*>(A.kt) + sg.bs * A.skt[0] + (hq / A.gt) * A.skt[1] + sg.k0 * A.skt[2];
-    const T* qs = reinterpret_cast<const T*>(A.qs) + sg.bs * A.sqs[0] + hq * A.sqs[1] + sg.q0 * A.sqs[2];
-    const T* ks = reinterpret_cast<const T*>(A.ks) + sg.bs * A.sks[0] + (hq / A.gs) * A.sks[1] + sg.k0 * A.sks[2];
-    str_t = OWN_Q ? kt : qt;
-    str_s = OWN_Q ? ks : qs;
-    // the row offsets are formed from an opaque copy of orow in every pass: computed once before the
-    // pass loop instead, they would hold registers through the tile loop that its LDS reads need
-    int row = orow;
-    asm volatile("" : "+v"(row));
-    const bool valid = row < n_own;
-    load_row_regs<T, DT>(ot_r, (OWN_Q ? qt : kt) + (int64_t)row * own_pt, valid, hf);
-    load_row_regs<T, DS>(os_r, (OWN_Q ? qs : ks) + (int64_t)row * own_ps, valid, hf);
-    const int64_t r0 = ((int64_t)sg.bs * A.H + hq) * A.Nq + sg.q0;
-    lse_t_bh = A.lse_t + r0;
-    lse_s_bh = A.lse_s + r0;
-    g_bh = A.g + r0;
-    kl_bh = (TEACHER || JS) ? A.kl + r0 : nullptr;  // KL, or (JS) the teacher half js_t
-    js_bh = JS ? A.js + r0 : nullptr;
-  };
+    // Per query head hq (one pass): the streamed operands, this wave's owned rows of both sides (the
+    // other side's key head can change from pass to pass), and the row statistics of head hq.
+    const T *str_t, *str_s;
+    const float *lse_t_bh, *lse_s_bh, *g_bh, *kl_bh, *js_bh;
+    auto set_head = [&](const BwdArgs& A, int hq) {
+      const T* qt = reinterpret_cast<const T*>(A.qt) + sg.bs * A.sqt[0] + hq * A.sqt[1] + sg.q0 * A.sqt[2];
+      const T* kt = reinterpret_cast<const T*>(A.kt) + sg.bs * A.skt[0] + (hq / A.gt) * A.skt[1] + sg.k0 * A.skt[2];
+      const T* qs = reinterpret_cast<const T*>(A.qs) + sg.bs * A.sqs[0] + hq * A.sqs[1] + sg.q0 * A.sqs[2];
+      const T* ks = reinterpret_cast<const T*>(A.ks) + sg.bs * A.sks[0] + (hq / A.gs) * A.sks[1] + sg.k0 * A.sks[2];
+      str_t = OWN_Q ? kt : qt;
+      str_s = OWN_Q ? ks : qs;
+      // the row offsets are formed from an opaque copy of orow in every pass: computed once before the
+      // pass loop instead, they would hold registers through the tile loop that its LDS reads need
+      int row = orow;
+      asm volatile("" : "+v"(row));
+      const bool valid = row < n_own;
+      load_row_regs<T, DT>(ot_r, (OWN_Q ? qt : kt) + (int64_t)row * own_pt, valid, hf);
+      load_row_regs<T, DS>(os_r, (OWN_Q ? qs : ks) + (int64_t)row * own_ps, valid, hf);
+      const int64_t r0 = ((int64_t)sg.bs * A.H + hq) * A.Nq + sg.q0;
+      lse_t_bh = A.lse_t + r0;
+      lse_s_bh = A.lse_s + r0;
+      g_bh = A.g + r0;
+      kl_bh = (TEACHER || JS) ? A.kl + r0 : nullptr;  // KL, or (JS) the teacher half js_t
+      js_bh = JS ? A.js + r0 : nullptr;
+    };
 
-  // query-owner: this lane's row statistics (log2 units), constant over the key stream
-  float own_lt = 0.f, own_ls = 0.f, own_c = 0.f;
+    // query-owner: this lane's row statistics (log2 units), constant over the key stream
+    float own_lt = 0.f, own_ls = 0.f, own_c = 0.f;
 
-  // streamed range of the workgroup: tiles t_begin .. t_begin + ntile - 1 (ntile >= 1)
-  int t_begin, t_end;
-  if constexpr (OWN_Q) {
-    const int q_last = min(n_own, o0 + BW) - 1;
-    const int kend = CAUSAL ? min(n_str, q_last + off + 1) : n_str;
-    t_begin = 0;
-    t_end = (kend + BS - 1) / BS;
-  } else {
-    const int qmin = CAUSAL ? max(0, o0 - off) : 0;  // first query that may see this block's first key
-    t_begin = qmin / BS;
-    t_end = (n_str + BS - 1) / BS;
-  }
-  // never negative: the two groups' barrier counts (ntile + 2 each) stay equal even for rows
-  // with no allowed key (an invalid segment of a packed batch)
-  const int ntile = max(t_end - t_begin, 0);
-
-  // ---- streamed tiles: buffer->LDS DMA into the ring, two tiles ahead
-  u32x4 rs_t, rs_s, rst[5];
-  auto set_rsrc = [&]() {  // buffer descriptors of the current head's streamed rows and statistics
-    rs_t = rsrc_words(str_t, n_str > 0 ? (uint32_t)((n_str - 1) * str_pt + RBT) : 0u);
-    rs_s = rsrc_words(str_s, n_str > 0 ? (uint32_t)((n_str - 1) * str_ps + RBS) : 0u);
-    if constexpr (!OWN_Q) {
-      rst[0] = rsrc_words(lse_t_bh, (uint32_t)n_str * 4u);
-      rst[1] = rsrc_words(lse_s_bh, (uint32_t)n_str * 4u);
-      rst[2] = rsrc_words(g_bh, (uint32_t)n_str * 4u);
-      rst[3] = (TEACHER || JS) ? rsrc_words(kl_bh, (uint32_t)n_str * 4u) : rst[2];
-      rst[4] = JS ? rsrc_words(js_bh, (uint32_t)n_str * 4u) : rst[2];
-    }
-  };
-  DmaT dma_t;  // per-lane offsets set at the start of each run (below)
-  DmaS dma_s;
-  auto slot_ptr = [&](int u) -> char* { return ring[u]; };
-  // This wave's share of tile s of the workgroup's stream into ring slot u, in two parts: part 0 the
-  // teacher rows (and, key owner, the statistics), part 1 the student rows.
-  auto issue_part = [&](int s, int u, auto part) {
-    const int t = t_begin + s;
-    char* sl = slot_ptr(u);
-    const bool whole = (t + 1) * BS <= n_str;
-    if constexpr (decltype(part)::value == 0) {
-      dma_t.issue(rs_t, t * BS * (int)str_pt, whole, sl, wave);
-      if constexpr (!OWN_Q) {
-        if (wave == 0) {
-          const int vo = (t * BS + lane) * 4;  // lanes 32..63 fetch the next tile's rows: unused
-#pragma unroll
-          for (int k = 0; k < NIS; ++k) dma_dword(rst[k], vo, sl + TILE + k * 256);
-        }
-      }
-    } else {
-      dma_s.issue(rs_s, t * BS * (int)str_ps, whole, sl + BS * RBT, wave);
-    }
-  };
-  auto issue = [&](int s, int u) {
-    issue_part(s, u, std::integral_constant<int, 0>{});
-    issue_part(s, u, std::integral_constant<int, 1>{});
-  };
-  // this wave's DMA of the older of its two newest tiles has landed (the newest may be in flight)
-  auto wait_tile = [&]() {
-    if constexpr (NIS > 0) {
-      if (wave == 0)
-        wait_vmcnt<(PD - 1) * (NI + NIS)>();
-      else
-        wait_vmcnt<(PD - 1) * NI>();
-    } else {
-      wait_vmcnt<(PD - 1) * NI>();
-    }
-  };
-  auto tile_state = [&](int s, bool& skip, bool& full) {
-    const int sb = (t_begin + s) * BS;  // first streamed row of the tile
+    // streamed range of the workgroup: tiles t_begin .. t_begin + ntile - 1 (ntile >= 1)
+    int t_begin, t_end;
     if constexpr (OWN_Q) {
-      skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
-      full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
+      const int q_last = min(n_own, o0 + BW) - 1;
+      const int kend = CAUSAL ? min(n_str, q_last + off + 1) : n_str;
+      t_begin = 0;
+      t_end = (kend + BS - 1) / BS;
     } else {
-      skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
-      full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
+      const int qmin = CAUSAL ? max(0, o0 - off) : 0;  // first query that may see this block's first key
+      t_begin = qmin / BS;
+      t_end = (n_str + BS - 1) / BS;
     }
-  };
+    // never negative: the two groups' barrier counts (ntile + 2 each) stay equal even for rows
+    // with no allowed key (an invalid segment of a packed batch)
+    const int ntile = max(t_end - t_begin, 0);
 
-  int off_t[NCT / 2], off_s[NCS / 2];  // logit-product operand offsets (row r32 of a tile)
-  int toff[2][DX / 32];                 // transpose-read offsets of the gradient product
-  // The per-lane offsets above and the DMA's are formed at the start of each run from an opaque copy
-  // of the lane index: formed once, the compiler kept some of them through the fast run for the
-  // hi + lo rerun and spilled them to scratch.
-  auto set_offsets = [&]() {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    dma_t.init(str_pt, wave, ln);
-    dma_s.init(str_ps, wave, ln);
-    swz_operand_offsets<RBT, NCT / 2>(off_t, ln & 31, ln >> 5);
-    swz_operand_offsets<RBS, NCS / 2>(off_s, ln & 31, ln >> 5);
-    tr_offsets<RBX, DX>(toff, ln);
-  };
-
-  f32x16 dacc[DX / 32];
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
-  f32x16 st = {}, ss = {};
-  DsTile<T> dsr;  // dS of the last tile through the vector phase, for the gradient product
-
-  // Key owner: statistics of the streamed query rows, converted per tile to the units the vector
-  // phase uses.  The row weight g enters the exponents: g P = sgn(g) exp2(x - (LSE log2 e - log2|g|)),
-  // so dS needs no per-element product with g; only a tile holding a negative weight multiplies by
-  // the sign afterwards (g = 0 gives an exponent near -1e30 and a zero term, see log2_weight).
-  //   0: LSE_t log2 e - log2|g|   1: LSE_s log2 e - log2|g|   2: sgn(g)
-  //   3: KL: KL + LSE_t - LSE_s (teacher).  JS: the gradient side's half KL(P || M) in log2 units,
-  //      js_t for the teacher and 2 js - js_t for the student
-  constexpr int NSTAT = (TEACHER || JS) ? 4 : 3;
-  // Fast path: dS is formed times 2^esh (an exponent offset, so no extra product): for the query
-  // owner esh = 14 - e with 2^e above its rows' bound on |dS| before the row weight (e = 1, or per row
-  // for KL teacher gradients), for the key owner 14 - e with 2^e above |g| times that bound for every
-  // query the workgroup streams.  0 on the hi + lo path.
-  float esh = 0.f;
-  bool fast_run = false;
-  auto convert_one = [&](int k, const float* raw) -> float {
-    const float g = raw[128 + r32];
-    if (k == 0) return raw[r32] * kLog2e - log2_weight(g) - esh;
-    if (k == 1) return raw[64 + r32] * kLog2e - log2_weight(g) - esh;
-    if (k == 2) return g;  // its sign is taken when stored
-    if constexpr (JS) return (TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32])) * kLog2e;
-    return raw[192 + r32] + raw[r32] - raw[64 + r32];
-  };
-  // Ping-pong: each wave converts the statistics of tile s in its own matrix phase of that tile (the
-  // tile landed before it, and the wave's VALU is mostly idle while its MFMAs run).  The two lane
-  // halves hold the same 32 rows and split the statistics: half hf converts k = hf (the exponent
-  // offsets) and k = 2 + hf (the sign of g; the KL or JS term when there are four).  The raw values
-  // are read early (stats_read), converted and stored late (stats_store); tile_neg tells the vector
-  // phase whether some row weight of the tile is negative.
-  bool tile_neg = false;
-  auto stats_read = [&](const char* sl) -> f32x4 {
-    const float* raw = reinterpret_cast<const float*>(sl + TILE);
-    float c3 = 0.f;
-    if constexpr (JS) c3 = TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32]);
-    else if constexpr (TEACHER) c3 = raw[192 + r32] + raw[r32] - raw[64 + r32];
-    return f32x4{raw[64 * hf + r32], raw[128 + r32], c3, 0.f};  // LSE of side hf, g, term 3
-  };
-  auto stats_store = [&](const f32x4& rv) {
-    const float g = rv[1];
-    wst[wave][hf][r32] = rv[0] * kLog2e - log2_weight(g) - esh;
-    if (hf == 0)
-      wst[wave][2][r32] = g < 0.f ? -1.f : 1.f;
-    else if (NSTAT == 4)
-      wst[wave][3][r32] = JS ? rv[2] * kLog2e : rv[2];
-    tile_neg = __builtin_amdgcn_ballot_w64(g < 0.f) != 0;
-  };
-
-  // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
-  auto vector_phase = [&](int s, int u, const char* sl, auto f16c) {
-    constexpr bool F16 = decltype(f16c)::value;
-    bool skip, full;
-    tile_state(s, skip, full);
-    if (NG == 1 && skip) return;  // ping-pong: a skipped tile goes through the masked path (all zero)
-    bool neg = false;  // some row weight of the tile is negative
-    if constexpr (!OWN_Q && !MCONV) {  // statistics of the 32 streamed queries, converted by each wave
-      const float* raw = reinterpret_cast<const float*>(sl + TILE);
-#pragma unroll
-      for (int k = 0; k < NSTAT; ++k) {
-        const float v = convert_one(k, raw);
-        wst[wave][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
+    // ---- streamed tiles: buffer->LDS DMA into the ring, two tiles ahead
+    u32x4 rs_t, rs_s, rst[5];
+    auto set_rsrc = [&]() {  // buffer descriptors of the current head's streamed rows and statistics
+      rs_t = rsrc_words(str_t, n_str > 0 ? (uint32_t)((n_str - 1) * str_pt + RBT) : 0u);
+      rs_s = rsrc_words(str_s, n_str > 0 ? (uint32_t)((n_str - 1) * str_ps + RBS) : 0u);
+      if constexpr (!OWN_Q) {
+        rst[0] = rsrc_words(lse_t_bh, (uint32_t)n_str * 4u);
+        rst[1] = rsrc_words(lse_s_bh, (uint32_t)n_str * 4u);
+        rst[2] = rsrc_words(g_bh, (uint32_t)n_str * 4u);
+        rst[3] = (TEACHER || JS) ? rsrc_words(kl_bh, (uint32_t)n_str * 4u) : rst[2];
+        rst[4] = JS ? rsrc_words(js_bh, (uint32_t)n_str * 4u) : rst[2];
       }
-      neg = __builtin_amdgcn_ballot_w64(raw[128 + r32] < 0.f) != 0;
-    }
-    if constexpr (MCONV) neg = tile_neg;
-    const int sb = (t_begin + s) * BS;
-    float ds[16];
+    };
+    DmaT dma_t;  // per-lane offsets set at the start of each run (below)
+    DmaS dma_s;
+    auto slot_ptr = [&](int u) -> char* { return ring[u]; };
+    // This wave's share of tile s of the workgroup's stream into ring slot u, in two parts: part 0 the
+    // teacher rows (and, key owner, the statistics), part 1 the student rows.
+    auto issue_part = [&](int s, int u, auto part) {
+      const int t = t_begin + s;
+      const uint32_t sl = lds_addr(ring) + (uint32_t)(u * SLOT);
+      const bool whole = (t + 1) * BS <= n_str;
+      if constexpr (decltype(part)::value == 0) {
+        dma_t.issue(rs_t, t * BS * (int)str_pt, whole, sl, wave);
+        if constexpr (!OWN_Q) {
+          if (wave == 0) {
+            const int vo = (t * BS + lane) * 4;  // lanes 32..63 fetch the next tile's rows: unused
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      // The row weight is not applied here: the query owner scales each output row by it at the
-      // store, the key owner has it folded into the statistics (sign below).
-      f32x4 lt4, ls4, cc4;
-      if constexpr (OWN_Q) {
-        lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
-        ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
-        cc4 = f32x4{own_c, own_c, own_c, own_c};
+            for (int k = 0; k < NIS; ++k) dma_dword(rst[k], vo, sl + TILE + k * 256);
+          }
+        }
       } else {
-        const int ql = 8 * g4 + 4 * hf;
-        const float(*cs)[32] = wst[wave];
-        lt4 = *reinterpret_cast<const f32x4*>(&cs[0][ql]);
-        ls4 = *reinterpret_cast<const f32x4*>(&cs[1][ql]);
-        cc4 = (TEACHER || JS) ? *reinterpret_cast<const f32x4*>(&cs[3][ql]) : f32x4{};
+        dma_s.issue(rs_s, t * BS * (int)str_ps, whole, sl + BS * RBT, wave);
       }
+    };
+    auto issue = [&](int s, int u) {
+      issue_part(s, u, std::integral_constant<int, 0>{});
+      issue_part(s, u, std::integral_constant<int, 1>{});
+    };
+    // this wave's DMA of the older of its two newest tiles has landed (the newest may be in flight)
+    auto wait_tile = [&]() {
+      if constexpr (NIS > 0) {
+        if (wave == 0)
+          wait_vmcnt<(PD - 1) * (NI + NIS)>();
+        else
+          wait_vmcnt<(PD - 1) * NI>();
+      } else {
+        wait_vmcnt<(PD - 1) * NI>();
+      }
+    };
+    auto tile_state = [&](int s, bool& skip, bool& full) {
+      const int sb = (t_begin + s) * BS;  // first streamed row of the tile
+      if constexpr (OWN_Q) {
+        skip = sb >= n_str || (CAUSAL && sb > o0w + 31 + off);
+        full = sb + 31 < n_str && (!CAUSAL || sb + 31 <= o0w + off);
+      } else {
+        skip = sb >= n_str || (CAUSAL && o0w > sb + 31 + off);
+        full = sb + 31 < n_str && (!CAUSAL || o0w + 31 <= sb + off);
+      }
+    };
+
+    int off_t[NCT / 2], off_s[NCS / 2];  // logit-product operand offsets (row r32 of a tile)
+    int toff[2][DX / 32];                 // transpose-read offsets of the gradient product
+    // The per-lane offsets above and the DMA's are formed at the start of each run from an opaque copy
+    // of the lane index: formed once, the compiler kept some of them through the fast run for the
+    // hi + lo rerun and spilled them to scratch.
+    auto set_offsets = [&]() {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      dma_t.init(str_pt, wave, ln);
+      dma_s.init(str_ps, wave, ln);
+      swz_operand_offsets<RBT, NCT / 2>(off_t, ln & 31, ln >> 5);
+      swz_operand_offsets<RBS, NCS / 2>(off_s, ln & 31, ln >> 5);
+      tr_offsets<RBX, DX>(toff, ln);
+    };
+
+    f32x16 dacc[DX / 32];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * g4 + e;
-        float v;
-        if constexpr (JS) {
-          // P (log2(P/M) - KL(P || M) log2 e) of the gradient's side, with r = log2(P_s/P_t) and
-          // log2(P_t/M) = w - max(r, 0), log2(P_s/M) = w + min(r, 0), w = 1 - log2(1 + 2^-|r|)
-          const float x = fmaf(st[i], a.c_t, -lt4[e]), y = fmaf(ss[i], a.c_s, -ls4[e]);
-          const float r = y - x;
-          const float w = 1.f - fast_log2(1.f + fast_exp2(-fabsf(r)));
-          v = TEACHER ? fast_exp2(x) * (w - fmaxf(r, 0.f) - cc4[e]) : fast_exp2(y) * (w + fminf(r, 0.f) - cc4[e]);
-          ds[i] = v;
-          continue;
+    for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
+    f32x16 st = {}, ss = {};
+    DsTile<T> dsr;  // dS of the last tile through the vector phase, for the gradient product
+
+    // Key owner: statistics of the streamed query rows, converted per tile to the units the vector
+    // phase uses.  The row weight g enters the exponents: g P = sgn(g) exp2(x - (LSE log2 e - log2|g|)),
+    // so dS needs no per-element product with g; only a tile holding a negative weight multiplies by
+    // the sign afterwards (g = 0 gives an exponent near -1e30 and a zero term, see log2_weight).
+    //   0: LSE_t log2 e - log2|g|   1: LSE_s log2 e - log2|g|   2: sgn(g)
+    //   3: KL: KL + LSE_t - LSE_s (teacher).  JS: the gradient side's half KL(P || M) in log2 units,
+    //      js_t for the teacher and 2 js - js_t for the student
+    constexpr int NSTAT = (TEACHER || JS) ? 4 : 3;
+    // Fast path: dS is formed times 2^esh (an exponent offset, so no extra product): for the query
+    // owner esh = 14 - e with 2^e above its rows' bound on |dS| before the row weight (e = 1, or per row
+    // for KL teacher gradients), for the key owner 14 - e with 2^e above |g| times that bound for every
+    // query the workgroup streams.  0 on the hi + lo path.
+    float esh = 0.f;
+    bool fast_run = false;
+    auto convert_one = [&](int k, const float* raw) -> float {
+      const float g = raw[128 + r32];
+      if (k == 0) return raw[r32] * kLog2e - log2_weight(g) - esh;
+      if (k == 1) return raw[64 + r32] * kLog2e - log2_weight(g) - esh;
+      if (k == 2) return g;  // its sign is taken when stored
+      if constexpr (JS) return (TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32])) * kLog2e;
+      return raw[192 + r32] + raw[r32] - raw[64 + r32];
+    };
+    // Ping-pong: each wave converts the statistics of tile s in its own matrix phase of that tile (the
+    // tile landed before it, and the wave's VALU is mostly idle while its MFMAs run).  The two lane
+    // halves hold the same 32 rows and split the statistics: half hf converts k = hf (the exponent
+    // offsets) and k = 2 + hf (the sign of g; the KL or JS term when there are four).  The raw values
+    // are read early (stats_read), converted and stored late (stats_store); tile_neg tells the vector
+    // phase whether some row weight of the tile is negative.
+    bool tile_neg = false;
+    auto stats_read = [&](const char* sl) -> f32x4 {
+      const float* raw = reinterpret_cast<const float*>(sl + TILE);
+      float c3 = 0.f;
+      if constexpr (JS) c3 = TEACHER ? raw[192 + r32] : fmaf(2.f, raw[256 + r32], -raw[192 + r32]);
+      else if constexpr (TEACHER) c3 = raw[192 + r32] + raw[r32] - raw[64 + r32];
+      return f32x4{raw[64 * hf + r32], raw[128 + r32], c3, 0.f};  // LSE of side hf, g, term 3
+    };
+    auto stats_store = [&](const f32x4& rv) {
+      const float g = rv[1];
+      wst[wave][hf][r32] = rv[0] * kLog2e - log2_weight(g) - esh;
+      if (hf == 0)
+        wst[wave][2][r32] = g < 0.f ? -1.f : 1.f;
+      else if (NSTAT == 4)
+        wst[wave][3][r32] = JS ? rv[2] * kLog2e : rv[2];
+      tile_neg = __builtin_amdgcn_ballot_w64(g < 0.f) != 0;
+    };
+
+    // Vector work of tile s (ring slot u at sl): probabilities from the saved statistics, then dS.
+    auto vector_phase = [&](int s, int u, const char* sl, auto f16c) {
+      constexpr bool F16 = decltype(f16c)::value;
+      bool skip, full;
+      tile_state(s, skip, full);
+      if (NG == 1 && skip) return;  // ping-pong: a skipped tile goes through the masked path (all zero)
+      bool neg = false;  // some row weight of the tile is negative
+      if constexpr (!OWN_Q && !MCONV) {  // statistics of the 32 streamed queries, converted by each wave
+        const float* raw = reinterpret_cast<const float*>(sl + TILE);
+#pragma unroll
+        for (int k = 0; k < NSTAT; ++k) {
+          const float v = convert_one(k, raw);
+          wst[wave][k][r32] = k == 2 ? (v < 0.f ? -1.f : 1.f) : v;
         }
-        const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
-        if constexpr (TEACHER) {
-          v = pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
-        } else {
-          const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
-          v = ps - pt;
-        }
-        ds[i] = v;
+        neg = __builtin_amdgcn_ballot_w64(raw[128 + r32] < 0.f) != 0;
       }
-    }
-    if (neg) {  // key owner, a tile with a negative row weight: dS takes the sign of g
-      asm volatile("");  // keep this a branch: taken only for such tiles
-      const float(*cs)[32] = wst[wave];
+      if constexpr (MCONV) neg = tile_neg;
+      const int sb = (t_begin + s) * BS;
+      float ds[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 sg4 = *reinterpret_cast<const f32x4*>(&cs[2][8 * g4 + 4 * hf]);
+        // The row weight is not applied here: the query owner scales each output row by it at the
+        // store, the key owner has it folded into the statistics (sign below).
+        f32x4 lt4, ls4, cc4;
+        if constexpr (OWN_Q) {
+          lt4 = f32x4{own_lt, own_lt, own_lt, own_lt};
+          ls4 = f32x4{own_ls, own_ls, own_ls, own_ls};
+          cc4 = f32x4{own_c, own_c, own_c, own_c};
+        } else {
+          const int ql = 8 * g4 + 4 * hf;
+          const float(*cs)[32] = wst[wave];
+          lt4 = *reinterpret_cast<const f32x4*>(&cs[0][ql]);
+          ls4 = *reinterpret_cast<const f32x4*>(&cs[1][ql]);
+          cc4 = (TEACHER || JS) ? *reinterpret_cast<const f32x4*>(&cs[3][ql]) : f32x4{};
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ds[4 * g4 + e] *= sg4[e];
-      }
-    }
-    if (!full) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int sr = sb + acc_row(i, hf);
-        const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
-        ds[i] = ok ? ds[i] : 0.f;
-      }
-    }
-    if constexpr (F16)
-      dsr.set16(ds);
-    else
-      dsr.set(ds);
-  };
-  // Matrix-core work of tile s (ring slot at sl): the gradient product, and the two logit products.
-  auto grad_phase = [&](int s, const char* sl) {
-    bool skip, full;
-    tile_state(s, skip, full);
-    if (!skip) grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sl : sl + BS * RBT, toff, lane);
-  };
-  auto logit_phase = [&](int s, const char* sl) {
-    bool skip, full;
-    tile_state(s, skip, full);
-    if (!skip) {
-      st = f32x16{};
-      ss = f32x16{};
-      tile_dot2_swz<T, DT, DS>(st, ss, sl, sl + BS * RBT, off_t, off_s, ot_r, os_r);
-      if constexpr (sizeof(T) == 2) sched_read_ahead<NRL, 4>();
-    }
-  };
-  // Matrix phase of the ping-pong: gradient product of tile s-1 (slot sp), logit products of
-  // tile s (slot sc), as one straight run of LDS reads and MFMAs so that the reads for the logit
-  // products go out while the gradient MFMAs still run.  It has no branches: a tile that a wave
-  // skips has an all-zero dS (its vector phase masks every element), at s = 0 the gradient
-  // product adds a zero dS times ring slot 3 (zero-filled before the first barrier; tile 3 only
-  // arrives in period 1), and at s = ntile the logit products (of a tile that has landed, so
-  // finite) are not used.  Those cost under one percent of the MFMA work of a causal problem and
-  // keep a single register assignment for the accumulators.
-  auto matrix_phase = [&](const char* sp, const char* sc) {
-    grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sp : sp + BS * RBT, toff, lane);
-    st = f32x16{};
-    ss = f32x16{};
-    tile_dot2_swz<T, DT, DS>(st, ss, sc, sc + BS * RBT, off_t, off_s, ot_r, os_r);
-    if constexpr (sizeof(T) == 2) sched_read_ahead<NRG + NRL, 6>();
-  };
-  bool risky = false;  // fast path: some converted value left the safe range (see HalfToF16)
-  // Fast matrix phase: gradient product of tile s-1 from its fp16 copy at hp, logit products of
-  // tile s (ring slot sc), and this group's half of tile s converted to fp16 at hd.  The order is
-  // fixed by scheduling barriers: LDS reads go out LA logit steps (of two MFMAs) ahead of their
-  // MFMAs; the conversion's read goes out with the first logit reads and its VALU steps ride behind
-  // logit MFMAs from step CD on, when the value has arrived.  dma(part) queues the two parts of this
-  // wave's share of a later tile behind the logit MFMAs of steps DM0 and DM1: a DMA instruction can
-  // wait at issue while the memory pipeline takes other waves' DMA, and there the matrix core keeps
-  // working through the MFMAs already issued.
-  auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd, int u, auto&& dma) {
-    if constexpr (FAST) {
-      // key owner: this wave converts the statistics of tile s here (see stats_read)
-      constexpr int NDB = DX / 32, NT2 = RBT / 32, NS2 = RBS / 32, NM = NT2 > NS2 ? NT2 : NS2;
-      constexpr int LA = 2, CD = 2, DM0 = 1, DM1 = NM > 4 ? 4 : NM - 1;
-      using Conv = HalfToF16<HROW / 2>;
-      const char* tt = sc;
-      const char* ts = sc + BS * RBT;
-      auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-      u32x4 b0[NDB], b1[NDB];
-      grad_operands<DX, RBX>(b0, hp, toff, 0);
-      fence();
-      grad_operands<DX, RBX>(b1, hp, toff, 1);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[0], b0[db]);
-      fence();
-      u32x4 at[NM], as[NM];
-      auto lread = [&](int c) {
-        if (c < NT2) at[c] = lds_read16(tt + off_t[c]);
-        if (c < NS2) as[c] = lds_read16(ts + off_s[c]);
-      };
-#pragma unroll
-      for (int c = 0; c < LA; ++c) lread(c);
-      Conv cv;
-      cv.read(TEACHER ? tt : ts, grp, tid & 255);
-      f32x4 rv = {};
-      if constexpr (MCONV) rv = stats_read(sc);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[1], b1[db]);
-      fence();
-      st = f32x16{};
-      ss = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NM; ++c) {
-        if (c + LA < NM) lread(c + LA);
-        if (c < NT2) mma_chunk<T>(st, at[c], ot_r[c]);
-        if (c < NS2) mma_chunk<T>(ss, as[c], os_r[c]);
-        if (c >= CD && c - CD < Conv::NWD) cv.step(c - CD);
-        if (c - CD == Conv::NWD) risky |= cv.finish(hd);
-        if (MCONV && c == NM - 2) stats_store(rv);
-        if (c == DM0) dma(std::integral_constant<int, 0>{});
-        if (c == DM1) dma(std::integral_constant<int, 1>{});
-        fence();
-      }
-      if constexpr (NM - CD <= Conv::NWD) {  // short logit runs: whatever steps remain
-#pragma unroll
-        for (int p = NM - CD; p < Conv::NWD; ++p) cv.step(p);
-        risky |= cv.finish(hd);
-      }
-    }
-  };
-
-  const int pbeg = GRP ? sp * GX / NSP : 0, pend = GRP ? (sp + 1) * GX / NSP : 1;
-  // Every pass over the stream, into dacc; F16: with the fast gradient product.
-  auto run = [&](auto f16c) {
-    constexpr bool F16 = decltype(f16c)::value;
-    set_offsets();
-    if constexpr (F16 && !OWN_Q) {
-      // the largest |g| (times the row's bound on |dS|) of the queries this workgroup streams, over
-      // all its passes, read up front
-      float gm = 0.f;
-      for (int pass = pbeg; pass < pend; ++pass) {
-        const int64_t r0 = ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
-        const float* gp = a.g + r0;
-        for (int q = t_begin * BS + tid; q < n_str; q += 16 * NT) {  // 16 loads in flight per lane
-          float v[16], c[16];
-#pragma unroll
-          for (int k = 0; k < 16; ++k) v[k] = gp[min(q + k * NT, n_str - 1)];  // unconditional loads
-          if constexpr (KLT) {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) c[k] = a.kl[r0 + min(q + k * NT, n_str - 1)];
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float v;
+          if constexpr (JS) {
+            // P (log2(P/M) - KL(P || M) log2 e) of the gradient's side, with r = log2(P_s/P_t) and
+            // log2(P_t/M) = w - max(r, 0), log2(P_s/M) = w + min(r, 0), w = 1 - log2(1 + 2^-|r|)
+            const float x = fmaf(st[i], a.c_t, -lt4[e]), y = fmaf(ss[i], a.c_s, -ls4[e]);
+            const float r = y - x;
+            const float w = 1.f - fast_log2(1.f + fast_exp2(-fabsf(r)));
+            v = TEACHER ? fast_exp2(x) * (w - fmaxf(r, 0.f) - cc4[e]) : fast_exp2(y) * (w + fminf(r, 0.f) - cc4[e]);
+            ds[i] = v;
+            continue;
           }
-#pragma unroll
-          for (int k = 0; k < 16; ++k) gm = fmaxf(gm, fabsf(v[k]) * (KLT ? teacher_ds_bound(c[k]) : 1.f));
+          const float pt = fast_exp2(fmaf(st[i], a.c_t, -lt4[e]));
+          if constexpr (TEACHER) {
+            v = pt * (scaled_diff(st[i], a.scale_t, ss[i], a.scale_s) - cc4[e]);
+          } else {
+            const float ps = fast_exp2(fmaf(ss[i], a.c_s, -ls4[e]));
+            v = ps - pt;
+          }
+          ds[i] = v;
         }
       }
+      if (neg) {  // key owner, a tile with a negative row weight: dS takes the sign of g
+        asm volatile("");  // keep this a branch: taken only for such tiles
+        const float(*cs)[32] = wst[wave];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
-      if (lane == 0) gred[wave] = gm;
-      __syncthreads();
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 sg4 = *reinterpret_cast<const f32x4*>(&cs[2][8 * g4 + 4 * hf]);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) gm = fmaxf(gm, gred[w]);
-      esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // gm < 2^e, e = frexp exponent
-    } else {
-      esh = F16 ? 13.f : 0.f;  // |dS| < 2 (KL student, either JS half); KL teacher rows: below
-    }
-    fast_run = F16;
-    for (int pass = pbeg; pass < pend; ++pass) {
-      set_head(a, ho * GX + pass);
-      set_rsrc();
-      if constexpr (OWN_Q) {
-        if (ovalid) {
-          // KL teacher: this row's own shift, 14 - e with 2^e above the row's bound on |dS|
-          const float sh = (F16 && KLT) ? (float)(14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(kl_bh[orow]))) : esh;
-          own_lt = lse_t_bh[orow] * kLog2e - sh;
-          own_ls = lse_s_bh[orow] * kLog2e - sh;
-          if constexpr (JS)
-            own_c = (TEACHER ? kl_bh[orow] : fmaf(2.f, js_bh[orow], -kl_bh[orow])) * kLog2e;
-          else if constexpr (TEACHER)
-            own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
+          for (int e = 0; e < 4; ++e) ds[4 * g4 + e] *= sg4[e];
         }
       }
-      {
-        float z[16] = {};
-        if constexpr (F16)
-          dsr.set16(z);
-        else
-          dsr.set(z);
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int sr = sb + acc_row(i, hf);
+          const bool ok = sr < n_str && (!CAUSAL || (OWN_Q ? sr <= orow + off : orow <= sr + off));
+          ds[i] = ok ? ds[i] : 0.f;
+        }
       }
-      if constexpr (F16) {  // zero the fp16 copy that the s = 0 gradient product reads (times a zero dS)
-        static_assert(HROW % 16 == 0, "copy fill");
-#pragma unroll
-        for (int o = 16 * tid; o < HROW; o += 16 * NT) *reinterpret_cast<u32x4*>(h16[1] + o) = u32x4{};
-      } else if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
-        static_assert(TILE % 16 == 0, "slot fill");
-#pragma unroll
-        for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
+      if constexpr (F16)
+        dsr.set16(ds);
+      else
+        dsr.set(ds);
+    };
+    // Matrix-core work of tile s (ring slot at sl): the gradient product, and the two logit products.
+    auto grad_phase = [&](int s, const char* sl) {
+      bool skip, full;
+      tile_state(s, skip, full);
+      if (!skip) grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sl : sl + BS * RBT, toff, lane);
+    };
+    auto logit_phase = [&](int s, const char* sl) {
+      bool skip, full;
+      tile_state(s, skip, full);
+      if (!skip) {
+        st = f32x16{};
+        ss = f32x16{};
+        tile_dot2_swz<T, DT, DS>(st, ss, sl, sl + BS * RBT, off_t, off_s, ot_r, os_r);
+        if constexpr (sizeof(T) == 2) sched_read_ahead<NRL, 4>();
       }
-      wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
+    };
+    // Matrix phase of the ping-pong: gradient product of tile s-1 (slot sp), logit products of
+    // tile s (slot sc), as one straight run of LDS reads and MFMAs so that the reads for the logit
+    // products go out while the gradient MFMAs still run.  It has no branches: a tile that a wave
+    // skips has an all-zero dS (its vector phase masks every element), at s = 0 the gradient
+    // product adds a zero dS times ring slot 3 (zero-filled before the first barrier; tile 3 only
+    // arrives in period 1), and at s = ntile the logit products (of a tile that has landed, so
+    // finite) are not used.  Those cost under one percent of the MFMA work of a causal problem and
+    // keep a single register assignment for the accumulators.
+    auto matrix_phase = [&](const char* sp, const char* sc) {
+      grad_product<T, DX, RBX>(dacc, dsr, TEACHER ? sp : sp + BS * RBT, toff, lane);
+      st = f32x16{};
+      ss = f32x16{};
+      tile_dot2_swz<T, DT, DS>(st, ss, sc, sc + BS * RBT, off_t, off_s, ot_r, os_r);
+      if constexpr (sizeof(T) == 2) sched_read_ahead<NRG + NRL, 6>();
+    };
+    bool risky = false;  // fast path: some converted value left the safe range (see HalfToF16)
+    // Fast matrix phase: gradient product of tile s-1 from its fp16 copy at hp, logit products of
+    // tile s (ring slot sc), and this group's half of tile s converted to fp16 at hd.  The order is
+    // fixed by scheduling barriers: LDS reads go out LA logit steps (of two MFMAs) ahead of their
+    // MFMAs; the conversion's read goes out with the first logit reads and its VALU steps ride behind
+    // logit MFMAs from step CD on, when the value has arrived.  dma(part) queues the two parts of this
+    // wave's share of a later tile behind the logit MFMAs of steps DM0 and DM1: a DMA instruction can
+    // wait at issue while the memory pipeline takes other waves' DMA, and there the matrix core keeps
+    // working through the MFMAs already issued.
+    auto matrix_phase16 = [&](const char* hp, const char* sc, char* hd, int u, auto&& dma) {
+      if constexpr (FAST) {
+        // key owner: this wave converts the statistics of tile s here (see stats_read)
+        constexpr int NDB = DX / 32, NT2 = RBT / 32, NS2 = RBS / 32, NM = NT2 > NS2 ? NT2 : NS2;
+        constexpr int LA = 2, CD = 2, DM0 = 1, DM1 = NM > 4 ? 4 : NM - 1;
+        using Conv = HalfToF16<HROW / 2>;
+        const char* tt = sc;
+        const char* ts = sc + BS * RBT;
+        auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+        u32x4 b0[NDB], b1[NDB];
+        grad_operands<DX, RBX>(b0, hp, toff, 0);
+        fence();
+        grad_operands<DX, RBX>(b1, hp, toff, 1);
 #pragma unroll
-      for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
-      wait_tile();
-      __syncthreads();
-      if constexpr (NG == 2) {
-        // Periods s = 0 .. ntile, one workgroup barrier at the end of each.  In period s group 0 runs
-        // the matrix phase of tile s, then its vector phase; group 1 runs the vector phase of tile s-1,
-        // then the matrix phase of tile s, so on every SIMD one wave is in its matrix phase while the
-        // other is in its vector phase, and each wave moves on to its second phase as soon as it is
-        // done with the first.  No wave reads in a period what another wave writes in that period:
-        // a matrix phase reads tile s (landed and published by the previous barrier) and the fp16
-        // copy of tile s-1 (both halves written in period s-1), and writes its half of the copy of
-        // tile s into the other buffer; the statistics are the wave's own.  Ring: both groups issue
-        // their shares of tile s+PD in period s, into the slot of tile s-2, last read in period s-1
-        // (fast path: within the matrix phase of tile s; hi + lo path: group 0 after its matrix
-        // phase, group 1 before its vector phase of tile s-1); each wave waits for its share of
-        // tile s+1 before the barrier that ends period s.  The last slot, read by the s = 0
-        // gradient product of the hi + lo path, first receives a tile in period 1.
-        if (!F16 && grp == 1) issue(PD, PD);  // group 1's share of tile PD (period 0 has no vector phase for it)
-        for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
+        for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[0], b0[db]);
+        fence();
+        u32x4 at[NM], as[NM];
+        auto lread = [&](int c) {
+          if (c < NT2) at[c] = lds_read16(tt + off_t[c]);
+          if (c < NS2) as[c] = lds_read16(ts + off_s[c]);
+        };
 #pragma unroll
-          for (int u = 0; u < NBUF; ++u) {
-            const int s = s0 + u;
-            if (s <= ntile) {
-              // matrix phase of tile s: first half of period s (group 0) or second half (group 1)
-              if constexpr (F16) {
-                matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1], u,  // converts the statistics too
-                               [&](auto part) { issue_part(s + PD, (u + PD) % NBUF, part); });
-              } else {
-                matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
-                if constexpr (MCONV) stats_store(stats_read(slot_ptr(u)));  // tile s landed before this phase
+        for (int c = 0; c < LA; ++c) lread(c);
+        Conv cv;
+        cv.read(TEACHER ? tt : ts, grp, tid & 255);
+        f32x4 rv = {};
+        if constexpr (MCONV) rv = stats_read(sc);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) mma_chunk<_Float16>(dacc[db], dsr.h[1], b1[db]);
+        fence();
+        st = f32x16{};
+        ss = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NM; ++c) {
+          if (c + LA < NM) lread(c + LA);
+          if (c < NT2) mma_chunk<T>(st, at[c], ot_r[c]);
+          if (c < NS2) mma_chunk<T>(ss, as[c], os_r[c]);
+          if (c >= CD && c - CD < Conv::NWD) cv.step(c - CD);
+          if (c - CD == Conv::NWD) risky |= cv.finish(hd);
+          if (MCONV && c == NM - 2) stats_store(rv);
+          if (c == DM0) dma(std::integral_constant<int, 0>{});
+          if (c == DM1) dma(std::integral_constant<int, 1>{});
+          fence();
+        }
+        if constexpr (NM - CD <= Conv::NWD) {  // short logit runs: whatever steps remain
+#pragma unroll
+          for (int p = NM - CD; p < Conv::NWD; ++p) cv.step(p);
+          risky |= cv.finish(hd);
+        }
+      }
+    };
+
+    const int pbeg = GRP ? sp * GX / NSP : 0, pend = GRP ? (sp + 1) * GX / NSP : 1;
+    // Every pass over the stream, into dacc; F16: with the fast gradient product.
+    auto run = [&](auto f16c) {
+      constexpr bool F16 = decltype(f16c)::value;
+      set_offsets();
+      if constexpr (F16 && !OWN_Q) {
+        // the largest |g| (times the row's bound on |dS|) of the queries this workgroup streams, over
+        // all its passes, read up front
+        float gm = 0.f;
+        for (int pass = pbeg; pass < pend; ++pass) {
+          const int64_t r0 = ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
+          const float* gp = a.g + r0;
+          for (int q = t_begin * BS + tid; q < n_str; q += 16 * NT) {  // 16 loads in flight per lane
+            float v[16], c[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = gp[min(q + k * NT, n_str - 1)];  // unconditional loads
+            if constexpr (KLT) {
+#pragma unroll
+              for (int k = 0; k < 16; ++k) c[k] = a.kl[r0 + min(q + k * NT, n_str - 1)];
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) gm = fmaxf(gm, fabsf(v[k]) * (KLT ? teacher_ds_bound(c[k]) : 1.f));
+          }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+        if (lane == 0) gred[wave] = gm;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) gm = fmaxf(gm, gred[w]);
+        esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // gm < 2^e, e = frexp exponent
+      } else {
+        esh = F16 ? 13.f : 0.f;  // |dS| < 2 (KL student, either JS half); KL teacher rows: below
+      }
+      fast_run = F16;
+      for (int pass = pbeg; pass < pend; ++pass) {
+        set_head(a, ho * GX + pass);
+        set_rsrc();
+        if constexpr (OWN_Q) {
+          if (ovalid) {
+            // KL teacher: this row's own shift, 14 - e with 2^e above the row's bound on |dS|
+            const float sh = (F16 && KLT) ? (float)(14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(kl_bh[orow]))) : esh;
+            own_lt = lse_t_bh[orow] * kLog2e - sh;
+            own_ls = lse_s_bh[orow] * kLog2e - sh;
+            if constexpr (JS)
+              own_c = (TEACHER ? kl_bh[orow] : fmaf(2.f, js_bh[orow], -kl_bh[orow])) * kLog2e;
+            else if constexpr (TEACHER)
+              own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
+          }
+        }
+        {
+          float z[16] = {};
+          if constexpr (F16)
+            dsr.set16(z);
+          else
+            dsr.set(z);
+        }
+        if constexpr (F16) {  // zero the fp16 copy that the s = 0 gradient product reads (times a zero dS)
+          static_assert(HROW % 16 == 0, "copy fill");
+#pragma unroll
+          for (int o = 16 * tid; o < HROW; o += 16 * NT) *reinterpret_cast<u32x4*>(h16[1] + o) = u32x4{};
+        } else if constexpr (NG == 2) {  // zero the last slot: the s = 0 gradient product reads it (times a zero dS)
+          static_assert(TILE % 16 == 0, "slot fill");
+#pragma unroll
+          for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
+        }
+        wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
+#pragma unroll
+        for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
+        wait_tile();
+        __syncthreads();
+        if constexpr (NG == 2) {
+          // Periods s = 0 .. ntile, one workgroup barrier at the end of each.  In period s group 0 runs
+          // the matrix phase of tile s, then its vector phase; group 1 runs the vector phase of tile s-1,
+          // then the matrix phase of tile s, so on every SIMD one wave is in its matrix phase while the
+          // other is in its vector phase, and each wave moves on to its second phase as soon as it is
+          // done with the first.  No wave reads in a period what another wave writes in that period:
+          // a matrix phase reads tile s (landed and published by the previous barrier) and the fp16
+          // copy of tile s-1 (both halves written in period s-1), and writes its half of the copy of
+          // tile s into the other buffer; the statistics are the wave's own.  Ring: both groups issue
+          // their shares of tile s+PD in period s, into the slot of tile s-2, last read in period s-1
+          // (fast path: within the matrix phase of tile s; hi + lo path: group 0 after its matrix
+          // phase, group 1 before its vector phase of tile s-1); each wave waits for its share of
+          // tile s+1 before the barrier that ends period s.  The last slot, read by the s = 0
+          // gradient product of the hi + lo path, first receives a tile in period 1.
+          if (!F16 && grp == 1) issue(PD, PD);  // group 1's share of tile PD (period 0 has no vector phase for it)
+          for (int s0 = 0; s0 <= ntile; s0 += NBUF) {
+#pragma unroll
+            for (int u = 0; u < NBUF; ++u) {
+              const int s = s0 + u;
+              if (s <= ntile) {
+                // matrix phase of tile s: first half of period s (group 0) or second half (group 1)
+                if constexpr (F16) {
+                  matrix_phase16(h16[(u + 1) & 1], slot_ptr(u), h16[u & 1], u,  // converts the statistics too
+                                 [&](auto part) { issue_part(s + PD, (u + PD) % NBUF, part); });
+                } else {
+                  matrix_phase(slot_ptr((u + NBUF - 1) % NBUF), slot_ptr(u));
+                  if constexpr (MCONV) stats_store(stats_read(slot_ptr(u)));  // tile s landed before this phase
+                }
+                if (grp == 1) {  // the end of period s for group 1
+                  wait_tile();
+                  __syncthreads();
+                }
+                // hi + lo path: group 0's share of tile s+PD after its matrix phase (issued at the start of
+                // the period together with group 1's share, the DMA instructions of all eight waves
+                // queued at once)
+                if (!F16 && grp == 0) issue(s + PD, (u + PD) % NBUF);
+                // vector phase of tile s: second half of period s (group 0) or first half of s+1 (group 1)
+                if (s < ntile) {
+                  if (!F16 && grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
+                  vector_phase(s, u, slot_ptr(u), f16c);
+                }
+                if (grp == 0) {  // the end of period s for group 0 (ntile + 1 barriers for each group)
+                  if (s < ntile) wait_tile();
+                  __syncthreads();
+                }
               }
-              if (grp == 1) {  // the end of period s for group 1
+            }
+          }
+        } else {
+          // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
+          // and tile s+1 waited for at its end.
+          for (int s0 = 0; s0 < ntile; s0 += NBUF) {
+#pragma unroll
+            for (int u = 0; u < NBUF; ++u) {
+              const int s = s0 + u;
+              if (s < ntile) {
+                issue(s + PD, (u + PD) % NBUF);
+                logit_phase(s, slot_ptr(u));
+                vector_phase(s, u, slot_ptr(u), f16c);
+                grad_phase(s, slot_ptr(u));
                 wait_tile();
                 __syncthreads();
               }
-              // hi + lo path: group 0's share of tile s+PD after its matrix phase (issued at the start of
-              // the period together with group 1's share, the DMA instructions of all eight waves
-              // queued at once)
-              if (!F16 && grp == 0) issue(s + PD, (u + PD) % NBUF);
-              // vector phase of tile s: second half of period s (group 0) or first half of s+1 (group 1)
-              if (s < ntile) {
-                if (!F16 && grp == 1) issue(s + PD + 1, (u + PD + 1) % NBUF);
-                vector_phase(s, u, slot_ptr(u), f16c);
-              }
-              if (grp == 0) {  // the end of period s for group 0 (ntile + 1 barriers for each group)
-                if (s < ntile) wait_tile();
-                __syncthreads();
-              }
             }
           }
         }
-      } else {
-        // One group: each tile is finished within its step; tile s+PD is issued at the start of step s
-        // and tile s+1 waited for at its end.
-        for (int s0 = 0; s0 < ntile; s0 += NBUF) {
-#pragma unroll
-          for (int u = 0; u < NBUF; ++u) {
-            const int s = s0 + u;
-            if (s < ntile) {
-              issue(s + PD, (u + PD) % NBUF);
-              logit_phase(s, slot_ptr(u));
-              vector_phase(s, u, slot_ptr(u), f16c);
-              grad_phase(s, slot_ptr(u));
-              wait_tile();
-              __syncthreads();
-            }
-          }
-        }
+        wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
+        if (pass + 1 < pend) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
       }
-      wait_vmcnt<0>();  // no DMA may still target the ring when it is refilled or the workgroup exits
-      if (pass + 1 < pend) __syncthreads();  // all waves' DMAs have landed before the ring is refilled
-    }
-  };
-  if constexpr (FAST) {
-    run(std::true_type{});
-    // a streamed value outside the fp16 conversion's safe range, or a non-finite gradient (a
-    // non-finite input): redo the workgroup with the hi + lo product
-    bool bad = risky;
+    };
+    if constexpr (FAST) {
+      run(std::true_type{});
+      // a streamed value outside the fp16 conversion's safe range, or a non-finite gradient (a
+      // non-finite input): redo the workgroup with the hi + lo product
+      bool bad = risky;
 #pragma unroll
-    for (int db = 0; db < DX / 32; ++db)
+      for (int db = 0; db < DX / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bad |= !__builtin_isfinite(dacc[db][i]);
-    if (__syncthreads_or(bad)) {
+        for (int i = 0; i < 16; ++i) bad |= !__builtin_isfinite(dacc[db][i]);
+      if (__syncthreads_or(bad)) {
 #pragma unroll
-      for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
+        for (int db = 0; db < DX / 32; ++db) dacc[db] = f32x16{};
+        run(std::false_type{});
+      }
+    } else {
       run(std::false_type{});
     }
-  } else {
-    run(std::false_type{});
-  }
 
 
-  // JS: dS above is in log2 units and lacks the 1/2 of each half: ln 2 / 2 goes into the scale
-  const float scale = (TEACHER ? a.scale_t : a.scale_s) * (JS ? 0.5f * kLn2 : 1.f);
-  // a split group writes its partial dK into its part of the workspace (same layout as dK)
-  float* out = (OWN_Q ? a.dq : (GRP && NSP > 1 ? a.ws + sp * a.ws_part : a.dk)) +
-               (((int64_t)sg.bs * HX + ho) * (OWN_Q ? a.Nq : a.Nk) + (OWN_Q ? sg.q0 : sg.k0)) * DX;
-  // query owner: dS was formed without the row weight (it is one factor per output row)
-  float rscale[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = o0w + acc_row(i, hf);
-    // fast path: dS was formed times 2^esh, per row for the query owner of KL teacher gradients
-    int sh = (int)esh;
-    if (OWN_Q && KLT && fast_run && r < n_own) sh = 14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(kl_bh[r]));
-    rscale[i] = OWN_Q ? (r < n_own ? ldexpf(scale * g_bh[r], -sh) : 0.f) : ldexpf(scale, -sh);
-  }
-#pragma unroll
-  for (int db = 0; db < DX / 32; ++db) {
+    // JS: dS above is in log2 units and lacks the 1/2 of each half: ln 2 / 2 goes into the scale
+    const float scale = (TEACHER ? a.scale_t : a.scale_s) * (JS ? 0.5f * kLn2 : 1.f);
+    // a split group writes its partial dK into its part of the workspace (same layout as dK)
+    float* out = (OWN_Q ? a.dq : (GRP && NSP > 1 ? a.ws + sp * a.ws_part : a.dk)) +
+                 (((int64_t)sg.bs * HX + ho) * (OWN_Q ? a.Nq : a.Nk) + (OWN_Q ? sg.q0 : sg.k0)) * DX;
+    // query owner: dS was formed without the row weight (it is one factor per output row)
+    float rscale[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = o0w + acc_row(i, hf);
-      if (r < n_own) out[(int64_t)r * DX + db * 32 + r32] = rscale[i] * dacc[db][i];
+      // fast path: dS was formed times 2^esh, per row for the query owner of KL teacher gradients
+      int sh = (int)esh;
+      if (OWN_Q && KLT && fast_run && r < n_own) sh = 14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(kl_bh[r]));
+      rscale[i] = OWN_Q ? (r < n_own ? ldexpf(scale * g_bh[r], -sh) : 0.f) : ldexpf(scale, -sh);
+    }
+#pragma unroll
+    for (int db = 0; db < DX / 32; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = o0w + acc_row(i, hf);
+        if (r < n_own) out[(int64_t)r * DX + db * 32 + r32] = rscale[i] * dacc[db][i];
+      }
     }
   }
 }
 
 // ----------------------------------------------------------------------------------------------
 template <bool JS, typename T, int DT, int DS, bool C, bool TE, bool OWN_Q>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+static hipError_t launch_bwd_t(const BwdArgs& args, hipStream_t s) {
+  BwdArgs a = args;
   const int n_own = OWN_Q ? a.mq : a.mk;  // longest segment (dense batch: all rows)
   // owned heads: query heads, or the key heads of the gradient's side
   const int gx = OWN_Q ? 1 : (TE ? a.gt : a.gs);
-  const int64_t nblk = (int64_t)((n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW) * a.B * (a.H / gx);
+  const int64_t nob = (n_own + BwdTile<T>::BW - 1) / BwdTile<T>::BW;
+  // pairs of owned blocks per workgroup: causal, dense and ungrouped only
+  a.pair = (a.pair && C && gx == 1 && a.cu_q == nullptr) ? 1 : 0;
+  const int64_t nblk = (a.pair ? (nob + 1) / 2 : nob) * a.B * (a.H / gx);
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (!OWN_Q) {

@@ -116,7 +116,8 @@ struct DmaTile {
       vo[j] = pr * (int)pitch + ((pc ^ swz<RB>(pr)) * 16);
     }
   }
-  // Queue the tile whose first row sits at byte offset `toff` of the buffer into LDS at `dst`.
+  // Queue the tile whose first row sits at byte offset `toff` of the buffer into LDS at byte
+  // address `dst` (see lds_addr).
   // Issued as inline asm so that the compiler does not track these LDS writes: callers order
   // them with explicit vmcnt waits and barriers (the destination slot is never read while a DMA
   // into it can be in flight).  The asm has no output register.
@@ -126,8 +127,8 @@ struct DmaTile {
   // wave-uniform flag) passes toff in the SGPR; any other tile (the ragged last one, or one past
   // the end) adds it to the VGPR offset, so its rows beyond the buffer arrive as zeros and no
   // byte outside the buffer is read.  The two asm strings differ so the branches stay separate.
-  __device__ __forceinline__ void issue(const u32x4& rsrc, int toff, bool whole, char* dst, int wave) const {
-    const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)dst);
+  __device__ __forceinline__ void issue(const u32x4& rsrc, int toff, bool whole, uint32_t dst, int wave) const {
+    const uint32_t base = dst;
     const bool on = LPW == 64 || (int)(threadIdx.x & 63) < LPW;  // lanes past LPW stay masked off
     const int stoff = __builtin_amdgcn_readfirstlane(toff);       // wave-uniform: keep it in an SGPR
     if (whole) {
@@ -154,16 +155,22 @@ struct DmaTile {
   }
 };
 
-// One dword per lane from byte offset `voff` of the buffer into LDS at `dst` + 4 * lane (inline
-// asm, untracked like DmaTile::issue).  The whole offset is range-checked: past num_records the
-// lane writes zero.
-__device__ __forceinline__ void dma_dword(const u32x4& rsrc, int voff, char* dst) {
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)dst));
+// One dword per lane from byte offset `voff` of the buffer into LDS at byte address `dst` + 4 * lane
+// (inline asm, untracked like DmaTile::issue).  The whole offset is range-checked: past num_records
+// the lane writes zero.
+__device__ __forceinline__ void dma_dword(const u32x4& rsrc, int voff, uint32_t dst) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(dst);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
                : "s"(m0v), "v"(voff), "s"(rsrc), "s"(0)
                : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ array (its first byte), for the DMA's M0.  Taken from the array
+// itself, not from a generic pointer into it, so that the conversion needs no null check.
+template <class A>
+__device__ __forceinline__ uint32_t lds_addr(A& arr) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)&arr);
 }
 
 // Raw buffer descriptor words (base, stride 0, num_records = bytes, gfx9 data-format word)

@@ -298,8 +298,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   auto slot_ptr = [&](int slot) -> char* { return slot == 0 ? slot0 : (slot == 1 ? slot1 : slot2); };
   auto issue = [&](int tile, int slot) {
     const bool whole = (tile + 1) * BK <= nk;
-    dma_t.issue(rk_t, tile * BK * (int)kt_pitch, whole, slot_ptr(slot), wave);
-    dma_s.issue(rk_s, tile * BK * (int)ks_pitch, whole, slot_ptr(slot) + BK * RBT, wave);
+    const uint32_t dst = slot == 0 ? lds_addr(slot0) : (slot == 1 ? lds_addr(slot1) : lds_addr(slot2));
+    dma_t.issue(rk_t, tile * BK * (int)kt_pitch, whole, dst, wave);
+    dma_s.issue(rk_s, tile * BK * (int)ks_pitch, whole, dst + BK * RBT, wave);
   };
   // this lane's operand chunk offsets (row r32 of a tile), loop-invariant
   int off_t[NCT / 2], off_s[NCS / 2];

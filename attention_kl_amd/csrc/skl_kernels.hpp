@@ -64,6 +64,9 @@ struct BwdArgs {
   // Small grids (set by the launcher): inside each XCD's share of whole heads, workgroups go out in order
   // of stream length across those heads instead of head by head (see bwd_kernel).
   int32_t len_major;
+  // Causal dense problems whose two kernels run side by side (set by the launcher): each workgroup
+  // takes a long owned block and then a short one (see bwd_kernel), half the workgroups of one kernel.
+  int32_t pair;
   float c_t, c_s;            // scale * log2(e)
   float scale_t, scale_s;
 };

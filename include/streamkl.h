@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10600 /* 1.6.0: small backward problems on two streams; 1.5.0: allocation-free backward; 1.4.0: workspace for grouped keys;
+#define STREAMKL_VERSION 10601 /* 1.6.1: paired causal blocks on the two streams; 1.6.0: small backward problems on two streams; 1.5.0: allocation-free backward; 1.4.0: workspace for grouped keys;
                                   1.3.0: Jensen-Shannon; 1.2.0: packed batches; 1.1.0: key heads */
 
 typedef enum {
@@ -154,7 +154,9 @@ int streamkl_fwd(const streamkl_problem_t* p,
  * the device's side stream instead and run beside the key-owner ones: the side
  * stream first waits for everything issued to hip_stream before the call, and
  * hip_stream then waits for the side stream's kernels (event record and wait, so
- * a HIP graph capture of hip_stream takes both).  Calls that overlap in time share
+ * a HIP graph capture of hip_stream takes both); for a causal dense batch each
+ * workgroup of these kernels then runs a long owned block and a short one, half
+ * as many workgroups per kernel (same results bit for bit).  Calls that overlap in time share
  * the side stream in the order they reach it; a capture of hip_stream should not
  * overlap another thread's uncaptured calls on the same device.  Should recording
  * or waiting on the join event fail, the call returns STREAMKL_ERR_LAUNCH and the
