@@ -190,6 +190,24 @@ int fwd_fold(const skl::FwdArgs& a) {
   return small_grid((int64_t)((a.mq + 127) / 128) * a.B * a.H) ? 1 : 0;
 }
 
+// Compute units per XCD of the current device (0 if unknown).
+int device_cpx() {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  const DeviceSide* d = device_side(false);
+  return d != nullptr && d->ncu > 0 ? d->ncu / 8 : 0;
+}
+
+// Small causal forward grids (dense bf16, Nk >= Nq, at least two query blocks of 128 rows, at most twice
+// the device's compute units in workgroups, so a third of each CU's workgroup slots idle): given a
+// workspace of this many floats, the key tiles of the later half of each head's query blocks are
+// split over two workgroups, whose row states (5 floats a row) a second kernel merges.  0: no split.
+int64_t fwd_split_floats(const streamkl_problem_t* p) {
+  if (!p->causal || p->cu_seqlens_q != nullptr || p->dtype != STREAMKL_BF16 || p->Nk < p->Nq) return 0;
+  const int64_t nqb = (p->Nq + 127) / 128;
+  if (nqb < 2 || !small_grid(nqb * p->B * p->H)) return 0;
+  return p->B * p->H * (nqb - nqb / 2) * 2 * 5 * 128;
+}
+
 skl::BwdArgs bwd_args(const streamkl_problem_t* p, const void* qt, const void* kt, const void* qs, const void* ks,
                       const float* lse_t, const float* lse_s, const float* kl, const float* g, bool own_q) {
   skl::BwdArgs a{};
@@ -249,6 +267,12 @@ int streamkl_fwd(const streamkl_problem_t* p, const void* q_t, const void* k_t, 
   a.scale_t = p->scale_t;
   a.eq_ok = 1;
   a.fold = fwd_fold(a);
+  const int64_t need = fwd_split_floats(p);
+  if (need > 0 && p->workspace != nullptr && p->workspace_floats >= need) {
+    a.part = p->workspace;
+    a.qsplit = (int32_t)((p->Nq + 127) / 128 / 2);
+    a.cpx = device_cpx();
+  }
   return to_status(skl::launch_fwd(a, p->dtype, p->d_t, p->d_s, p->causal != 0, (hipStream_t)hip_stream));
 }
 
@@ -474,7 +498,7 @@ int64_t streamkl_workspace_floats(const streamkl_problem_t* p) {
     const int64_t n = nb * hk[side] <= 65535 ? g : skl::split_wanted(g, nob * p->B * hk[side]);
     if (n > 1) best = std::max(best, n * nb * hk[side] * p->Nk * dd[side]);
   }
-  return best;
+  return std::max(best, fwd_split_floats(p));  // the forward's split of small causal grids
 }
 
 }  // extern "C"

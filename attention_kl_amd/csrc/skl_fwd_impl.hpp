@@ -232,18 +232,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   // share a CU: with `fold`, the first half goes out longest first across the heads and the second
   // half shortest first, so each CU's two query blocks hold about the same number of key tiles
   // (head by head, causal, the CU of position 0 held the two longest).
+  // Split (a.part): a head has nqb + nsb units, longest first: units 2i and 2i + 1 are the two key
+  // halves of query block nqb-1-i (i < nsb), then come the whole blocks qsplit-1 .. 0.  Three
+  // workgroups share a CU, at positions j, j + cpx and j + 2 cpx of the XCD's share: the share's units
+  // are ranked by length across its heads and dealt out in a serpentine (ranks j, 2 cpx - 1 - j,
+  // 2 cpx + j), so each CU mixes long and short units.
+  const bool split = CAUSAL && !JS && a.part != nullptr && a.qsplit < nqb;
+  const int nsb = split ? nqb - a.qsplit : 0;  // split blocks per head
+  const int nun = nqb + nsb;                   // units per head
   const int nblk = (int)gridDim.x;
   const int S8 = nblk / 8, j8 = (int)(blockIdx.x / 8);
   int pos = j8;  // position in the XCD's eighth, head-major
-  if (a.fold && S8 % nqb == 0 && S8 % 2 == 0) {
+  if (split) {
+    if (S8 % nun == 0 && a.cpx > 0 && S8 % a.cpx == 0) {
+      const int hs = S8 / nun;  // whole heads in the eighth
+      const int k = j8 / a.cpx, r = j8 % a.cpx;
+      const int rank = k * a.cpx + ((k & 1) ? a.cpx - 1 - r : r);
+      pos = (rank % hs) * nun + rank / hs;
+    }
+  } else if (a.fold && S8 % nqb == 0 && S8 % 2 == 0) {
     const int hs = S8 / nqb;                                     // whole heads in the eighth
     const int pp = j8 < S8 / 2 ? j8 : (S8 + S8 / 2 - 1 - j8);  // rank by length
     pos = (pp % hs) * nqb + pp / hs;
   }
   const int L = (int)(blockIdx.x % 8) * S8 + pos;
   const bool xcd = nblk % 8 == 0;
-  const int bh = xcd ? L / nqb : blockIdx.x % nbh;
-  const int qi = xcd ? L % nqb : blockIdx.x / nbh;
+  const int bh = xcd ? L / nun : blockIdx.x % nbh;
+  const int ui = xcd ? L % nun : blockIdx.x / nbh;  // unit of the head
+  int qi = ui, part = -1;                          // part: which key half of a split block, -1 whole
+  if (split) {
+    if (ui < 2 * nsb) {
+      qi = ui / 2;
+      part = ui % 2;
+    } else {
+      qi = ui - nsb;
+    }
+  }
   const int qb = CAUSAL ? (nqb - 1 - qi) : qi;  // causal: longest rows first
   const int b = bh / a.H, h = bh % a.H;
   const Segment sg = segment_of(a, b);
@@ -286,7 +310,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 
   const int q_last = min(nq, q0 + BQ) - 1;
   const int kend = CAUSAL ? min(nk, q_last + off + 1) : nk;
-  const int ntiles = max(kend + BK - 1, 0) / BK;  // 0 only for rows with no key (an invalid segment)
+  const int nt_all = max(kend + BK - 1, 0) / BK;  // 0 only for rows with no key (an invalid segment)
+  // key tiles tb .. tb + ntiles - 1 (a half of a split block: the first or the rest); keys from klim
+  // on belong to the other half
+  const int tb = part == 1 ? nt_all / 2 : 0;
+  const int ntiles = part == 0 ? nt_all / 2 : nt_all - tb;
+  const int klim = min(nk, (tb + ntiles) * BK);
 
   // K tiles: buffer->LDS DMA (zero past the last key) into a NBUF-deep ring, two tiles ahead
   const u32x4 rk_t = rsrc_words(kt, nk > 0 ? (uint32_t)((nk - 1) * kt_pitch + RBT) : 0u);
@@ -314,8 +343,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     // The compiler cannot see the DMAs in the hardware's vmcnt; retire every load of its own now,
     // so that none of its waits lands inside the loop, where it would also drain the DMA ring.
     wait_vmcnt<0>();
-    issue(0, 0);
-    issue(1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
+    issue(tb, 0);
+    issue(tb + 1, 1);  // past the last tile a DMA returns zeros into a slot nobody reads
     // One step per tile; the loop is unrolled by the ring depth so every LDS address is a
     // per-lane base plus an immediate.  The tile count is rounded up to a multiple of the ring
     // depth: the extra tiles lie past every row's last key, so they are fully masked and leave the
@@ -328,9 +357,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
         {
           wait_vmcnt<NI>();  // tile t has landed (tile t+1 may still be in flight)
           __syncthreads();   // ... for every wave; and every wave is done with tile t-1
-          issue(t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
+          issue(tb + t + 2, (u + 2) % NBUF);  // into the slot that held tile t-1
           const char* tile = slot_ptr(u);
-          const int kb = t * BK;
+          const int kb = (tb + t) * BK;
           f32x16 st = {}, ss = {};
           if constexpr (EQ) {
             // ss holds dd = st - q_s.k_s: the student chain starts from the finished teacher logits
@@ -359,13 +388,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
           // with every key at -inf the update leaves the state bit for bit unchanged, and the loop
           // keeps one definition of the state (no copies at a join).  Such tiles are under 1% of
           // a causal problem's.
-          const bool full = t < ntiles && kb + 31 < nk && (!CAUSAL || kb + 31 <= q0w + off);
+          const bool full = t < ntiles && kb + 31 < klim && (!CAUSAL || kb + 31 <= q0w + off);
           if (!full) {  // in place, so the update below has one copy of its state
             asm volatile("");  // keep this a branch: the compiler would otherwise select on every tile
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = kb + acc_row(i, hf);
-              const bool ok = key < nk && (!CAUSAL || key <= qrow + off);
+              const bool ok = key < klim && (!CAUSAL || key <= qrow + off);
               // JS: a large finite logit instead of -inf gives P_t = P_s = 0 with a finite r, so
               // the term is an exact zero rather than 0 * NaN
               st[i] = ok ? st[i] : (JS ? -1e30f : -INFINITY);
@@ -440,6 +469,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     merge();
   }
 
+  if (part >= 0) {  // a half of a split block: its row states go to the workspace (fwd_merge_kernel)
+    if (hf == 0 && qrow < nq) {
+      float* ps = a.part + ((int64_t)(bh * nsb + qb - a.qsplit) * 2 + part) * 5 * BQ + (qrow - q0);
+      ps[0] = Mt;
+      ps[BQ] = Ms;
+      ps[2 * BQ] = Lt;
+      ps[3 * BQ] = Ls;
+      ps[4 * BQ] = A;
+    }
+    return;
+  }
   if (hf == 0 && qrow < nq) {
     // true divisions: Ls / Lt is exactly 1 when the two states are bitwise equal
     const int64_t o = stat_index();
@@ -449,21 +489,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   }
 }
 
+// Rows of the split query blocks (dense batch): the two halves' row states (fwd_kernel, in part),
+// merged in a fixed order (first half, then second) and closed as fwd_kernel closes a row.  One
+// thread per row; nsb split blocks per head.
+template <int bq>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const FwdArgs a, int nsb) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (head, split block, row)
+  if (i >= (int64_t)a.B * a.H * nsb * bq) return;
+  const int r = (int)(i % bq);
+  const int64_t u = i / bq;  // head * nsb + split block
+  const int q = (a.qsplit + (int)(u % nsb)) * bq + r;
+  if (q >= a.Nq) return;
+  const float* p0 = a.part + u * 2 * 5 * bq + r;
+  const float* p1 = p0 + 5 * bq;
+  const float Mt = fmaxf(p0[0], p1[0]), Ms = fmaxf(p0[bq], p1[bq]);
+  const float f0 = fast_exp2(p0[0] - Mt), f1 = fast_exp2(p1[0] - Mt);
+  const float g0 = fast_exp2(p0[bq] - Ms), g1 = fast_exp2(p1[bq] - Ms);
+  const float Lt = p0[2 * bq] * f0 + p1[2 * bq] * f1;
+  const float Ls = p0[3 * bq] * g0 + p1[3 * bq] * g1;
+  const float A = p0[4 * bq] * f0 + p1[4 * bq] * f1;
+  const int64_t o = (u / nsb) * a.Nq + q;
+  a.kl[o] = a.scale_t * (A / Lt) + kLn2 * ((Ms - Mt) + fast_log2(Ls / Lt));
+  a.lse_t[o] = kLn2 * (Mt + fast_log2(Lt));
+  a.lse_s[o] = kLn2 * (Ms + fast_log2(Ls));
+}
+
 // ----------------------------------------------------------------------------------------------
 template <bool JS, typename T, int DT, int DS, bool C>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-  const int64_t nqb = (a.mq + FwdTile<T>::BQ - 1) / FwdTile<T>::BQ;
-  const int64_t nblk = nqb * a.B * a.H;
+static hipError_t launch_fwd_t(const FwdArgs& args, hipStream_t s) {
+  constexpr int BQ = FwdTile<T>::BQ;
+  FwdArgs a = args;
+  const int64_t nqb = (a.mq + BQ - 1) / BQ;
+  // split key halves: causal dense KL forward only, from query block qsplit >= 1 on
+  const bool split = C && !JS && a.part != nullptr && a.cu_q == nullptr && a.qsplit >= 1 && a.qsplit < nqb;
+  if (!split) a.part = nullptr;
+  const int64_t nsb = split ? nqb - a.qsplit : 0;
+  const int64_t nblk = (nqb + nsb) * a.B * a.H;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (!JS && sizeof(T) == 2) {
     if (a.c_t == a.c_s && a.eq_ok) {
       hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C, false, true>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s,
                          a);
-      return hipGetLastError();
+    } else {
+      hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C, false, false>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s,
+                         a);
     }
+  } else {
+    hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C, JS, false>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s, a);
   }
-  hipLaunchKernelGGL((fwd_kernel<T, DT, DS, C, JS, false>), dim3((unsigned)nblk), dim3(FwdTile<T>::NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  const int64_t rows = (int64_t)a.B * a.H * nsb * BQ;
+  hipLaunchKernelGGL(fwd_merge_kernel<BQ>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a, (int)nsb);
   return hipGetLastError();
 }
 

@@ -34,6 +34,13 @@ struct FwdArgs {
   // Small grids (set by the launcher): the two workgroups that share a CU pair a long query block with
   // a short one (see fwd_kernel); otherwise an XCD's share goes out head by head.
   int32_t fold;
+  // Small causal grids given a workspace (set by the launcher): the key tiles of query blocks qsplit ..
+  // nqb-1 are split in two halves, each run by a workgroup of its own that stores its row states (five
+  // floats a row) in part; fwd_merge_kernel then merges the two halves in a fixed order and closes
+  // those rows.  part = NULL: no split.  cpx: compute units per XCD (the workgroup order, see fwd_kernel).
+  float* part;
+  int32_t qsplit;
+  int32_t cpx;
 };
 
 struct BwdArgs {

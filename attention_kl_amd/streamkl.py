@@ -116,7 +116,8 @@ def _check(status: int, what: str):
 
 def attach_workspace(p: Problem, device, stream=None):
     """Give p the workspace the library asks for (grouped key heads with few key heads: the key-owner
-    work of each group is then split over several workgroups).  Returns the tensor (or None), which
+    work of each group is then split over several workgroups; small causal forwards: the long query
+    blocks' key tiles are split over two workgroups).  Returns the tensor (or None), which
     must stay alive until the launches that use it are enqueued; torch's allocator keeps it from
     being reused before they run on its stream."""
     import torch
@@ -252,6 +253,7 @@ def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, s
     if out is None:
         out = tuple(torch.empty(p.stat_shape(), dtype=torch.float32, device=qt.device) for _ in range(3))
     kl, lse_t, lse_s = out
+    ws = attach_workspace(p, qt.device, stream)  # noqa: F841 (kept alive through the call)
     _check(lib().streamkl_fwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(kl), _ptr(lse_t),
                               _ptr(lse_s), _stream(stream)), "streamkl_fwd")
     return kl, lse_t, lse_s

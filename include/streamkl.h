@@ -26,8 +26,8 @@
  *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *    allocates no memory and frees nothing: the only HBM it touches beyond the
  *    inputs is the outputs the caller passes (S8: no O(Nq*Nk) buffer), plus, for
- *    grouped key heads only, an optional caller workspace (see
- *    streamkl_workspace_floats) or, for streamkl_bwd_noalloc, a fixed scratch array
+ *    grouped key heads and small causal forwards only, an optional caller workspace
+ *    (see streamkl_workspace_floats) or, for streamkl_bwd_noalloc, a fixed scratch array
  *    the library holds on each GPU.  Its only other state, per device: a second HIP
  *    stream (default priority) and two events, made by the first streamkl_bwd or
  *    streamkl_js_bwd call that runs kernels side by side and kept until the process
@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define STREAMKL_VERSION 10601 /* 1.6.1: paired causal blocks on the two streams; 1.6.0: small backward problems on two streams; 1.5.0: allocation-free backward; 1.4.0: workspace for grouped keys;
+#define STREAMKL_VERSION 10700 /* 1.7.0: split key halves for small causal forwards; 1.6.1: paired causal blocks on the two streams; 1.6.0: small backward problems on two streams; 1.5.0: allocation-free backward; 1.4.0: workspace for grouped keys;
                                   1.3.0: Jensen-Shannon; 1.2.0: packed batches; 1.1.0: key heads */
 
 typedef enum {
@@ -123,19 +123,25 @@ typedef struct {
   int64_t workspace_floats;    /* its size in floats                                               */
 } streamkl_problem_t;
 
-/* Workspace (grouped key heads only).  Without one, a key-owner launch whose gradient side has
+/* Workspace (grouped key heads; small causal forwards).  Without one, a key-owner launch whose gradient side has
  * G > 1 query heads per key head makes G passes per workgroup, and when the key heads are few the
  * grid cannot fill the chip.  With a workspace the size of an ungrouped dK (B H Nk d floats), the
  * ungrouped kernel runs over every query head, each writing its contribution to its own slice, and
  * the G slices of each key head are summed in head order into dk; with a smaller workspace each
  * group's passes are split over as many workgroups as it holds partial dK, summed in a fixed order.
  * Results are bitwise repeatable for a given workspace size (not bitwise equal across sizes).
- * streamkl_workspace_floats(p) is the size of the best arrangement for p (0 when no side is
- * grouped).  The workspace is used in stream order: overlapping calls need their own.            */
+ * streamkl_fwd of a small causal problem (dense bf16 batch, Nk >= Nq, at least two query blocks of
+ * 128 rows and at most twice the device's compute units in such blocks) given a workspace of at
+ * least 1280 B H ceil(ceil(Nq / 128) / 2) floats splits the key tiles of the later half of each
+ * head's query blocks over two workgroups and merges their row states (5 floats a row) in a fixed
+ * order with a second kernel: repeatable bits, within float rounding of the unsplit forward.
+ * streamkl_workspace_floats(p) is the size of the best arrangement for p, for both directions (0
+ * when neither uses one).  The workspace is used in stream order: overlapping calls need their own. */
 int64_t streamkl_workspace_floats(const streamkl_problem_t* p);
 
 /* Forward (S4): KL_i, LSE_t,i, LSE_s,i for every row, float32 [B, H, Nq] each.
- * One pass over the keys; per row only five running floats are kept.             */
+ * One pass over the keys; per row only five running floats are kept (a small
+ * causal problem given a workspace: see the workspace note above).               */
 int streamkl_fwd(const streamkl_problem_t* p,
                  const void* q_t, const void* k_t, const void* q_s, const void* k_s,
                  float* kl, float* lse_t, float* lse_s,

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     assert set(declared) <= exported
-    assert S.version() == 10601
+    assert S.version() == 10700
 
 
 def test_status_strings():
