@@ -244,16 +244,19 @@ _PACKED_DOC = """Packed variable-length batch: cu_seqlens_q, cu_seqlens_k (and o
 
 
 def fwd(qt, kt, qs, ks, *, causal: bool, scale_t=None, scale_s=None, out=None, stream=None, cu_seqlens_q=None,
-        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True
+        cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, validate=True, split=True
         ) -> Tuple["torch.Tensor", "torch.Tensor", "torch.Tensor"]:
-    """Per-row KL(P_t || P_s), LSE_t, LSE_s as float32 [B, H, Nq] (streamkl_fwd)."""
+    """Per-row KL(P_t || P_s), LSE_t, LSE_s as float32 [B, H, Nq] (streamkl_fwd).  A small causal
+    problem gets the workspace that lets the library split its long query blocks' keys over two
+    workgroups (results within float rounding of the unsplit forward); split=False passes none, so
+    every query block is one workgroup, the arrangement a packed batch takes."""
     import torch
     p = make_problem(qt, kt, qs, ks, causal, scale_t, scale_s, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                      max_seqlen_k, validate)
     if out is None:
         out = tuple(torch.empty(p.stat_shape(), dtype=torch.float32, device=qt.device) for _ in range(3))
     kl, lse_t, lse_s = out
-    ws = attach_workspace(p, qt.device, stream)  # noqa: F841 (kept alive through the call)
+    ws = attach_workspace(p, qt.device, stream) if split else None  # noqa: F841 (alive through the call)
     _check(lib().streamkl_fwd(ctypes.byref(p), _ptr(qt), _ptr(kt), _ptr(qs), _ptr(ks), _ptr(kl), _ptr(lse_t),
                               _ptr(lse_s), _stream(stream)), "streamkl_fwd")
     return kl, lse_t, lse_s

@@ -264,16 +264,22 @@ def _f32_or_bf16_inputs(w, dev):
     return tuple(torch.from_numpy(a).to(dev) for a in wl.full_f32(w))
 
 
-def warm_library(dev):
-    """One tiny forward and backward, so that loading the kernels' code objects (device memory of
-    their own) falls outside every measurement of what the path allocates."""
+def warm_library(dev, w):
+    """Tiny forwards and backwards with workload w's head dims, dtype and mask, so that loading the
+    kernels' code (device memory of the runtime's own, taken at a kernel's first launch) falls
+    outside every measurement of what the path allocates."""
     import torch
     from attention_kl_amd import streamkl as S
-    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=dev)
-    kl, lt, ls = S.fwd(x, x, x, x, causal=True)
-    S.bwd(x, x, x, x, lt, ls, torch.ones_like(kl), causal=True, kl=kl, teacher_grads=True)
-    js, lt, ls, ht = S.js_fwd(x, x, x, x, causal=True)
-    S.js_bwd(x, x, x, x, lt, ls, js, ht, torch.ones_like(kl), causal=True)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    xt = torch.zeros((1, 1, 64, w.d_t), dtype=dt, device=dev)
+    xs = torch.zeros((1, 1, 64, w.d_s), dtype=dt, device=dev)
+    x = (xt, xt, xs, xs)
+    kl, lt, ls = S.fwd(*x, causal=w.causal)
+    S.bwd(*x, lt, ls, torch.ones_like(kl), causal=w.causal, kl=kl, teacher_grads=True)
+    S.bwd_dq(*x, lt, ls, torch.ones_like(kl), causal=w.causal)
+    S.bwd_dk(*x, lt, ls, torch.ones_like(kl), causal=w.causal)
+    js, lt, ls, ht = S.js_fwd(*x, causal=w.causal)
+    S.js_bwd(*x, lt, ls, js, ht, torch.ones_like(kl), causal=w.causal)
     torch.cuda.synchronize()
 
 
@@ -310,13 +316,16 @@ def measured_peak(dev, iters: int = 4000, nblocks: int = 4096):
 def time_step(w, dev, steps: int, warmup: int):
     """Forward, dK_s, dQ_s of workload w, each launch timed with HIP events on the launch stream.
 
-    Returns per-kernel mean ms, the step's algorithmic TFLOP/s, fractions of the published and the
-    measured peak, the extra HBM the path holds and what the library itself allocated."""
+    Returns per-kernel mean ms, the step's mean ms, what the library path allocated on its first call
+    and the floats of the workspace the binding attaches (small causal forwards, grouped keys)."""
+    import ctypes
     import numpy as np
     import torch
     from attention_kl_amd import streamkl as S
     from attention_kl_amd import workloads as wl
     qt, kt, qs, ks = _f32_or_bf16_inputs(w, dev)
+    ws_floats = int(S.lib().streamkl_workspace_floats(ctypes.byref(
+        S.make_problem(qt, kt, qs, ks, w.causal, w.scale_t, w.scale_s))))
     g = torch.from_numpy(wl.full_g(w)).to(dev)
     kl = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     lt, ls = torch.empty_like(kl), torch.empty_like(kl)
@@ -369,7 +378,7 @@ def time_step(w, dev, steps: int, warmup: int):
     ms["step_call"] = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
     del qt, kt, qs, ks, g, kl, lt, ls, dq, dk
     torch.cuda.empty_cache()
-    return ms, step_ms, int(lib_alloc)
+    return ms, step_ms, int(lib_alloc), ws_floats
 
 
 def config_entry(w, ms, step_ms, lib_alloc, peak=None, workspace_floats=0):
@@ -442,7 +451,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S.lib()  # fail loudly if the library is missing
-    warm_library(dev)
+    warm_library(dev, w)
     qt, kt, qs, ks = _f32_or_bf16_inputs(w, dev)
     g = torch.from_numpy(wl.full_g(w)).to(dev)
     B, H = w.B, w.H
@@ -626,12 +635,13 @@ def main():
             wi = wl.WORKLOADS[wid]
             if wid == args.workload:
                 ms = {k: kern[k]["ms"] for k in ("fwd", "bwd_dk", "bwd_dq")}
-                cfg[wi.name] = config_entry(wi, ms, step_ms, out["library_alloc_bytes"], peak)
+                cfg[wi.name] = config_entry(wi, ms, step_ms, out["library_alloc_bytes"], peak, ws_floats)
                 continue
             print(f"bench: timing {wi.name}", file=sys.stderr, flush=True)
             big = wi.pairs_per_head() * wi.B * wi.H > 1e10
-            ms, sms, la = time_step(wi, dev, steps=min(args.steps, 5) if big else args.steps, warmup=min(args.warmup, 2))
-            cfg[wi.name] = config_entry(wi, ms, sms, la, peak)
+            ms, sms, la, wsf = time_step(wi, dev, steps=min(args.steps, 5) if big else args.steps,
+                                         warmup=min(args.warmup, 2))
+            cfg[wi.name] = config_entry(wi, ms, sms, la, peak, wsf)
         out["configs"] = cfg
     if not args.no_cpu_baseline and not seg and not js:  # the CPU sample is of the dense KL workload's rows
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)

@@ -115,7 +115,7 @@ def test_equal_segments_give_the_dense_batch_bit_for_bit():
     packed = tuple(x.permute(0, 2, 1, 3).reshape(w.B * w.Nq, w.H, x.shape[-1]).contiguous() for x in dense)
     cu = torch.arange(0, w.B * w.Nq + 1, w.Nq, dtype=torch.int32).cuda()
     g = torch.from_numpy(wl.full_g(w)).cuda()
-    a = S.fwd(*dense, causal=True)
+    a = S.fwd(*dense, causal=True, split=False)  # a packed batch never splits its query blocks' keys
     b = S.fwd(*packed, causal=True, cu_seqlens_q=cu, cu_seqlens_k=cu)
     ga = S.bwd(*dense, a[1], a[2], g, causal=True, kl=a[0], teacher_grads=True)
     gp = g.permute(1, 0, 2).reshape(w.H, w.B * w.Nq).contiguous()  # [B, H, N] -> [H, B*N]
