@@ -706,9 +706,10 @@ bwd_kernel(const BwdArgs a) {
     auto run = [&](auto f16c) {
       constexpr bool F16 = decltype(f16c)::value;
       set_offsets();
-      if constexpr (F16 && !OWN_Q) {
-        // the largest |g| (times the row's bound on |dS|) of the queries this workgroup streams, over
-        // all its passes, read up front
+      // Key owner, fast path: the largest |g| (times the row's bound on |dS|) of the queries this
+      // workgroup streams, over all its passes: for grouped keys read up front, otherwise while the
+      // first tiles' DMA and the owned rows' loads are in flight (below).
+      auto g_scan = [&]() {
         float gm = 0.f;
         for (int pass = pbeg; pass < pend; ++pass) {
           const int64_t r0 = ((int64_t)sg.bs * a.H + ho * GX + pass) * a.Nq + sg.q0;
@@ -732,23 +733,44 @@ bwd_kernel(const BwdArgs a) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) gm = fmaxf(gm, gred[w]);
         esh = (float)(14 - __builtin_amdgcn_frexp_expf(gm));  // gm < 2^e, e = frexp exponent
+      };
+      if constexpr (F16 && !OWN_Q) {
+        if constexpr (GRP) g_scan();
       } else {
         esh = F16 ? 13.f : 0.f;  // |dS| < 2 (KL student, either JS half); KL teacher rows: below
       }
       fast_run = F16;
       for (int pass = pbeg; pass < pend; ++pass) {
-        set_head(a, ho * GX + pass);
+        set_head(a, ho * GX + pass);  // the owned rows' loads go out
         set_rsrc();
+        // query owner: this row's statistics, loaded here (unconditionally, at a clamped row: a
+        // load under a lane mask would be waited for where the masks join, before the DMA below)
+        // and used after it
+        float r_lt = 0.f, r_ls = 0.f, r_k = 0.f, r_j = 0.f;
+        if constexpr (OWN_Q) {
+          const int rr = min(orow, n_own - 1);
+          r_lt = lse_t_bh[rr];
+          r_ls = lse_s_bh[rr];
+          if constexpr (TEACHER || JS) r_k = kl_bh[rr];  // KL, or (JS) the teacher half js_t
+          if constexpr (JS) r_j = js_bh[rr];
+        }
+        // The first tiles' DMA goes out with these loads and the owned rows' (and the key owner's scan
+        // of |g|): one memory round trip before the first period instead of two or three.  The
+        // compiler's waits for its own loads also wait for these older DMAs, which the first period
+        // needs anyway.
+#pragma unroll
+        for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
+        if constexpr (F16 && !OWN_Q && !GRP) g_scan();
         if constexpr (OWN_Q) {
           if (ovalid) {
             // KL teacher: this row's own shift, 14 - e with 2^e above the row's bound on |dS|
-            const float sh = (F16 && KLT) ? (float)(14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(kl_bh[orow]))) : esh;
-            own_lt = lse_t_bh[orow] * kLog2e - sh;
-            own_ls = lse_s_bh[orow] * kLog2e - sh;
+            const float sh = (F16 && KLT) ? (float)(14 - __builtin_amdgcn_frexp_expf(teacher_ds_bound(r_k))) : esh;
+            own_lt = r_lt * kLog2e - sh;
+            own_ls = r_ls * kLog2e - sh;
             if constexpr (JS)
-              own_c = (TEACHER ? kl_bh[orow] : fmaf(2.f, js_bh[orow], -kl_bh[orow])) * kLog2e;
+              own_c = (TEACHER ? r_k : fmaf(2.f, r_j, -r_k)) * kLog2e;
             else if constexpr (TEACHER)
-              own_c = kl_bh[orow] + lse_t_bh[orow] - lse_s_bh[orow];
+              own_c = r_k + r_lt - r_ls;
           }
         }
         {
@@ -767,10 +789,9 @@ bwd_kernel(const BwdArgs a) {
 #pragma unroll
           for (int o = 16 * tid; o < TILE; o += 16 * NT) *reinterpret_cast<u32x4*>(ring[NBUF - 1] + o) = u32x4{};
         }
-        wait_vmcnt<0>();  // retire the compiler's own loads before the untracked DMAs start
-#pragma unroll
-        for (int i = 0; i < PD; ++i) issue(i, i);  // past the last tile a DMA reads nothing, writes zeros
-        wait_tile();
+        // both first tiles and every load of the compiler's own have landed: none of its waits for
+        // them falls inside the loop, where it would also drain the DMA ring
+        wait_vmcnt<0>();
         __syncthreads();
         if constexpr (NG == 2) {
           // Periods s = 0 .. ntile, one workgroup barrier at the end of each.  In period s group 0 runs
