@@ -313,6 +313,15 @@ def measured_peak(dev, iters: int = 4000, nblocks: int = 4096):
                     "each on register operands; clock = shader-clock counter / constant-rate counter"}
 
 
+def alloc_outside_torch(free0: int, reserved0: int) -> int:
+    """Device bytes taken since free0 (hipMemGetInfo) that torch's caching allocator does not hold:
+    what the library allocated by itself.  The caller workspace the binding attaches for some paths is
+    a torch tensor (reported as workspace_bytes), so a segment the allocator reserves for it is not
+    counted here."""
+    import torch
+    return max(0, (free0 - torch.cuda.mem_get_info()[0]) - (torch.cuda.memory_reserved() - reserved0))
+
+
 def time_step(w, dev, steps: int, warmup: int):
     """Forward, dK_s, dQ_s of workload w, each launch timed with HIP events on the launch stream.
 
@@ -343,10 +352,10 @@ def time_step(w, dev, steps: int, warmup: int):
         ev and ev[3].record()
 
     torch.cuda.synchronize()
-    free0, alloc0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated()
-    step()  # the first call: whatever the path allocates shows here
+    free0, res0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_reserved()
+    step()  # the first call: whatever the library allocates shows here
     torch.cuda.synchronize()
-    lib_alloc = max(free0 - torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated() - alloc0)
+    lib_alloc = alloc_outside_torch(free0, res0)
     for _ in range(warmup):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -395,7 +404,8 @@ def config_entry(w, ms, step_ms, lib_alloc, peak=None, workspace_floats=0):
          "peak_tflops": mp, "dtype": w.dtype,
          **({"bwd_call_ms": round(ms["bwd_call"], 4), "step_call_ms": round(ms["step_call"], 4),
              "step_call_tflops": round((fwd_fl + bwd_fl) / ms["step_call"] / 1e9, 2)} if "bwd_call" in ms else {}),
-         "extra_hbm_bytes": 12 * w.B * w.H * w.Nq + 4 * int(workspace_floats), "library_alloc_bytes": lib_alloc}
+         "extra_hbm_bytes": 12 * w.B * w.H * w.Nq + 4 * int(workspace_floats),
+         "workspace_bytes": 4 * int(workspace_floats), "library_alloc_bytes": lib_alloc}
     if peak and w.dtype == "bf16":
         e["fwd_frac_of_measured_peak"] = round(fwd_fl / ms["fwd"] / 1e9 / peak["tflops"], 4)
         e["bwd_frac_of_measured_peak"] = round(bwd_fl / bwd_ms / 1e9 / peak["tflops"], 4)
@@ -524,13 +534,13 @@ def main():
             if ev is not None:
                 ev[4].record()
 
-    # what the library path itself allocates: device memory taken around the first call (torch's
-    # caching allocator grows by the grouped-key workspace here, if any, and keeps it afterwards)
+    # what the library itself allocates: device memory taken around the first call beyond what torch's
+    # caching allocator reserves (it grows by the binding's workspace here, if any, and keeps it)
     torch.cuda.synchronize()
-    free0, alloc0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated()
+    free0, res0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_reserved()
     step()
     torch.cuda.synchronize()
-    first_call_alloc = max(free0 - torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated() - alloc0)
+    first_call_alloc = alloc_outside_torch(free0, res0)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -540,7 +550,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    free0 = torch.cuda.mem_get_info()[0]
+    free0, res0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_reserved()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5 if teacher else 4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -548,7 +558,7 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    steady_alloc = free0 - torch.cuda.mem_get_info()[0]
+    steady_alloc = alloc_outside_torch(free0, res0)
     per = {"js_fwd": [], "js_bwd": []} if js else {"fwd": [], "bwd_dk": [], "bwd_dq": []}
     if teacher:
         per["bwd_teacher"] = []
