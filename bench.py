@@ -412,6 +412,85 @@ def config_entry(w, ms, step_ms, lib_alloc, peak=None, workspace_floats=0):
     return e
 
 
+def power_profile(w, dev, seconds: float = 6.0):
+    """Board power and shader clocks while each kernel of workload w (and the MFMA probe) runs back to
+    back for `seconds`: `amd-smi metric -p -c --json` sampled every 0.5 s; medians of the samples
+    taken after the first second.  None where amd-smi is missing or reports no socket power."""
+    import ctypes
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    import torch
+    from attention_kl_amd import streamkl as S
+    from attention_kl_amd import workloads as wl
+    if shutil.which("amd-smi") is None:
+        return None
+    qt, kt, qs, ks = _f32_or_bf16_inputs(w, dev)
+    kw = dict(causal=w.causal, scale_t=w.scale_t, scale_s=w.scale_s)
+    kl, lt, ls = S.fwd(qt, kt, qs, ks, **kw)
+    g = torch.from_numpy(wl.full_g(w)).to(dev)
+    dq = torch.empty((w.B, w.H, w.Nq, w.d_s), dtype=torch.float32, device=dev)
+    dk = torch.empty((w.B, w.H, w.Nk, w.d_s), dtype=torch.float32, device=dev)
+    psink = torch.empty(4096 * 256, dtype=torch.float32, device=dev)
+    pclk = torch.empty(2 * 4096, dtype=torch.int64, device=dev)
+    khz = ctypes.c_double(0.0)
+    launches = {
+        "mfma_probe": lambda: S.lib().streamkl_probe_mfma(4096, 4000, psink.data_ptr(), pclk.data_ptr(),
+                                                          ctypes.byref(khz), torch.cuda.current_stream().cuda_stream),
+        "fwd": lambda: S.fwd(qt, kt, qs, ks, out=(kl, lt, ls), **kw),
+        "bwd_dk": lambda: S.bwd_dk(qt, kt, qs, ks, lt, ls, g, out=dk, **kw),
+        "bwd_dq": lambda: S.bwd_dq(qt, kt, qs, ks, lt, ls, g, out=dq, **kw),
+    }
+
+    def sample():
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        d = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = [v["clk"]["value"] for k, v in d["clock"].items() if k.startswith("gfx_") and isinstance(v, dict)]
+        return float(d["power"]["socket_power"]["value"]), [float(c) for c in clk]
+
+    out = {}
+    for name, fn in launches.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            t0 = time.perf_counter()
+            while not stop.is_set():
+                try:
+                    p_w, clk = sample()
+                    if time.perf_counter() - t0 > 1.0:
+                        samples.append((p_w, clk))
+                except Exception:
+                    pass
+                stop.wait(0.5)
+        th = threading.Thread(target=sampler)
+        th.start()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                fn()
+                n += 1
+            torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        stop.set()
+        th.join()
+        if not samples:
+            return None
+        nx = len(samples[0][1])
+        out[name] = {"socket_power_w": statistics.median(p for p, _ in samples),
+                     "gfx_clock_mhz_per_xcd": [statistics.median(c[i] for _, c in samples) for i in range(nx)],
+                     "ms_per_launch": round(el * 1e3 / n, 3), "samples": len(samples)}
+    del qt, kt, qs, ks, g, kl, lt, ls, dq, dk, psink, pclk
+    torch.cuda.empty_cache()
+    out["what"] = (f"each kernel of {w.name} (and the MFMA probe) launched back to back for {seconds:.0f} s; "
+                   "amd-smi socket power and per-XCD gfx clocks every 0.5 s, medians after the first second")
+    return out
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-pmc":
         # python bench.py --ingest-pmc <fetch counter csv> <write counter csv> [workload id]
@@ -441,6 +520,8 @@ def main():
     ap.add_argument("--packed-mix", type=int, default=None, metavar="SEED",
                     help="packed variable-length batch: the workload's rows cut into segments of a seeded "
                          "log-uniform length mix (256..8192 rows), each its own (causal) problem")
+    ap.add_argument("--power", action="store_true",
+                    help="also sample board power and per-XCD clocks while each kernel runs back to back (amd-smi)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -653,6 +734,9 @@ def main():
                                          warmup=min(args.warmup, 2))
             cfg[wi.name] = config_entry(wi, ms, sms, la, peak, wsf)
         out["configs"] = cfg
+    if args.power and not seg and not js and not teacher:
+        print("bench: sampling power", file=sys.stderr, flush=True)
+        out["power"] = power_profile(w, dev)
     if not args.no_cpu_baseline and not seg and not js:  # the CPU sample is of the dense KL workload's rows
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)
